@@ -1,0 +1,179 @@
+"""CPU oracle for the speculative-decoding verify step (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never does: it shares
+no code with the HIP library, and the HIP path never falls back to it.
+
+The arithmetic lives in ``oracle.c`` (IEEE double, plain loops, one function
+per definition on the pages); this module only marshals numpy arrays.
+
+Sources (page title, section):
+  "KV Cache + Speculative Decoding": 2.1 (KV-cache size), 5.2-5.3 (paging),
+      6.1/6.3 (cached causal GQA attention), 7.1-7.6 (rejection sampler)
+  "50 | Speculative Decoding": 3.1 (decision rule), 3.2 (exactness proof)
+  "Lecture 10 - Inference": 3.3 (KV-cache bytes)
+  "Speculative decoding and KV cache optimisation": 3.1 (KV-cache bytes)
+"""
+import contextlib
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+KV_F32, KV_BF16, KV_FP8_E4M3 = 0, 1, 2
+
+_lib = None
+
+
+def _bind(lib):
+    c = ctypes
+    lib.oracle_decode_bf16.restype = c.c_double
+    lib.oracle_decode_bf16.argtypes = [c.c_uint16]
+    lib.oracle_decode_e4m3.restype = c.c_double
+    lib.oracle_decode_e4m3.argtypes = [c.c_uint8]
+    lib.oracle_softmax_row.restype = None
+    lib.oracle_softmax_row.argtypes = [c.c_void_p, c.c_int64, c.c_void_p]
+    lib.oracle_attn_rows.restype = c.c_int
+    lib.oracle_attn_rows.argtypes = (
+        [c.c_void_p] * 7 + [c.c_int] * 8 + [c.c_double, c.c_void_p, c.c_int64, c.c_void_p, c.c_int])
+    lib.oracle_sample.restype = c.c_int
+    lib.oracle_sample.argtypes = (
+        [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Routes every oracle call through another build of oracle.c while the
+    context is open (the test that plants mistakes in copies of the oracle
+    uses this to show that the pins catch them)."""
+    global _lib
+    saved = _load()
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def decode_bf16(bits: int) -> float:
+    """bfloat16 bit pattern -> value, from the format definition."""
+    return _load().oracle_decode_bf16(int(bits) & 0xFFFF)
+
+
+def decode_e4m3(bits: int) -> float:
+    """OCP E4M3 (fn) bit pattern -> value, from the format definition."""
+    return _load().oracle_decode_e4m3(int(bits) & 0xFF)
+
+
+def softmax_row(logits: np.ndarray) -> np.ndarray:
+    """fp64 softmax of one fp32 logit row (max subtracted)."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    p = np.empty(x.shape[0], dtype=np.float64)
+    _load().oracle_softmax_row(_ptr(x), x.shape[0], _ptr(p))
+    return p
+
+
+def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=None,
+         v_scale=None, sm_scale=None, rows=None, block_size=16, nthreads=None):
+    """Verify attention by the plain definition, in fp64.
+
+    q [B,T,Hq,d] fp32; k_cache/v_cache [num_blocks,16,Hkv,d] as stored
+    (fp32, bf16 bits as uint16, or E4M3 codes as uint8); k_scale/v_scale
+    [num_blocks] fp32 for E4M3; block_table [B,max_blocks] int32;
+    context_lens [B] int32 (the T new positions included).
+    rows: optional flat row indices (b*T + t)*Hq + h.
+    Returns [B,T,Hq,d] fp64, or [len(rows), d] when rows is given.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, T, Hq, d = q.shape
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    Hkv = k_cache.shape[2]
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    max_blocks = block_table.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    if kv_dtype == KV_FP8_E4M3:
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+    if rows is None:
+        nrows = B * T * Hq
+        rows_arr = None
+        out = np.empty((B, T, Hq, d), dtype=np.float64)
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.shape[0]
+        out = np.empty((nrows, d), dtype=np.float64)
+    rc = _load().oracle_attn_rows(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), B, T, Hq, Hkv, d, block_size, max_blocks,
+        int(kv_dtype), float(sm_scale), _ptr(rows_arr), nrows, _ptr(out),
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_rows rejected its arguments")
+    return out
+
+
+def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6, nthreads=None):
+    """The verify sampler by the pages' rule, in fp64.
+
+    Returns a dict: num_accepted [B] int32, out_tokens [B,K+1] int32,
+    accept_ratio [B,K] fp64 (NaN after the first rejection), near_pos [B]
+    int32 (first position decided within near_eps of its threshold, or -1),
+    resid_mass [B] fp64.
+    """
+    tl = np.ascontiguousarray(target_logits, dtype=np.float32)
+    dp = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B, T, V = tl.shape
+    K = T - 1
+    assert dp.shape == (B, K, V) and dt.shape == (B, K) and u.shape == (B, K + 1)
+    res = {
+        "num_accepted": np.empty(B, dtype=np.int32),
+        "out_tokens": np.empty((B, K + 1), dtype=np.int32),
+        "accept_ratio": np.empty((B, K), dtype=np.float64),
+        "near_pos": np.empty(B, dtype=np.int32),
+        "resid_mass": np.empty(B, dtype=np.float64),
+    }
+    rc = _load().oracle_sample(
+        _ptr(tl), _ptr(dp), _ptr(dt), _ptr(u), B, K, V, float(near_eps),
+        _ptr(res["num_accepted"]), _ptr(res["out_tokens"]), _ptr(res["accept_ratio"]),
+        _ptr(res["near_pos"]), _ptr(res["resid_mass"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_sample rejected its arguments")
+    return res
+
+
+def kv_cache_bytes(ctx_len, n_layers, n_kv_heads, head_dim, bytes_per_elem, batch=1):
+    """KV-cache size: 2 (K and V) * L_ctx * N_layers * N_kv_heads * d_head * bytes,
+    times the batch ("KV Cache + Speculative Decoding" 2.1; "Lecture 10 -
+    Inference" 3.3; "Speculative decoding and KV cache optimisation" 3.1).
+    The query-head count never enters."""
+    return 2 * ctx_len * n_layers * n_kv_heads * head_dim * bytes_per_elem * batch

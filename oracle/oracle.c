@@ -1,0 +1,430 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link, load
+ * or call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no source with the HIP library.
+ *
+ * Everything is computed in IEEE double from the definitions on the pages, with
+ * plain nested loops in the order the definitions state.  The only parallelism
+ * is an optional split of independent output rows / sequences over POSIX
+ * threads; it does not change any arithmetic inside a row or sequence.
+ *
+ * Sources (page title, section):
+ *   [KV]  "KV Cache + Speculative Decoding" (AI knowledge base)
+ *   [SD]  "50 | Speculative Decoding" (Transformer and attention series)
+ *   [L10] "Lecture 10 - Inference" (CS336 notes)
+ *   [WC]  "Speculative decoding and KV cache optimisation"
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_KV_F32 = 0, OR_KV_BF16 = 1, OR_KV_FP8_E4M3 = 2 };
+
+/* ------------------------------------------------------------------ decoders */
+
+/* bfloat16, from the format definition: 1 sign bit, 8 exponent bits (bias 127),
+ * 7 fraction bits; exponent 0 is subnormal, exponent 255 is inf/NaN. */
+double oracle_decode_bf16(uint16_t bits)
+{
+    int s = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int m = bits & 0x7F;
+    double sign = s ? -1.0 : 1.0;
+    if (e == 0xFF)
+        return m ? NAN : sign * INFINITY;
+    if (e == 0)
+        return sign * ldexp((double)m / 128.0, -126);
+    return sign * ldexp(1.0 + (double)m / 128.0, e - 127);
+}
+
+/* OCP 8-bit float E4M3 ("fn" variant): 1 sign bit, 4 exponent bits (bias 7),
+ * 3 fraction bits, no infinities, S.1111.111 is NaN, largest finite is 448.
+ * The pages store the KV cache in 8-bit float and compute in a wider type
+ * ([KV] section 4.5 on KV quantisation; [WC] section 3.5). */
+double oracle_decode_e4m3(uint8_t bits)
+{
+    int s = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xF;
+    int m = bits & 0x7;
+    double sign = s ? -1.0 : 1.0;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        return sign * ldexp((double)m / 8.0, -6);
+    return sign * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* One cached element as a real number: the stored value, times the per-block
+ * scale for 8-bit storage. */
+static double kv_elem(const void *cache, int kv_dtype, const float *scale,
+                      int64_t blk, int64_t idx)
+{
+    switch (kv_dtype) {
+    case OR_KV_F32:
+        return (double)((const float *)cache)[idx];
+    case OR_KV_BF16:
+        return oracle_decode_bf16(((const uint16_t *)cache)[idx]);
+    default:
+        return oracle_decode_e4m3(((const uint8_t *)cache)[idx]) * (double)scale[blk];
+    }
+}
+
+/* ----------------------------------------------------------------- attention */
+
+typedef struct {
+    const float *q;
+    const void *k_cache, *v_cache;
+    const float *k_scale, *v_scale;
+    const int32_t *block_table, *context_lens;
+    int B, T, Hq, Hkv, d, block_size, max_blocks, kv_dtype;
+    double sm_scale;
+    const int64_t *rows;
+    int64_t nrows;
+    double *out;
+    double *scratch; /* per thread: score[max_blocks*block_size] */
+} attn_job;
+
+/*
+ * One output row (b, t, h) of verify attention, from the definition.
+ *
+ * The verify forward feeds [last token, x_1 .. x_K] (T = K+1 rows) after their
+ * K/V were appended to the cache, so the cache holds L_b positions including
+ * the T new ones and row t sits at position L_b - T + t; it may attend to
+ * positions 0 .. L_b - T + t ([KV] 6.1 and 6.3: concatenate, then the causal
+ * mask tril with diagonal L_total - L_new; [KV] 7.6 step 2).
+ * Query head h reads KV head floor(h / G), G = Hq / Hkv ([KV] 6.3,
+ * repeat_interleave over the head axis).
+ * Logical position p lives in physical block block_table[b][p / 16], slot
+ * p mod 16 ([KV] 5.2-5.3; [L10] 9.2).  Cache layout [block][slot][kv head][d].
+ * Scores are q.k * sm_scale (sm_scale = 1/sqrt(d) in [KV] 6.1), softmax over
+ * the visible positions, output = softmax-weighted sum of values.
+ */
+static void attn_one_row(const attn_job *J, int64_t row, double *score, double *o)
+{
+    const int T = J->T, Hq = J->Hq, Hkv = J->Hkv, d = J->d, bs = J->block_size;
+    const int64_t b = row / ((int64_t)T * Hq);
+    const int t = (int)((row / Hq) % T);
+    const int h = (int)(row % Hq);
+    const int G = Hq / Hkv;
+    const int g = h / G;
+    const int64_t L = J->context_lens[b];
+    const int64_t n_vis = L - T + 1 + t;
+    const float *qrow = J->q + row * d;
+
+    for (int c = 0; c < d; ++c)
+        o[c] = 0.0;
+    if (n_vis <= 0) {
+        for (int c = 0; c < d; ++c)
+            o[c] = NAN;
+        return;
+    }
+
+    double smax = -INFINITY;
+    for (int64_t p = 0; p < n_vis; ++p) {
+        int64_t blk = J->block_table[b * J->max_blocks + p / bs];
+        int64_t slot = p % bs;
+        int64_t base = ((blk * bs + slot) * Hkv + g) * d;
+        double s = 0.0;
+        for (int c = 0; c < d; ++c)
+            s += (double)qrow[c] * kv_elem(J->k_cache, J->kv_dtype, J->k_scale, blk, base + c);
+        s *= J->sm_scale;
+        score[p] = s;
+        if (s > smax)
+            smax = s;
+    }
+    double denom = 0.0;
+    for (int64_t p = 0; p < n_vis; ++p) {
+        score[p] = exp(score[p] - smax);
+        denom += score[p];
+    }
+    for (int64_t p = 0; p < n_vis; ++p) {
+        int64_t blk = J->block_table[b * J->max_blocks + p / bs];
+        int64_t slot = p % bs;
+        int64_t base = ((blk * bs + slot) * Hkv + g) * d;
+        double w = score[p] / denom;
+        for (int c = 0; c < d; ++c)
+            o[c] += w * kv_elem(J->v_cache, J->kv_dtype, J->v_scale, blk, base + c);
+    }
+}
+
+typedef struct {
+    const attn_job *job;
+    int64_t begin, end;
+} attn_slice;
+
+static void *attn_worker(void *arg)
+{
+    const attn_slice *S = (const attn_slice *)arg;
+    const attn_job *J = S->job;
+    double *score = (double *)malloc(sizeof(double) * ((size_t)J->max_blocks * J->block_size + 1));
+    if (!score)
+        return (void *)1;
+    for (int64_t i = S->begin; i < S->end; ++i) {
+        int64_t row = J->rows ? J->rows[i] : i;
+        attn_one_row(J, row, score, J->out + i * J->d);
+    }
+    free(score);
+    return NULL;
+}
+
+/*
+ * Computes the requested output rows into out[nrows][d] (double).
+ * rows[i] is the flat row index (b*T + t)*Hq + h; rows == NULL means every row
+ * in order (nrows must then be B*T*Hq).  Returns 0, or -1 on bad arguments.
+ * Rows with no visible position (L_b < T - t) are NaN.
+ */
+int oracle_attn_rows(const float *q, const void *k_cache, const void *v_cache,
+                     const float *k_scale, const float *v_scale,
+                     const int32_t *block_table, const int32_t *context_lens,
+                     int B, int T, int Hq, int Hkv, int d, int block_size,
+                     int max_blocks, int kv_dtype, double sm_scale,
+                     const int64_t *rows, int64_t nrows, double *out, int nthreads)
+{
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+        return -1;
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || block_size < 1 || max_blocks < 1)
+        return -1;
+    if (kv_dtype == OR_KV_FP8_E4M3 && (!k_scale || !v_scale))
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (context_lens[b] < 0 || context_lens[b] > (int64_t)max_blocks * block_size)
+            return -1;
+    attn_job J = {q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                  B, T, Hq, Hkv, d, block_size, max_blocks, kv_dtype, sm_scale,
+                  rows, nrows, out, NULL};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > nrows)
+        nthreads = nrows > 0 ? (int)nrows : 1;
+    pthread_t th[256];
+    attn_slice sl[256];
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &J;
+        sl[i].begin = nrows * i / nthreads;
+        sl[i].end = nrows * (i + 1) / nthreads;
+    }
+    if (nthreads == 1)
+        return attn_worker(&sl[0]) ? -1 : 0;
+    for (int i = 0; i < nthreads; ++i)
+        pthread_create(&th[i], NULL, attn_worker, &sl[i]);
+    for (int i = 0; i < nthreads; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r)
+            rc = -1;
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------- sampler */
+
+/* Target distribution of one verify row: softmax of the fp32 logits, computed
+ * with the maximum subtracted ([KV] 7.6 step 3 applies softmax to each target
+ * row; temperature 1). */
+void oracle_softmax_row(const float *logits, int64_t V, double *p)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < V; ++j)
+        if ((double)logits[j] > m)
+            m = (double)logits[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+        p[j] = exp((double)logits[j] - m);
+        z += p[j];
+    }
+    for (int64_t j = 0; j < V; ++j)
+        p[j] /= z;
+}
+
+typedef struct {
+    const float *target_logits, *draft_probs, *uniforms;
+    const int32_t *draft_tokens;
+    int B, K;
+    int64_t V;
+    double near_eps;
+    int32_t *num_accepted, *out_tokens, *near_pos;
+    double *accept_ratio, *resid_mass;
+} sample_job;
+
+/*
+ * One sequence of the verify sampler ([SD] 3.1; [KV] 7.1-7.3 and 7.6).
+ *   Row i of the target logits gives p_i; row i < K verifies draft x_i, row K
+ *   is the bonus row.  Draft x_i is accepted with probability
+ *   min(1, p_i(x_i)/q_i(x_i)): with the caller's uniform u_i that is the test
+ *   u_i * q_i(x_i) < p_i(x_i) (strict, as "rand < r" in [KV] 7.6).
+ *   At the first rejection n the replacement is drawn from
+ *   max(0, p_n - q_n) / sum(max(0, p_n - q_n)); if all K are accepted the
+ *   bonus is drawn from p_K.  Drawing uses u_K and the inverse CDF in
+ *   ascending token order: the smallest j whose cumulative weight exceeds
+ *   u_K * S.  Should rounding leave no such j, the largest j of positive
+ *   weight is taken; should the residual mass S be 0 (only reachable by
+ *   rounding, since p <= q everywhere forces p = q), p_n is drawn instead.
+ *   Output: n accepted drafts, then the drawn token, then -1 padding.
+ *   near_pos = first position whose decision lies within near_eps of its
+ *   threshold (acceptance: |u_i - min(1, p/q)|; final draw: u_K within
+ *   near_eps of either edge of the chosen token's CDF interval), else -1.
+ */
+static void sample_one(const sample_job *J, int b, double *p, double *w)
+{
+    const int K = J->K;
+    const int64_t V = J->V;
+    const float *u = J->uniforms + (int64_t)b * (K + 1);
+    int n = K;
+    int near = -1;
+
+    for (int i = 0; i < K; ++i) {
+        const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + i) * V;
+        const float *qrow = J->draft_probs + ((int64_t)b * K + i) * V;
+        oracle_softmax_row(lrow, V, p);
+        int x = J->draft_tokens[(int64_t)b * K + i];
+        double a = p[x];
+        double c = (double)qrow[x];
+        double r = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
+        J->accept_ratio[(int64_t)b * K + i] = r;
+        if (near < 0 && fabs((double)u[i] - r) < J->near_eps)
+            near = i;
+        if (!((double)u[i] * c < a)) {
+            n = i;
+            break;
+        }
+    }
+    for (int i = n + 1; i < K; ++i)
+        J->accept_ratio[(int64_t)b * K + i] = NAN;
+
+    const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;
+    oracle_softmax_row(lrow, V, p);
+    double S = 0.0;
+    if (n < K) {
+        const float *qrow = J->draft_probs + ((int64_t)b * K + n) * V;
+        for (int64_t j = 0; j < V; ++j) {
+            double r = p[j] - (double)qrow[j];
+            w[j] = r > 0.0 ? r : 0.0;
+            S += w[j];
+        }
+    } else {
+        for (int64_t j = 0; j < V; ++j) {
+            w[j] = p[j];
+            S += w[j];
+        }
+    }
+    J->resid_mass[b] = S;
+    if (S == 0.0) {
+        S = 0.0;
+        for (int64_t j = 0; j < V; ++j) {
+            w[j] = p[j];
+            S += w[j];
+        }
+    }
+
+    double target = (double)u[K] * S;
+    double C = 0.0, Cprev = 0.0;
+    int64_t tok = -1;
+    for (int64_t j = 0; j < V; ++j) {
+        Cprev = C;
+        C += w[j];
+        if (C > target) {
+            tok = j;
+            break;
+        }
+    }
+    if (tok < 0) {
+        for (int64_t j = V - 1; j >= 0; --j)
+            if (w[j] > 0.0) {
+                tok = j;
+                break;
+            }
+        Cprev = S;
+        C = S;
+    }
+    if (near < 0 && (fabs((double)u[K] - Cprev / S) < J->near_eps ||
+                     fabs((double)u[K] - C / S) < J->near_eps))
+        near = n;
+
+    int32_t *ot = J->out_tokens + (int64_t)b * (K + 1);
+    for (int i = 0; i < n; ++i)
+        ot[i] = J->draft_tokens[(int64_t)b * K + i];
+    ot[n] = (int32_t)tok;
+    for (int i = n + 1; i <= K; ++i)
+        ot[i] = -1;
+    J->num_accepted[b] = n;
+    J->near_pos[b] = near;
+}
+
+typedef struct {
+    const sample_job *job;
+    int begin, end;
+} sample_slice;
+
+static void *sample_worker(void *arg)
+{
+    const sample_slice *S = (const sample_slice *)arg;
+    double *p = (double *)malloc(sizeof(double) * (size_t)S->job->V);
+    double *w = (double *)malloc(sizeof(double) * (size_t)S->job->V);
+    if (!p || !w) {
+        free(p);
+        free(w);
+        return (void *)1;
+    }
+    for (int b = S->begin; b < S->end; ++b)
+        sample_one(S->job, b, p, w);
+    free(p);
+    free(w);
+    return NULL;
+}
+
+/*
+ * The whole sampler for B sequences.  Shapes: target_logits [B][K+1][V],
+ * draft_probs [B][K][V], draft_tokens [B][K] (in [0, V)), uniforms [B][K+1];
+ * outputs num_accepted [B], out_tokens [B][K+1], accept_ratio [B][K]
+ * (positions after the first rejection are NaN), near_pos [B],
+ * resid_mass [B] (S before any fallback).  Returns 0, or -1 on bad arguments.
+ */
+int oracle_sample(const float *target_logits, const float *draft_probs,
+                  const int32_t *draft_tokens, const float *uniforms,
+                  int B, int K, int64_t V, double near_eps,
+                  int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
+                  int32_t *near_pos, double *resid_mass, int nthreads)
+{
+    if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted ||
+        !out_tokens || !accept_ratio || !near_pos || !resid_mass)
+        return -1;
+    if (B < 1 || K < 1 || V < 1)
+        return -1;
+    for (int64_t i = 0; i < (int64_t)B * K; ++i)
+        if (draft_tokens[i] < 0 || draft_tokens[i] >= V)
+            return -1;
+    sample_job J = {target_logits, draft_probs, uniforms, draft_tokens, B, K, V, near_eps,
+                    num_accepted, out_tokens, near_pos, accept_ratio, resid_mass};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > B)
+        nthreads = B;
+    pthread_t th[256];
+    sample_slice sl[256];
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &J;
+        sl[i].begin = (int)((int64_t)B * i / nthreads);
+        sl[i].end = (int)((int64_t)B * (i + 1) / nthreads);
+    }
+    if (nthreads == 1)
+        return sample_worker(&sl[0]) ? -1 : 0;
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i)
+        pthread_create(&th[i], NULL, sample_worker, &sl[i]);
+    for (int i = 0; i < nthreads; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r)
+            rc = -1;
+    }
+    return rc;
+}

@@ -1,0 +1,82 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that the pins catch every one of them: a dropped term, a wrong sign, index or
+comparison, a transposed operand.  Each mutant is oracle.c with one textual
+edit, built with gcc into a temporary library and swapped in for the real
+oracle while a chosen set of pin tests runs against it."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from . import test_oracle_attention as TA
+from . import test_oracle_sampler as TS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# Ordered so that pins whose inputs leave slack in the block table run first: a
+# mutant that reads one position too far then hits a poisoned slot, not memory
+# past the end of the table.
+ATTN_PINS = [
+    TA.test_causal_mask_offset, TA.test_gqa_head_map_uses_floor_h_over_G,
+    TA.test_two_visible_keys_closed_form, TA.test_zero_query_gives_mean_of_visible_values,
+    TA.test_bf16_decoder_exhaustive, TA.test_e4m3_decoder_exhaustive,
+] + [lambda c=c: TA.test_oracle_matches_library_attention(*c) for c in TA.CASES]
+SAMPLE_PINS = [
+    lambda: TS.test_every_emitted_position_follows_target("noisy"),
+    TS.test_boundary_uniforms, TS.test_two_token_worked_example,
+    TS.test_residual_mass_identity_on_config_rows, TS.test_accept_ratio_matches_library_softmax,
+    TS.test_draft_equal_to_target_accepts_all_and_draws_bonus,
+    lambda: TS.test_mean_tokens_per_round_closed_form(4, 0.6),
+]
+
+# (name, original text, replacement, pins expected to catch it)
+MUTANTS = [
+    ("head map h % Hkv", "const int g = h / G;", "const int g = h % Hkv;", ATTN_PINS),
+    ("causal offset one short", "const int64_t n_vis = L - T + 1 + t;", "const int64_t n_vis = L - T + t;", ATTN_PINS),
+    ("causal offset one long", "const int64_t n_vis = L - T + 1 + t;", "const int64_t n_vis = L - T + 2 + t;", ATTN_PINS),
+    ("scale dropped", "        s *= J->sm_scale;", "        s *= 1.0;", ATTN_PINS),
+    ("values read from K", "o[c] += w * kv_elem(J->v_cache, J->kv_dtype, J->v_scale",
+     "o[c] += w * kv_elem(J->k_cache, J->kv_dtype, J->k_scale", ATTN_PINS),
+    ("softmax denominator dropped", "double w = score[p] / denom;", "double w = score[p];", ATTN_PINS),
+    ("fp8 scale dropped", "* (double)scale[blk];", "* 1.0;", ATTN_PINS),
+    ("bf16 bias off by one", "return sign * ldexp(1.0 + (double)m / 128.0, e - 127);",
+     "return sign * ldexp(1.0 + (double)m / 128.0, e - 126);", ATTN_PINS),
+    ("e4m3 subnormal exponent", "return sign * ldexp((double)m / 8.0, -6);",
+     "return sign * ldexp((double)m / 8.0, -7);", ATTN_PINS),
+    ("residual sign flipped", "double r = p[j] - (double)qrow[j];", "double r = (double)qrow[j] - p[j];", SAMPLE_PINS),
+    ("residual is p itself", "w[j] = r > 0.0 ? r : 0.0;", "w[j] = p[j];", SAMPLE_PINS),
+    ("acceptance ratio inverted", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * a < c)) {", SAMPLE_PINS),
+    ("non-strict acceptance", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * c <= a)) {", SAMPLE_PINS),
+    ("inverse CDF >=", "if (C > target) {", "if (C >= target) {", SAMPLE_PINS),
+    ("final row always 0", "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;\n    oracle_softmax_row",
+     "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + 0) * V;\n    oracle_softmax_row", SAMPLE_PINS),
+    ("bonus from draft-free row K-1",
+     "        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
+     "        oracle_softmax_row(lrow - V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
+     SAMPLE_PINS),
+    ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, pins):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor must be unique: " + name
+    with tempfile.TemporaryDirectory() as tmp:
+        path_c = os.path.join(tmp, "mutant.c")
+        path_so = os.path.join(tmp, "libmutant.so")
+        with open(path_c, "w") as f:
+            f.write(src.replace(old, new))
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", path_c, "-o", path_so,
+                        "-lm", "-lpthread"], check=True)
+        caught = False
+        with oracle.use_library(path_so):
+            for pin in pins:
+                try:
+                    pin()
+                except (AssertionError, ValueError):
+                    caught = True
+                    break
+        assert caught, "no pin caught the planted mistake: " + name

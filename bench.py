@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one spec_verify_attn call (paged GQA attention of the K+1 verify
+rows over the whole KV cache of one layer) followed by one spec_verify_sample
+call (the rejection sampler over the K+1 target rows), on seeded synthetic
+inputs already resident in HBM.  Several copies of the inputs are rotated so
+that every step reads cold data (the 256 MiB Infinity Cache cannot hold them).
+
+Prints one JSON line.  Default workload: the LLaMA-3-8B-style layer (B=8,
+Hq=32, Hkv=8, d=128, context 4096, 16-token pages, K=5, bf16 KV, V=128256).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+ATTN_SRC = os.path.join(ROOT, "speculative_decoding_verify_attn_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+METRIC = "verify steps/sec and achieved HBM GB/s (% of MI355X peak) per config"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0: enough to defeat the MALL)")
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 vector ALU, 2 matrix cores")
+    ap.add_argument("--bps", type=int, default=0, help="context pages per split (0: planner)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
+    ap.add_argument("--probe", choices=["none", "copy"], default="none",
+                    help="copy: run only a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def attn_source_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def probe_copy():
+    import torch
+    n = 1 << 28  # 256 MiB per direction
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.probe == "copy":
+        probe_copy()
+        return
+
+    import torch
+    import speculative_decoding_verify_attn_amd as sv
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    t_gen = time.time()
+    a = W.make_attn(args.config, seed=args.seed)
+    s = W.make_sample(args.config, seed=args.seed)
+    print("# generated %s in %.1f s" % (args.config, time.time() - t_gen), file=sys.stderr, flush=True)
+
+    attn_bytes = W.attn_algorithmic_bytes(a)
+    step_in_bytes = a.k_cache.nbytes + a.v_cache.nbytes + s.target_logits.nbytes + s.draft_probs.nbytes
+    copies = args.copies or max(2, int(np.ceil(3 * MALL_BYTES / step_in_bytes)) + 1)
+    copies = min(copies, 16)
+
+    def up(x, view=None):
+        t = torch.from_numpy(x).to(dev)
+        return t.view(view) if view is not None else t
+
+    sets = []
+    for _ in range(copies):
+        st = {"q": up(a.q), "table": up(a.block_table), "lens": up(a.context_lens)}
+        if a.kv_dtype == W.KV_BF16:
+            st["k"] = up(a.k_cache.view(np.int16), torch.bfloat16)
+            st["v"] = up(a.v_cache.view(np.int16), torch.bfloat16)
+        else:
+            st["k"] = up(a.k_cache)
+            st["v"] = up(a.v_cache)
+        if a.kv_dtype == W.KV_FP8_E4M3:
+            st["ks"] = up(a.k_scale)
+            st["vs"] = up(a.v_scale)
+        st["logits"] = up(s.target_logits)
+        st["probs"] = up(s.draft_probs)
+        st["tokens"] = up(s.draft_tokens)
+        st["u"] = up(s.uniforms)
+        sets.append(st)
+    out = torch.empty((a.B, a.T, a.Hq, a.d), dtype=torch.float32, device=dev)
+    ws_a = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, args.bps), dev)
+    ws_s = sv.alloc_workspace(sv.sample_workspace_size(s.B, s.K, s.V), dev)
+    n_acc = torch.empty(s.B, dtype=torch.int32, device=dev)
+    toks = torch.empty((s.B, s.K + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(st, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sv.spec_verify_attn(st["q"], st["k"], st["v"], st["table"], st["lens"], out, ws_a,
+                            k_scale=st.get("ks"), v_scale=st.get("vs"), kv_dtype=a.kv_dtype,
+                            stream=stream, algo=args.algo, blocks_per_split=args.bps)
+        if ev is not None:
+            ev[1].record(stream)
+        sv.spec_verify_sample(st["logits"], st["probs"], st["tokens"], st["u"], n_acc, toks, ws_s, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % copies])
+    torch.cuda.synchronize()
+    print("# warmup done (%d copies of %.1f MB)" % (copies, step_in_bytes / 1e6), file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % copies], evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    samp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    n_rej = int((n_acc.cpu().numpy() < s.K).sum())
+    samp_bytes = W.sample_algorithmic_bytes(s, n_rej)
+
+    attn_gbs = attn_bytes / (attn_ms.mean() * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(args.config)
+        if ent and ent.get("attn_src_sha") == attn_source_hash() and args.algo == 0 and args.bps == 0:
+            traffic = ent.get("bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_step,
+        "unit": "verify steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {W.KV_F32: "f32", W.KV_BF16: "bf16", W.KV_FP8_E4M3: "fp8e4m3"}[a.kv_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s (B=%d, Hq=%d, Hkv=%d, d=%d, ctx=%s, page 16, K=%d, %s KV, V=%d)" % (
+                args.config, cfg["desc"], a.B, a.Hq, a.Hkv, a.d, cfg["ctx"], s.K, cfg["kv"], s.V),
+            "B": a.B, "K": s.K, "V": s.V, "context": int(a.context_lens.max()),
+            "rotating_copies": copies,
+        },
+        "attn_us": float(attn_ms.mean() * 1e3),
+        "attn_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
+        "sample_us": float(samp_ms.mean() * 1e3),
+        "attn_bytes": attn_bytes,
+        "sample_bytes": samp_bytes,
+        "step_gbs": (attn_bytes + samp_bytes) / (ms_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(a, s, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(a, s, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    a subset of attention output rows and a subset of sequences through the
+    sampler, each timed and scaled to a whole step."""
+    import oracle
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+    total_rows = a.B * a.T * a.Hq
+    # calibrate on a few rows, then take as many as fit the budget
+    probe = rng.choice(total_rows, size=min(total_rows, 2 * threads), replace=False).astype(np.int64)
+    t = time.time()
+    oracle.attn(a.q, a.k_cache, a.v_cache, a.block_table, a.context_lens, kv_dtype=a.kv_dtype,
+                k_scale=a.k_scale, v_scale=a.v_scale, rows=probe, nthreads=threads)
+    per_row = max(1e-6, (time.time() - t) / len(probe))
+    n_rows = int(min(total_rows, max(len(probe), 0.7 * budget_s / per_row)))
+    rows = rng.choice(total_rows, size=n_rows, replace=False).astype(np.int64)
+    t = time.time()
+    oracle.attn(a.q, a.k_cache, a.v_cache, a.block_table, a.context_lens, kv_dtype=a.kv_dtype,
+                k_scale=a.k_scale, v_scale=a.v_scale, rows=rows, nthreads=threads)
+    t_attn = (time.time() - t) * total_rows / n_rows
+    n_seq = max(1, min(s.B, threads))
+    t = time.time()
+    oracle.sample(s.target_logits[:n_seq], s.draft_probs[:n_seq], s.draft_tokens[:n_seq], s.uniforms[:n_seq],
+                  nthreads=threads)
+    t_samp = (time.time() - t) * s.B / n_seq
+    return {
+        "value": 1.0 / (t_attn + t_samp),
+        "unit": "verify steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d attention rows and %d of %d sampler sequences, scaled to one step "
+                  "(attention %.3f s, sampler %.3f s per step)" % (n_rows, total_rows, n_seq, s.B, t_attn, t_samp),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify: the verify step of speculative
+ * decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One verify step is one spec_verify_attn call per layer (the target model
+ * scoring K+1 positions against its paged KV cache) followed by one
+ * spec_verify_sample call on the target logits (the rejection sampler that
+ * decides how many of the K draft tokens survive and draws one more token).
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers, row-major, dense, owned by the
+ *     caller.  The library never allocates, frees or retains them.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Outputs are valid once the stream has been
+ *     synchronised.  No call synchronises or reads device data on the host.
+ *   - Every call returns an sv_status.  Host-checkable preconditions are
+ *     validated before anything is enqueued; sv_last_error() then holds a
+ *     thread-local description.  Nothing aborts and no exception crosses
+ *     the ABI.
+ *   - Device-data preconditions (block ids, context lengths, token ids,
+ *     uniforms) are documented, not checked: results for violating data are
+ *     unspecified, but every index is clamped, so kernels stay in bounds.
+ *   - Workspaces: size them with the *_workspace_size queries.  Their
+ *     contents on entry do not matter (every byte read is written earlier in
+ *     the same call); calls that share a workspace must not overlap in time.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    SV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
+    SV_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement       */
+    SV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returned   */
+    SV_ERR_ALIGN = 5,       /* a pointer lacks the alignment stated for it         */
+    SV_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing  */
+} sv_status;
+
+/* Storage type of the KV cache. */
+typedef enum {
+    SV_KV_F32 = 0,       /* float32                                                */
+    SV_KV_BF16 = 1,      /* bfloat16                                               */
+    SV_KV_FP8_E4M3 = 2   /* OCP 8-bit float E4M3 ("fn": bias 7, no inf, max 448),
+                            value = decode(code) * scale[physical block]           */
+} sv_kv_dtype;
+
+/* Attention implementation (spec_verify_attn_ex only). */
+typedef enum {
+    SV_ATTN_AUTO = 0,  /* matrix cores for bf16/fp8 storage, vector ALU for fp32  */
+    SV_ATTN_VALU = 1,  /* vector-ALU kernel, any storage type                      */
+    SV_ATTN_MFMA = 2   /* matrix-core kernel (bf16 and fp8 storage only)           */
+} sv_attn_algo;
+
+int sv_abi_version(void);
+const char *sv_status_string(int status);
+/* Thread-local text of the last non-OK return on this thread ("" if none). */
+const char *sv_last_error(void);
+
+/* Zero-fills `bytes` bytes at the device pointer `workspace` on `stream` with a
+ * fill kernel (safe to capture in a HIP graph).  Optional: no call requires a
+ * zeroed workspace. */
+int spec_verify_workspace_clear(void *workspace, size_t bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_attn: paged GQA attention for the K+1 verify rows.
+ *
+ * Defines ("KV Cache + Speculative Decoding" 5.2-5.3 paging, 6.1 cached
+ * causal attention, 6.3 GQA; "Lecture 10 - Inference" 9.2):
+ * for sequence b, verify row t in [0,T) and query head h in [0,Hq),
+ *   g     = h / (Hq/Hkv)                      (query head -> KV head)
+ *   n_vis = L_b - T + 1 + t                   (L_b counts the T new tokens,
+ *                                              whose K/V are already cached)
+ *   key/value of position p < n_vis: block_table[b][p/16], slot p%16, head g
+ *   s_p   = sm_scale * <q[b,t,h,:], k_p>,  w = softmax(s),  out = sum_p w_p v_p
+ *
+ * q            [B,T,Hq,d] float32, 16-byte aligned.
+ * k_cache      [num_blocks,16,Hkv,d] in kv_dtype, 16-byte aligned (8 for fp8).
+ * v_cache      same shape and type as k_cache.
+ * k_scale      [num_blocks] float32 per-block scales; required for
+ * v_scale        SV_KV_FP8_E4M3, must be NULL otherwise.
+ * block_table  [B,max_blocks_per_seq] int32 physical block ids in
+ *              [0,num_blocks); entries at and past ceil(L_b/16) are never read.
+ * context_lens [B] int32, T <= L_b <= 16*max_blocks_per_seq.
+ * out          [B,T,Hq,d] float32, 16-byte aligned; fully overwritten.
+ * T            = K+1 verify rows per sequence, 1..16.
+ * Hq % Hkv == 0; T*(Hq/Hkv) <= 64; d in {64,128}; block_size == 16;
+ * max_blocks_per_seq <= 65536 (contexts up to 1M tokens).
+ * sm_scale     softmax scale, normally 1/sqrt(d).
+ * workspace    >= spec_verify_attn_workspace_size(...) bytes, 256-byte
+ *              aligned.
+ * Work: one attention kernel, plus a small merge kernel when a sequence's
+ * context is split across workgroups.
+ * Slots past L_b in a sequence's last block may hold anything (NaN
+ * included): they never reach the result.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int d,
+                                       int max_blocks_per_seq);
+
+int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache,
+                     const float *k_scale, const float *v_scale,
+                     const int32_t *block_table, const int32_t *context_lens,
+                     float *out,
+                     int B, int T, int Hq, int Hkv, int d, int block_size,
+                     int max_blocks_per_seq, int num_blocks, int kv_dtype,
+                     float sm_scale, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* As spec_verify_attn, with the implementation and the context split chosen
+ * by the caller (for measurement).  blocks_per_split = 0 lets the planner
+ * choose; otherwise it must be a positive multiple of 4, at most 512, with
+ * ceil(max_blocks_per_seq / blocks_per_split) <= 128.  The workspace must
+ * then hold spec_verify_attn_workspace_size_ex(..., blocks_per_split) bytes. */
+size_t spec_verify_attn_workspace_size_ex(int B, int T, int Hq, int Hkv, int d,
+                                          int max_blocks_per_seq, int blocks_per_split);
+
+int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache,
+                        const float *k_scale, const float *v_scale,
+                        const int32_t *block_table, const int32_t *context_lens,
+                        float *out,
+                        int B, int T, int Hq, int Hkv, int d, int block_size,
+                        int max_blocks_per_seq, int num_blocks, int kv_dtype,
+                        float sm_scale, void *workspace, size_t workspace_bytes,
+                        void *stream, int algo, int blocks_per_split);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_sample: the rejection sampler of the verify step.
+ *
+ * Defines ("50 | Speculative Decoding" 3.1; "KV Cache + Speculative
+ * Decoding" 7.1-7.3, 7.6): with p_i = softmax(target_logits[b,i,:]),
+ *   for i = 0..K-1, draft x_i = draft_tokens[b,i] is accepted iff
+ *     u[b,i] * q_i(x_i) < p_i(x_i)        (acceptance with min(1, p/q));
+ *   n = index of the first rejection, or K if none;
+ *   weights w = max(0, p_n - q_n) if n < K, else w = p_K (bonus);
+ *   if sum(w) == 0 (reachable only by rounding) w = p_n;
+ *   the drawn token is the smallest j with sum_{j'<=j} w_j' > u[b,K]*sum(w)
+ *   in ascending token order (the largest j with w_j > 0 if rounding leaves
+ *   none).
+ * Outputs: num_accepted[b] = n; out_tokens[b,0:n] = the accepted drafts,
+ * out_tokens[b,n] = the drawn token, out_tokens[b,n+1:] = -1.
+ *
+ * target_logits [B,K+1,V] float32 (finite), draft_probs [B,K,V] float32
+ * (>= 0, used as given), draft_tokens [B,K] int32 in [0,V), uniforms [B,K+1]
+ * float32 in [0,1): [:, :K] drive acceptance, [:, K] the final draw.
+ * num_accepted [B] int32; out_tokens [B,K+1] int32; accept_prob [B,K] float32
+ * (optional, NULL to skip) receives min(1, p_i(x_i)/q_i(x_i)) for every i.
+ * 1 <= K <= 15; V >= 1.  workspace as for attention.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_sample_workspace_size(int B, int K, int V);
+
+int spec_verify_sample(const float *target_logits, const float *draft_probs,
+                       const int32_t *draft_tokens, const float *uniforms,
+                       int32_t *num_accepted, int32_t *out_tokens, float *accept_prob,
+                       int B, int K, int V,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,161 @@
+"""Python binding of libspecverify (the speculative-decoding verify step on MI355X).
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels of ``libspecverify.so``; torch supplies device memory and the stream.
+There is no fallback: if the library is missing or a call fails, this module
+raises.
+
+Calls (same names as the C ABI in include/spec_verify.h):
+    spec_verify_attn(...)    paged GQA attention for the K+1 verify rows
+    spec_verify_sample(...)  the accept / residual / bonus rejection sampler
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK = 0
+SV_KV_F32, SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1, 2
+SV_ATTN_AUTO, SV_ATTN_VALU, SV_ATTN_MFMA = 0, 1, 2
+BLOCK_SIZE = 16
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__("%s failed with status %d: %s" % (fn, status, detail))
+        self.status = status
+
+
+def lib():
+    """The loaded library (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libspecverify.so is not built (run __graft_entry__.build() or "
+                              "python speculative_decoding_verify_attn_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        P, I, S, F = c.c_void_p, c.c_int, c.c_size_t, c.c_float
+        L.sv_abi_version.restype = I
+        L.sv_abi_version.argtypes = []
+        L.sv_status_string.restype = c.c_char_p
+        L.sv_status_string.argtypes = [I]
+        L.sv_last_error.restype = c.c_char_p
+        L.sv_last_error.argtypes = []
+        L.spec_verify_workspace_clear.restype = I
+        L.spec_verify_workspace_clear.argtypes = [P, S, P]
+        L.spec_verify_attn_workspace_size.restype = S
+        L.spec_verify_attn_workspace_size.argtypes = [I] * 6
+        L.spec_verify_attn_workspace_size_ex.restype = S
+        L.spec_verify_attn_workspace_size_ex.argtypes = [I] * 7
+        attn_args = [P] * 8 + [I] * 9 + [F, P, S, P]
+        L.spec_verify_attn.restype = I
+        L.spec_verify_attn.argtypes = attn_args
+        L.spec_verify_attn_ex.restype = I
+        L.spec_verify_attn_ex.argtypes = attn_args + [I, I]
+        L.spec_verify_sample_workspace_size.restype = S
+        L.spec_verify_sample_workspace_size.argtypes = [I] * 3
+        L.spec_verify_sample.restype = I
+        L.spec_verify_sample.argtypes = [P] * 7 + [I] * 3 + [P, S, P]
+        if L.sv_abi_version() != 1:
+            raise ImportError("libspecverify ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != SV_OK:
+        L = lib()
+        raise SpecVerifyError(fn, status, "%s (%s)" % (L.sv_status_string(status).decode(),
+                                                       L.sv_last_error().decode()))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def kv_dtype_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_KV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_KV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return SV_KV_FP8_E4M3
+    raise TypeError("unsupported KV cache dtype %s" % t.dtype)
+
+
+def attn_workspace_size(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split=0) -> int:
+    n = lib().spec_verify_attn_workspace_size_ex(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split)
+    if n == 0:
+        raise ValueError("unsupported attention shape")
+    return n
+
+
+def sample_workspace_size(B, K, V) -> int:
+    n = lib().spec_verify_sample_workspace_size(B, K, V)
+    if n == 0:
+        raise ValueError("unsupported sampler shape")
+    return n
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled device workspace (the caching allocator aligns to >= 256 B)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_clear(ws: torch.Tensor, stream=None):
+    _check("spec_verify_workspace_clear",
+           lib().spec_verify_workspace_clear(_ptr(ws), ws.numel() * ws.element_size(),
+                                             _stream_handle(stream, ws.device)))
+
+
+def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, workspace, *,
+                     k_scale=None, v_scale=None, sm_scale=None, kv_dtype=None, stream=None,
+                     algo=SV_ATTN_AUTO, blocks_per_split=0):
+    """Paged GQA verify attention (see include/spec_verify.h).
+
+    q [B,T,Hq,d] f32; k_cache/v_cache [num_blocks,16,Hkv,d] (f32, bf16, or E4M3
+    codes as uint8 / float8_e4m3fn); block_table [B,max_blocks] i32;
+    context_lens [B] i32; out [B,T,Hq,d] f32; workspace: uint8 device tensor of
+    at least attn_workspace_size(...) bytes, zero-filled before first use.
+    """
+    B, T, Hq, d = q.shape
+    num_blocks, bs, Hkv, d2 = k_cache.shape
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    if sm_scale is None:
+        sm_scale = 1.0 / (d ** 0.5)
+    _check("spec_verify_attn", lib().spec_verify_attn_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
+        kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, q.device), int(algo), int(blocks_per_split)))
+    return out
+
+
+def spec_verify_sample(target_logits, draft_probs, draft_tokens, uniforms, num_accepted, out_tokens,
+                       workspace, *, accept_prob=None, stream=None):
+    """Verify sampler (see include/spec_verify.h).
+
+    target_logits [B,K+1,V] f32, draft_probs [B,K,V] f32, draft_tokens [B,K] i32,
+    uniforms [B,K+1] f32 in [0,1); outputs num_accepted [B] i32, out_tokens
+    [B,K+1] i32, optional accept_prob [B,K] f32.
+    """
+    B, K1, V = target_logits.shape
+    _check("spec_verify_sample", lib().spec_verify_sample(
+        _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(num_accepted), _ptr(out_tokens), _ptr(accept_prob), B, K1 - 1, V,
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, target_logits.device)))
+    return num_accepted, out_tokens

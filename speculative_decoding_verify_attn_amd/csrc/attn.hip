@@ -1,0 +1,844 @@
+// attn.hip -- paged GQA verify attention for gfx950.
+//
+// What is computed ("KV Cache + Speculative Decoding" 5.2-5.3, 6.1, 6.3;
+// "Lecture 10 - Inference" 9.2): for sequence b, verify row t and query head
+// h, softmax(sm_scale * q . k_p) over the positions p <= L_b - T + t, applied
+// to v_p, where K/V of position p live in block block_table[b][p/16], slot
+// p%16, KV head h / (Hq/Hkv).
+//
+// Work decomposition (one design for the whole family of shapes):
+//   * a workgroup owns one (sequence b, KV head g) unit and one contiguous
+//     split of its context pages; all T*G query rows of the unit share every
+//     K/V byte it loads, so each cached byte is fetched once per step;
+//   * the four waves of a workgroup take interleaved 16-token pages of the
+//     split and keep independent online-softmax states, merged through LDS
+//     at the end of the split;
+//   * when a unit has several splits, each workgroup writes an unnormalised
+//     partial (o, running max, running sum) and a second, small kernel
+//     merges them (flash-decoding style).  Kernel order on the stream makes
+//     the partials visible; no device-wide fence is used (on this multi-die
+//     part such a fence writes back the L2 and costs far more than a launch).
+//
+// Matrix-core kernel (bf16 / E4M3 storage), per wave and page:
+//   * the page's K and V slices (16 slots x d) stream HBM -> LDS with direct
+//     buffer-to-LDS copies into a 4-stage ring, so three pages are in flight
+//     while one is computed and no registers hold data in flight;
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, query rows on N);
+//     each lane reads back its own K operand, Q sits in registers as bf16;
+//   * V is transposed once through LDS into a swizzled [dim][slot] tile
+//     written over the consumed K slice (conflict-free writes and reads);
+//   * S^T leaves each lane holding one query row's P for four keys, which is
+//     exactly the B operand of v_mfma_f32_16x16x16_bf16 for O^T += V^T P^T,
+//     so P needs no cross-lane shuffle; bf16 row sums come from the same
+//     instruction with an all-ones A operand.
+// Scores are kept in base-2 units (q pre-scaled by sm_scale*log2 e) and
+// exponentiated with v_exp_f32; the running maximum only moves (with a
+// rescale of the accumulators) when a score exceeds it by more than 8.
+//
+// Vector-ALU kernel: the same decomposition one page at a time through LDS,
+// with fp32 arithmetic throughout.  It serves fp32 storage and is the
+// baseline the matrix-core kernel is measured against.
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kNW = 4;  // waves per workgroup
+constexpr float kSlack = 8.0f;  // base-2 headroom before the running max is moved
+
+struct UnitWork {
+    int b, g, unit, split;
+    int L;          // clamped context length
+    int blk_begin;  // first logical block of the split
+    int blk_end;    // one past the last
+    int nsplit;     // splits of this sequence
+};
+
+// Workgroup -> (unit, split).  Workgroups are handed to the eight XCDs round
+// robin; the remap gives each XCD a contiguous range of units, so the splits
+// of one unit (and their partials) stay within one XCD's L2.
+__device__ __forceinline__ bool decode_work(const AttnParams &p, UnitWork &w)
+{
+    const int bid = blockIdx.x;
+    const int per_xcd = p.grid >> 3;
+    const int wg = (bid & 7) * per_xcd + (bid >> 3);
+    const int unit = wg / p.max_splits;
+    if (unit >= p.B * p.Hkv)
+        return false;
+    w.unit = unit;
+    w.split = wg - unit * p.max_splits;
+    w.b = unit / p.Hkv;
+    w.g = unit - w.b * p.Hkv;
+    int L = p.context_lens[w.b];
+    L = L < 0 ? 0 : (L > p.max_blocks * kBlock ? p.max_blocks * kBlock : L);
+    w.L = L;
+    const int nblk = (L + kBlock - 1) / kBlock;
+    w.blk_begin = w.split * p.bps;
+    if (w.blk_begin >= nblk)
+        return false;
+    w.blk_end = min(w.blk_begin + p.bps, nblk);
+    w.nsplit = (nblk + p.bps - 1) / p.bps;
+    return true;
+}
+
+__device__ __forceinline__ int clamp_block(int v, int n) { return v < 0 ? 0 : (v >= n ? n - 1 : v); }
+
+// Normalises and stores the workgroup's result when its unit has a single
+// split, or publishes it as an unnormalised partial (o, running max, running
+// sum) for the merge kernel.  obuf: [TG][D+4] unnormalised output in LDS;
+// mrow/lrow: per-row max (base-2 units) and sum in LDS.  Called by all
+// threads.  No fence or atomic is needed: the merge runs as the next kernel
+// on the same stream.
+template <int D>
+__device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float *obuf, const float *mrow,
+                            const float *lrow)
+{
+    constexpr int OP = D + 4;
+    constexpr int C4 = D / 4;
+    const int tid = threadIdx.x;
+    const int TG = p.TG, G = p.G;
+    if (w.nsplit == 1) {
+        for (int idx = tid; idx < TG * C4; idx += kAttnThreads) {
+            const int row = idx / C4, c4 = idx - row * C4;
+            const float inv = 1.0f / lrow[row];
+            float4 o = *reinterpret_cast<const float4 *>(obuf + row * OP + c4 * 4);
+            o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+            const int t = row / G, hh = row - t * G;
+            float *dst = p.out + (((size_t)w.b * p.T + t) * p.Hq + (size_t)w.g * G + hh) * D + c4 * 4;
+            *reinterpret_cast<float4 *>(dst) = o;
+        }
+        return;
+    }
+    const size_t base = ((size_t)w.unit * p.max_splits + w.split) * TG;
+    for (int idx = tid; idx < TG * C4; idx += kAttnThreads) {
+        const int row = idx / C4, c4 = idx - row * C4;
+        *reinterpret_cast<float4 *>(p.part_o + (base + row) * D + c4 * 4) =
+            *reinterpret_cast<const float4 *>(obuf + row * OP + c4 * 4);
+    }
+    for (int row = tid; row < TG; row += kAttnThreads)
+        reinterpret_cast<float2 *>(p.part_ml)[base + row] = make_float2(mrow[row], lrow[row]);
+}
+
+// Split merge (flash-decoding second pass): one wave per (unit, row).
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s o_s 2^(m_s - M) / L.
+// Lanes first hold one split each (statistics, reduced with DPP), then
+// slices of the head dim; eight splits' partial rows are in flight at once.
+template <int D>
+__global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
+{
+    constexpr int PER = D / 64;  // floats per lane
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int units = p.B * p.Hkv;
+    if (gw >= units * p.TG)
+        return;
+    const int unit = gw / p.TG, row = gw - unit * p.TG;
+    const int b = unit / p.Hkv, g = unit - b * p.Hkv;
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.max_blocks * kBlock ? p.max_blocks * kBlock : L);
+    const int nblk = (L + kBlock - 1) / kBlock;
+    const int ns = (nblk + p.bps - 1) / p.bps;
+    if (ns <= 1)
+        return;  // written directly by the attention kernel
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + (size_t)unit * p.max_splits * p.TG + row;
+    const float ninf = -__builtin_inff();
+    float M = ninf;
+    for (int s = lane; s < ns; s += kWave)
+        M = fmaxf(M, ml[(size_t)s * p.TG].x);
+    M = wave_max_f32(M);
+    double Lsum = 0.0;
+    for (int s = lane; s < ns; s += kWave) {
+        const float2 v = ml[(size_t)s * p.TG];
+        if (v.x != ninf)
+            Lsum += (double)(v.y * __builtin_amdgcn_exp2f(v.x - M));
+    }
+    const float inv = (float)(1.0 / wave_sum_f64(Lsum));
+    const float *po = p.part_o + ((size_t)unit * p.max_splits * p.TG + row) * D + lane * PER;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        acc[k] = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float o[8][PER];
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = s0 + j;
+            f[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                o[j][k] = 0.0f;
+            if (s < ns) {
+                const float ms = ml[(size_t)s * p.TG].x;
+                f[j] = (ms == ninf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+                if constexpr (PER == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(po + (size_t)s * p.TG * D);
+                    o[j][0] = v.x;
+                    o[j][1] = v.y;
+                } else {
+                    o[j][0] = po[(size_t)s * p.TG * D];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                acc[k] += f[j] * o[j][k];
+    }
+    const int t = row / p.G, hh = row - t * p.G;
+    float *dst = p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hh) * D + lane * PER;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        dst[k] = acc[k] * inv;
+}
+
+// ---------------------------------------------------------------- MFMA kernel
+
+// Swizzled row of head dim `dim` in a transposed V tile: rows are grouped by
+// eight, and inside a group the row index is XORed with the group index.
+__device__ __forceinline__ int vt_row(int dim) { return (dim & ~7) | ((dim & 7) ^ ((dim >> 3) & 7)); }
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (V#) of one physical page of one tensor, as four SGPRs:
+// base, stride 0, num_records = page bytes, raw 32-bit data format (gfx9
+// family word 3).  Reads outside the page return zero.
+__device__ __forceinline__ int4v page_desc(const unsigned char *base, int page, uint32_t page_bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base) + (uint64_t)page * page_bytes;
+    int4v r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r.z = (int)page_bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
+// Direct HBM -> LDS copy (gfx950 buffer_load ... lds): every lane moves BYTES
+// bytes from desc + voff + soff to LDS address lds + lane * BYTES.  Issued
+// from inline assembly so that the kernel, not the compiler, decides how
+// many copies stay in flight; completion is awaited with wait_dma<N>().
+// m0 holds the LDS address of the copy; no other instruction in these
+// kernels reads m0.  lgkmcnt(0) first: the copy may overwrite LDS that this
+// wave has only just finished reading.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(uint32_t lds, int4v desc, int voff, int soff)
+{
+    if constexpr (BYTES == 16)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+}
+
+// Waits until at most N of this wave's memory loads are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// Eight stored values -> four packed bf16 pairs.
+__device__ __forceinline__ uint4 to_bf16x8(uint4 v) { return v; }
+__device__ __forceinline__ uint4 to_bf16x8(uint2 v)
+{
+    const uint2 lo = e4m3x4_to_bf16x4(v.x);
+    const uint2 hi = e4m3x4_to_bf16x4(v.y);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Geometry of one 16-token page of one KV head as it travels HBM -> LDS.
+//   K: lane l = (slot l%16, lane group q4 = l/16) carries the A operand of
+//      S^T = K Q^T for every 32-wide head-dim chunk dc (eight dims per lane).
+//      bf16: one 16-byte copy per chunk; E4M3: one 16-byte copy carries two
+//      chunks (sixteen dims), so the chunk -> dim map is permuted the same way
+//      on the Q side.
+//   V: lane l carries VS consecutive slots x (8 * DG) dims, which the lane
+//      transposes into the [dim][slot] bf16 tile the PV product reads.
+template <int D, bool FP8>
+struct PageGeom {
+    static constexpr int EB = FP8 ? 1 : 2;
+    static constexpr int PT = 16 * D * EB;        // bytes of one tensor's page slice
+    static constexpr int STAGE = 2 * PT;           // K slice, then V slice
+    static constexpr int NDC = D / 32;            // MFMA chunks of the head dim
+    static constexpr int NKI = FP8 ? D / 64 : D / 32;  // 16-byte K copies per page
+    // V copies
+    static constexpr int VBYTES = (FP8 && D == 64) ? 4 : 16;  // bytes per lane per copy
+    static constexpr int NVI = PT / (64 * VBYTES);            // copies per page
+    static constexpr int VS = FP8 ? (D == 64 ? 4 : 2) : (D == 128 ? 4 : 2);  // slots per lane
+    static constexpr int DG = FP8 ? (D == 64 ? 0 : 2) : 1;    // 8-dim groups per lane (0: four dims)
+    static constexpr int NI = NKI + NVI;                      // copies per page
+    // first head dim of lane group q4 in MFMA chunk dc
+    static __device__ __forceinline__ int qdim(int dc, int q4)
+    {
+        return FP8 ? (dc >> 1) * 64 + q4 * 16 + (dc & 1) * 8 : dc * 32 + q4 * 8;
+    }
+};
+
+template <int D, int RG, bool FP8>
+__global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParams p)
+{
+    typedef PageGeom<D, FP8> PG;
+    constexpr int NDC = PG::NDC;
+    constexpr int NDT = D / 16;          // 16-wide dim tiles of PV
+    constexpr int NS = 4;                // LDS stages per wave (pages in flight + 1)
+    constexpr int EB = PG::EB;
+    constexpr int OP = D + 4;
+    constexpr int RING = kNW * NS * PG::STAGE;
+    constexpr int OBUF_BYTES = RG * 16 * OP * 4;
+    // smem holds, in turn: the waves' page rings, then the merged output tile.
+    constexpr int SMEM = RING > OBUF_BYTES ? RING : OBUF_BYTES;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    __shared__ float s_m[kNW][64], s_l[kNW][64], s_mrow[64], s_lrow[64];
+    __shared__ int s_pages[kMaxBps];
+
+    UnitWork w;
+    if (!decode_work(p, w))
+        return;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int lane = tid & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int T = p.T, G = p.G, TG = p.TG, Hkv = p.Hkv;
+    const int L = w.L;
+    const int npg = w.blk_end - w.blk_begin;
+    const float ninf = -__builtin_inff();
+
+    // physical pages of this split, fetched once with one coalesced read
+    for (int i = tid; i < npg; i += kAttnThreads)
+        s_pages[i] = clamp_block(p.block_table[(size_t)w.b * p.max_blocks + w.blk_begin + i], p.num_blocks);
+
+    // Q tile of this unit as the B operand of S^T = K Q^T (row = l16, eight dims).
+    bf16x8 qf[RG][NDC];
+    int lim[RG];
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt) {
+        const int row = rt * 16 + l16;
+        const bool valid = row < TG;
+        const int t = valid ? row / G : T - 1;
+        const int hh = valid ? row - (row / G) * G : 0;
+        lim[rt] = L - T + t;
+        const float *src = p.q + (((size_t)w.b * T + t) * p.Hq + (size_t)w.g * G + hh) * D;
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+            if (valid) {
+                a = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4));
+                c = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4) + 4);
+            }
+            const float sc = p.qscale;
+            uint4 u;
+            u.x = f32x2_to_bf16x2(a.x * sc, a.y * sc);
+            u.y = f32x2_to_bf16x2(a.z * sc, a.w * sc);
+            u.z = f32x2_to_bf16x2(c.x * sc, c.y * sc);
+            u.w = f32x2_to_bf16x2(c.z * sc, c.w * sc);
+            qf[rt][dc] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+    __syncthreads();  // s_pages ready
+
+    // Running state per row tile: reference maximum m (base-2 units), the
+    // row sums and the unnormalised outputs O^T (lane: dims 4*q4+i of tile
+    // dt, row l16).  bf16 storage gets its row sums from one extra MFMA with
+    // an all-ones A operand; E4M3 storage scales P per page, so it sums P on
+    // the VALU.
+    float m[RG], lpart[RG];
+    floatx4 lsum[RG];
+    floatx4 acc[NDT][RG];
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt) {
+        m[rt] = ninf;
+        lpart[rt] = 0.0f;
+        lsum[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            acc[dt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const short4v ones4 = __builtin_bit_cast(short4v, make_uint2(0x3F803F80u, 0x3F803F80u));
+
+    const unsigned char *kbase = static_cast<const unsigned char *>(p.k_cache);
+    const unsigned char *vbase = static_cast<const unsigned char *>(p.v_cache);
+    const int slot_stride = Hkv * D * EB;                          // bytes between slots of a page
+    const uint32_t page_bytes = (uint32_t)slot_stride * kBlock;    // bytes of one page (all heads)
+    const int head_off = w.g * D * EB;
+    // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
+    const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
+    // V copy: lane -> slot group va (VS slots), dim group vc
+    int vc, va, v_voff;
+    if constexpr (PG::VBYTES == 4) {           // E4M3, d = 64: four dims per lane, four slots
+        vc = lane & 15;
+        va = lane >> 4;
+        v_voff = head_off + (va * 4) * slot_stride + vc * 4;
+    } else if constexpr (FP8) {                 // E4M3, d = 128: sixteen dims, two slots
+        vc = lane & 7;
+        va = lane >> 3;
+        v_voff = head_off + (va * 2) * slot_stride + vc * 16;
+    } else {                                    // bf16: eight dims, VS slots
+        vc = lane % (D / 8);
+        va = lane / (D / 8);
+        v_voff = head_off + (va * PG::VS) * slot_stride + vc * 16;
+    }
+    const uint32_t ring_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * NS * PG::STAGE;
+    unsigned char *ring = smem + wave * NS * PG::STAGE;
+
+    // This wave's pages are w.blk_begin + wave + k*kNW, k = 0, 1, ...
+    const int nk = npg > wave ? (npg - wave + kNW - 1) / kNW : 0;
+    auto issue = [&](int k) {
+        const int ph = s_pages[wave + k * kNW];
+        const int stage = k % NS;
+        const uint32_t lds = ring_lds + stage * PG::STAGE;
+        const int4v dk = page_desc(kbase, __builtin_amdgcn_readfirstlane(ph), page_bytes);
+        const int4v dv = page_desc(vbase, __builtin_amdgcn_readfirstlane(ph), page_bytes);
+#pragma unroll
+        for (int i = 0; i < PG::NKI; ++i)
+            dma_to_lds<16>(lds + i * 1024, dk, k_voff, FP8 ? i * 64 : i * 32 * EB);
+#pragma unroll
+        for (int j = 0; j < PG::NVI; ++j)
+            dma_to_lds<PG::VBYTES>(lds + PG::PT + j * 64 * PG::VBYTES, dv, v_voff,
+                                   (PG::VBYTES == 4 || FP8) ? j * slot_stride : j * slot_stride);
+    };
+    for (int k = 0; k < NS - 1 && k < nk; ++k)
+        issue(k);
+
+    for (int k = 0; k < nk; ++k) {
+        if (k + NS - 1 < nk)
+            issue(k + NS - 1);
+        // wait for page k: the copies of up to NS-1 younger pages may stay in flight
+        const int younger = (nk - 1 - k) < (NS - 1) ? (nk - 1 - k) : (NS - 1);
+        if (younger >= 3)
+            wait_dma<3 * PG::NI>();
+        else if (younger == 2)
+            wait_dma<2 * PG::NI>();
+        else if (younger == 1)
+            wait_dma<PG::NI>();
+        else
+            wait_dma<0>();
+        const int pg = wave + k * kNW;
+        const int key0 = (w.blk_begin + pg) * kBlock;
+        const int ph = s_pages[pg];
+        unsigned char *st = ring + (k % NS) * PG::STAGE;
+
+        // 1. S^T = K Q^T (keys on M, rows on N); K operands read back from LDS.
+        floatx4 s[RG];
+#pragma unroll
+        for (int rt = 0; rt < RG; ++rt)
+            s[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < PG::NKI; ++i) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(st + i * 1024 + lane * 16);
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(raw.x, raw.y)));
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(raw.z, raw.w)));
+#pragma unroll
+                for (int rt = 0; rt < RG; ++rt) {
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[rt][2 * i], s[rt], 0, 0, 0);
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[rt][2 * i + 1], s[rt], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) {
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(st + dc * 1024 + lane * 16));
+#pragma unroll
+                for (int rt = 0; rt < RG; ++rt)
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][dc], s[rt], 0, 0, 0);
+            }
+        }
+
+        // 2. V slice -> registers -> transposed, swizzled bf16 tile [dim][slot]
+        //    written over this stage (K has been read).
+        const bool tail = key0 + kBlock > L;
+        if constexpr (PG::VBYTES == 4) {
+            uint32_t raw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                raw[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + j * 256 + lane * 4);
+            uint2 wv[4];  // slot j: four dims as bf16
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wv[j] = e4m3x4_to_bf16x4(raw[j]);
+                if (tail && key0 + va * 4 + j >= L)
+                    wv[j] = make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                const int de = vc * 4 + 2 * wd;
+                const uint32_t e0 = (&wv[0].x)[wd], e1 = (&wv[1].x)[wd], e2 = (&wv[2].x)[wd], e3 = (&wv[3].x)[wd];
+                *reinterpret_cast<uint2 *>(st + vt_row(de) * 32 + va * 8) = make_uint2(pack_lo16(e0, e1), pack_lo16(e2, e3));
+                *reinterpret_cast<uint2 *>(st + vt_row(de + 1) * 32 + va * 8) = make_uint2(pack_hi16(e0, e1), pack_hi16(e2, e3));
+            }
+        } else if constexpr (FP8) {
+            uint4 raw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                raw[j] = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
+            uint4 wv[2][2];  // [slot j][dim group g] bf16
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                wv[j][0] = to_bf16x8(make_uint2(raw[j].x, raw[j].y));
+                wv[j][1] = to_bf16x8(make_uint2(raw[j].z, raw[j].w));
+                if (tail && key0 + va * 2 + j >= L)
+                    wv[j][0] = wv[j][1] = make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const int de = vc * 16 + g * 8 + 2 * wd;
+                    const uint32_t e0 = (&wv[0][g].x)[wd], e1 = (&wv[1][g].x)[wd];
+                    *reinterpret_cast<uint32_t *>(st + vt_row(de) * 32 + va * 4) = pack_lo16(e0, e1);
+                    *reinterpret_cast<uint32_t *>(st + vt_row(de + 1) * 32 + va * 4) = pack_hi16(e0, e1);
+                }
+        } else {
+            constexpr int VS = PG::VS;
+            uint4 wv[VS];
+#pragma unroll
+            for (int j = 0; j < VS; ++j) {
+                wv[j] = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
+                if (tail && key0 + va * VS + j >= L)
+                    wv[j] = make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const int de = vc * 8 + 2 * wd;
+                const uint32_t e0 = (&wv[0].x)[wd], e1 = (&wv[1].x)[wd];
+                if constexpr (VS == 4) {
+                    const uint32_t e2 = (&wv[2].x)[wd], e3 = (&wv[3].x)[wd];
+                    *reinterpret_cast<uint2 *>(st + vt_row(de) * 32 + va * 8) =
+                        make_uint2(pack_lo16(e0, e1), pack_lo16(e2, e3));
+                    *reinterpret_cast<uint2 *>(st + vt_row(de + 1) * 32 + va * 8) =
+                        make_uint2(pack_hi16(e0, e1), pack_hi16(e2, e3));
+                } else {
+                    *reinterpret_cast<uint32_t *>(st + vt_row(de) * 32 + va * 4) = pack_lo16(e0, e1);
+                    *reinterpret_cast<uint32_t *>(st + vt_row(de + 1) * 32 + va * 4) = pack_hi16(e0, e1);
+                }
+            }
+        }
+
+        float vsc = 1.0f;
+        if constexpr (FP8) {
+            const float ksc = p.k_scale[ph];
+            vsc = p.v_scale[ph];
+#pragma unroll
+            for (int rt = 0; rt < RG; ++rt)
+                s[rt] *= ksc;
+        }
+        // 3. Causal / length mask (only the last pages of a sequence need it).
+        if (key0 + kBlock - 1 > L - T) {
+#pragma unroll
+            for (int rt = 0; rt < RG; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (key0 + q4 * 4 + i > lim[rt])
+                        s[rt][i] = ninf;
+        }
+        // 4. Online softmax.  The common path only checks that no score of
+        //    this lane exceeds its row's reference maximum by more than
+        //    kSlack; only then (a wave-uniform, rarely taken branch) are the
+        //    row maxima reduced across lanes and the accumulators rescaled.
+        //    So P = 2^(s - m) <= 2^kSlack always.
+        float mloc[RG];
+        bool need = false;
+#pragma unroll
+        for (int rt = 0; rt < RG; ++rt) {
+            mloc[rt] = fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
+            need = need || (mloc[rt] > m[rt] + kSlack);
+        }
+        if (__builtin_expect(__ballot(need) != 0, 0)) {
+            __asm__ volatile("" ::: "memory");  // keep this block a real branch
+#pragma unroll
+            for (int rt = 0; rt < RG; ++rt) {
+                float mx = mloc[rt];
+                mx = fmaxf(mx, xor_lane_f32(mx, 16));
+                mx = fmaxf(mx, xor_lane_f32(mx, 32));
+                const float mnew = fmaxf(m[rt], mx);
+                const float alpha = (mnew == ninf) ? 1.0f : __builtin_amdgcn_exp2f(m[rt] - mnew);
+                m[rt] = mnew;
+                lpart[rt] *= alpha;
+                lsum[rt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    acc[dt][rt] *= alpha;
+            }
+        }
+        short4v pb[RG];
+#pragma unroll
+        for (int rt = 0; rt < RG; ++rt) {
+            const float msafe = (m[rt] == ninf) ? 0.0f : m[rt];
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pr[i] = __builtin_amdgcn_exp2f(s[rt][i] - msafe);
+            if constexpr (FP8)
+                lpart[rt] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            pb[rt] = __builtin_bit_cast(short4v, make_uint2(f32x2_to_bf16x2(pr[0] * vsc, pr[1] * vsc),
+                                                             f32x2_to_bf16x2(pr[2] * vsc, pr[3] * vsc)));
+        }
+        // 5. O^T += V^T P^T over the page's 16 keys: A = V^T (dim l16, slots
+        //    4*q4..+3), B = P^T (slots 4*q4..+3, row l16), exactly the S^T
+        //    output layout.
+        short4v va4[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            va4[dt] = __builtin_bit_cast(short4v, *reinterpret_cast<const uint2 *>(st + vt_row(dt * 16 + l16) * 32 + q4 * 8));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rt = 0; rt < RG; ++rt)
+                acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[dt], pb[rt], acc[dt][rt], 0, 0, 0);
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int rt = 0; rt < RG; ++rt)
+                lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb[rt], lsum[rt], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four waves of the workgroup (LDS) ----
+    wait_dma<0>();
+    __syncthreads();  // every wave is done with its ring; smem becomes obuf
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt) {
+        float ls;
+        if constexpr (FP8) {
+            ls = lpart[rt];
+            ls += xor_lane_f32(ls, 16);
+            ls += xor_lane_f32(ls, 32);
+        } else {
+            ls = lsum[rt][0];
+        }
+        if (q4 == 0) {
+            s_m[wave][rt * 16 + l16] = m[rt];
+            s_l[wave][rt * 16 + l16] = ls;
+        }
+    }
+    __syncthreads();
+    float fac[RG];
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt) {
+        const int row = rt * 16 + l16;
+        float M = s_m[0][row];
+#pragma unroll
+        for (int v2 = 1; v2 < kNW; ++v2)
+            M = fmaxf(M, s_m[v2][row]);
+        fac[rt] = (m[rt] == ninf) ? 0.0f : __builtin_amdgcn_exp2f(m[rt] - M);
+        if (wave == 0 && q4 == 0) {
+            float Ls = 0.0f;
+#pragma unroll
+            for (int v2 = 0; v2 < kNW; ++v2)
+                if (s_m[v2][row] != ninf)
+                    Ls += s_l[v2][row] * __builtin_amdgcn_exp2f(s_m[v2][row] - M);
+            s_mrow[row] = M;
+            s_lrow[row] = Ls;
+        }
+    }
+    float *obuf = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int v2 = 0; v2 < kNW; ++v2) {
+        if (wave == v2) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int rt = 0; rt < RG; ++rt) {
+                    float4 *dst = reinterpret_cast<float4 *>(obuf + (rt * 16 + l16) * OP + dt * 16 + q4 * 4);
+                    const floatx4 a = acc[dt][rt] * fac[rt];
+                    if (v2 == 0) {
+                        *dst = make_float4(a[0], a[1], a[2], a[3]);
+                    } else {
+                        float4 o = *dst;
+                        o.x += a[0]; o.y += a[1]; o.z += a[2]; o.w += a[3];
+                        *dst = o;
+                    }
+                }
+        }
+        __syncthreads();
+    }
+    finish_unit<D>(p, w, obuf, s_mrow, s_lrow);
+}
+
+// ---------------------------------------------------------------- VALU kernel
+
+template <int KVT>
+__device__ __forceinline__ float load_kv(const void *base, size_t idx)
+{
+    if constexpr (KVT == 0) {
+        return static_cast<const float *>(base)[idx];
+    } else if constexpr (KVT == 1) {
+        return bf16_bits_to_f32(static_cast<const uint16_t *>(base)[idx]);
+    } else {
+        const uint32_t code = static_cast<const uint8_t *>(base)[idx];
+        return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+    }
+}
+
+template <int D, int KVT>
+__global__ __launch_bounds__(kAttnThreads) void sv_attn_valu_kernel(AttnParams p)
+{
+    constexpr int OP = D + 4;
+    constexpr int KP = D + 1;
+    constexpr int PER = (kMaxRows * D + kAttnThreads - 1) / kAttnThreads;
+    __shared__ __attribute__((aligned(16))) float s_q[kMaxRows * OP];  // later: obuf
+    __shared__ float s_k[kBlock * KP], s_v[kBlock * D], s_p[kMaxRows * (kBlock + 1)];
+    __shared__ float s_alpha[kMaxRows], s_mrow[64], s_lrow[64];
+
+    UnitWork w;
+    if (!decode_work(p, w))
+        return;
+    const int tid = threadIdx.x;
+    const int T = p.T, G = p.G, TG = p.TG, Hkv = p.Hkv;
+    const int L = w.L;
+    const float ninf = -__builtin_inff();
+
+    for (int idx = tid; idx < TG * D; idx += kAttnThreads) {
+        const int row = idx / D, col = idx - row * D;
+        const int t = row / G, hh = row - t * G;
+        s_q[row * OP + col] = p.q[(((size_t)w.b * T + t) * p.Hq + (size_t)w.g * G + hh) * D + col] * p.qscale;
+    }
+    float o[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        o[k] = 0.0f;
+    float m_row = ninf, l_row = 0.0f;  // owned by thread `row` < TG
+    const int32_t *table = p.block_table + (size_t)w.b * p.max_blocks;
+
+    for (int lb = w.blk_begin; lb < w.blk_end; ++lb) {
+        const int ph = clamp_block(table[lb], p.num_blocks);
+        float ks = 1.0f, vs = 1.0f;
+        if constexpr (KVT == 2) {
+            ks = p.k_scale[ph];
+            vs = p.v_scale[ph];
+        }
+        __syncthreads();  // previous page fully consumed
+        for (int idx = tid; idx < kBlock * D; idx += kAttnThreads) {
+            const int s = idx / D, col = idx - s * D;
+            const size_t e = (((size_t)ph * kBlock + s) * Hkv + w.g) * D + col;
+            const bool ok = lb * kBlock + s < L;
+            s_k[s * KP + col] = ok ? load_kv<KVT>(p.k_cache, e) * ks : 0.0f;
+            s_v[s * D + col] = ok ? load_kv<KVT>(p.v_cache, e) * vs : 0.0f;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < TG * kBlock; idx += kAttnThreads) {
+            const int row = idx >> 4, key = idx & 15;
+            float dot = 0.0f;
+#pragma unroll 8
+            for (int col = 0; col < D; ++col)
+                dot += s_q[row * OP + col] * s_k[key * KP + col];
+            const int pos = lb * kBlock + key;
+            s_p[row * (kBlock + 1) + key] = (pos <= L - T + row / G) ? dot : ninf;
+        }
+        __syncthreads();
+        if (tid < TG) {
+            float mx = ninf;
+            for (int key = 0; key < kBlock; ++key)
+                mx = fmaxf(mx, s_p[tid * (kBlock + 1) + key]);
+            const float mnew = fmaxf(m_row, mx);
+            const float msafe = (mnew == ninf) ? 0.0f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m_row - msafe);
+            float ps = 0.0f;
+            for (int key = 0; key < kBlock; ++key) {
+                const float pv = __builtin_amdgcn_exp2f(s_p[tid * (kBlock + 1) + key] - msafe);
+                s_p[tid * (kBlock + 1) + key] = pv;
+                ps += pv;
+            }
+            l_row = l_row * alpha + ps;
+            m_row = mnew;
+            s_alpha[tid] = alpha;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * kAttnThreads;
+            if (idx < TG * D) {
+                const int row = idx / D, col = idx - row * D;
+                float a = o[k] * s_alpha[row];
+#pragma unroll
+                for (int key = 0; key < kBlock; ++key)
+                    a += s_p[row * (kBlock + 1) + key] * s_v[key * D + col];
+                o[k] = a;
+            }
+        }
+    }
+    __syncthreads();
+    float *obuf = s_q;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int idx = tid + k * kAttnThreads;
+        if (idx < TG * D) {
+            const int row = idx / D, col = idx - row * D;
+            obuf[row * OP + col] = o[k];
+        }
+    }
+    if (tid < TG) {
+        s_mrow[tid] = m_row;
+        s_lrow[tid] = l_row;
+    }
+    __syncthreads();
+    finish_unit<D>(p, w, obuf, s_mrow, s_lrow);
+}
+
+template <typename Kernel>
+hipError_t launch(Kernel k, const AttnParams &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k, dim3(p.grid), dim3(kAttnThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_mfma_d(const AttnParams &p, hipStream_t s)
+{
+    const int rg = (p.TG + 15) / 16;
+    switch (rg) {
+    case 1: return launch(sv_attn_mfma_kernel<D, 1, FP8>, p, s);
+    case 2: return launch(sv_attn_mfma_kernel<D, 2, FP8>, p, s);
+    case 3: return launch(sv_attn_mfma_kernel<D, 3, FP8>, p, s);
+    default: return launch(sv_attn_mfma_kernel<D, 4, FP8>, p, s);
+    }
+}
+
+template <int D>
+hipError_t launch_valu_d(const AttnParams &p, int kv, hipStream_t s)
+{
+    switch (kv) {
+    case 0: return launch(sv_attn_valu_kernel<D, 0>, p, s);
+    case 1: return launch(sv_attn_valu_kernel<D, 1>, p, s);
+    default: return launch(sv_attn_valu_kernel<D, 2>, p, s);
+    }
+}
+
+hipError_t launch_merge(const AttnParams &p, hipStream_t stream)
+{
+    if (p.max_splits <= 1)
+        return hipSuccess;
+    const long long waves = (long long)p.B * p.Hkv * p.TG;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (p.d == 64)
+        hipLaunchKernelGGL(sv_attn_merge_kernel<64>, grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(sv_attn_merge_kernel<128>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnParams &p, int kv_dtype, hipStream_t stream)
+{
+    const bool fp8 = kv_dtype == 2;
+    hipError_t e;
+    if (p.d == 64)
+        e = fp8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
+    else
+        e = fp8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
+    return e != hipSuccess ? e : launch_merge(p, stream);
+}
+
+hipError_t launch_attn_valu(const AttnParams &p, int kv_dtype, hipStream_t stream)
+{
+    const hipError_t e = p.d == 64 ? launch_valu_d<64>(p, kv_dtype, stream) : launch_valu_d<128>(p, kv_dtype, stream);
+    return e != hipSuccess ? e : launch_merge(p, stream);
+}
+
+}  // namespace sv

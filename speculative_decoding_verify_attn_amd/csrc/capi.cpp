@@ -1,0 +1,327 @@
+// capi.cpp -- the C ABI of libspecverify: argument validation, the split
+// planner, workspace layout and kernel dispatch on the caller's stream.
+// Nothing here reads device memory, synchronises, or allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/spec_verify.h"
+#include "sv_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return SV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+namespace sv {
+
+// Context split.  A workgroup streams its pages through a deep LDS pipeline,
+// so it wants long splits; the grid wants at least one workgroup per compute
+// unit (256).  Splits are multiples of 4 pages (one per wave) and at most
+// kMaxBps pages, which also bounds ragged batches' longest workgroups.
+AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, int bps_request)
+{
+    AttnPlan pl{};
+    const long long units = (long long)B * Hkv;
+    int bps;
+    if (bps_request > 0) {
+        bps = bps_request;
+    } else {
+        const long long target_wgs = 256;
+        long long splits = (target_wgs + units - 1) / units;
+        if (splits < 1)
+            splits = 1;
+        bps = ceil_div(max_blocks, splits);
+        bps = ((bps + 3) / 4) * 4;
+        if (bps > kMaxBps)
+            bps = kMaxBps;
+        if (bps < 4)
+            bps = 4;
+    }
+    pl.bps = bps;
+    pl.max_splits = ceil_div(max_blocks, bps);
+    const int TG = T * (Hq / Hkv);
+    size_t off = 0;
+    pl.off_part_o = off;
+    if (pl.max_splits > 1) {
+        off = align256(off + (size_t)units * pl.max_splits * TG * d * 4);
+        pl.off_part_ml = off;
+        off = align256(off + (size_t)units * pl.max_splits * TG * 2 * 4);
+    } else {
+        pl.off_part_ml = off;
+    }
+    pl.total = off > 256 ? off : 256;
+    return pl;
+}
+
+SamplePlan plan_sample(int B, int K, int V)
+{
+    SamplePlan pl{};
+    pl.nchunk = ceil_div(V, kSampleChunk);
+    size_t off = 0;
+    pl.off_state = off;
+    off = align256(off + (size_t)B * 16);
+    pl.off_stats = off;
+    off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 16);
+    pl.off_mass = off;
+    off = align256(off + (size_t)B * pl.nchunk * 2 * 8);
+    pl.total = off;
+    return pl;
+}
+
+}  // namespace sv
+
+namespace {
+
+int check_attn_shape(int B, int T, int Hq, int Hkv, int d, int max_blocks)
+{
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || max_blocks < 1)
+        return fail(SV_ERR_SHAPE, "B, T, Hq, Hkv and max_blocks_per_seq must be >= 1 (got %d, %d, %d, %d, %d)",
+                    B, T, Hq, Hkv, max_blocks);
+    if (T > 16)
+        return fail(SV_ERR_SHAPE, "T = K+1 must be <= 16 (got %d)", T);
+    if (Hq % Hkv)
+        return fail(SV_ERR_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (T * (Hq / Hkv) > sv::kMaxRows)
+        return fail(SV_ERR_UNSUPPORTED, "T*(Hq/Hkv) = %d exceeds %d", T * (Hq / Hkv), sv::kMaxRows);
+    if (d != 64 && d != 128)
+        return fail(SV_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+    if ((long long)max_blocks * sv::kBlock > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "max_blocks_per_seq too large");
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char *sv_status_string(int status)
+{
+    switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "null pointer";
+    case SV_ERR_SHAPE: return "bad shape";
+    case SV_ERR_UNSUPPORTED: return "unsupported";
+    case SV_ERR_WORKSPACE: return "workspace too small";
+    case SV_ERR_ALIGN: return "misaligned pointer";
+    case SV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *sv_last_error(void) { return g_err; }
+
+int spec_verify_workspace_clear(void *workspace, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return ok();
+    if (!workspace)
+        return fail(SV_ERR_NULL, "workspace is NULL");
+    const hipError_t e = sv::launch_clear(workspace, bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t spec_verify_attn_workspace_size_ex(int B, int T, int Hq, int Hkv, int d, int max_blocks_per_seq,
+                                          int blocks_per_split)
+{
+    if (check_attn_shape(B, T, Hq, Hkv, d, max_blocks_per_seq) != SV_OK)
+        return 0;
+    if (blocks_per_split < 0 || (blocks_per_split > 0 && blocks_per_split % 4) || blocks_per_split > sv::kMaxBps)
+        return 0;
+    if (blocks_per_split > 0 && ceil_div(max_blocks_per_seq, blocks_per_split) > sv::kMaxSplits)
+        return 0;
+    if (ceil_div(max_blocks_per_seq, sv::kMaxBps) > sv::kMaxSplits)
+        return 0;
+    return sv::plan_attention(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split).total;
+}
+
+size_t spec_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int d, int max_blocks_per_seq)
+{
+    return spec_verify_attn_workspace_size_ex(B, T, Hq, Hkv, d, max_blocks_per_seq, 0);
+}
+
+int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                        const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
+                        float *out, int B, int T, int Hq, int Hkv, int d, int block_size,
+                        int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale, void *workspace,
+                        size_t workspace_bytes, void *stream, int algo, int blocks_per_split)
+{
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+        return fail(SV_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and out must be non-NULL");
+    int st = check_attn_shape(B, T, Hq, Hkv, d, max_blocks_per_seq);
+    if (st != SV_OK)
+        return st;
+    if (block_size != sv::kBlock)
+        return fail(SV_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+    if (num_blocks < 1)
+        return fail(SV_ERR_SHAPE, "num_blocks must be >= 1 (got %d)", num_blocks);
+    if (kv_dtype != SV_KV_F32 && kv_dtype != SV_KV_BF16 && kv_dtype != SV_KV_FP8_E4M3)
+        return fail(SV_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+    const bool fp8 = kv_dtype == SV_KV_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale))
+        return fail(SV_ERR_NULL, "k_scale and v_scale are required for E4M3 storage");
+    if (!fp8 && (k_scale || v_scale))
+        return fail(SV_ERR_SHAPE, "k_scale / v_scale must be NULL unless kv_dtype is E4M3");
+    if (!(std::isfinite(sm_scale)) || sm_scale <= 0.0f)
+        return fail(SV_ERR_SHAPE, "sm_scale must be finite and positive");
+    if (algo != SV_ATTN_AUTO && algo != SV_ATTN_VALU && algo != SV_ATTN_MFMA)
+        return fail(SV_ERR_UNSUPPORTED, "unknown algo %d", algo);
+    if (algo == SV_ATTN_MFMA && kv_dtype == SV_KV_F32)
+        return fail(SV_ERR_UNSUPPORTED, "the matrix-core kernel needs bf16 or E4M3 storage");
+    if (blocks_per_split < 0 || (blocks_per_split > 0 && blocks_per_split % 4))
+        return fail(SV_ERR_SHAPE, "blocks_per_split must be 0 or a positive multiple of 4 (got %d)", blocks_per_split);
+    if (blocks_per_split > sv::kMaxBps)
+        return fail(SV_ERR_SHAPE, "blocks_per_split must be <= %d (got %d)", sv::kMaxBps, blocks_per_split);
+    if (blocks_per_split > 0 && ceil_div(max_blocks_per_seq, blocks_per_split) > sv::kMaxSplits)
+        return fail(SV_ERR_SHAPE, "blocks_per_split %d gives more than %d splits", blocks_per_split, sv::kMaxSplits);
+    if (ceil_div(max_blocks_per_seq, sv::kMaxBps) > sv::kMaxSplits)
+        return fail(SV_ERR_UNSUPPORTED, "max_blocks_per_seq %d exceeds %d pages", max_blocks_per_seq,
+                    sv::kMaxBps * sv::kMaxSplits);
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(SV_ERR_ALIGN, "q and out must be 16-byte aligned");
+    if (!aligned(k_cache, fp8 ? 8 : 16) || !aligned(v_cache, fp8 ? 8 : 16))
+        return fail(SV_ERR_ALIGN, "k_cache and v_cache must be %d-byte aligned", fp8 ? 8 : 16);
+    if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+        return fail(SV_ERR_ALIGN, "block_table and context_lens must be 4-byte aligned");
+
+    const sv::AttnPlan pl = sv::plan_attention(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split);
+    if (!workspace)
+        return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.total);
+    if (!aligned(workspace, 256))
+        return fail(SV_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pl.total)
+        return fail(SV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.total);
+
+    sv::AttnParams p{};
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.part_o = reinterpret_cast<float *>(ws + pl.off_part_o);
+    p.part_ml = reinterpret_cast<float *>(ws + pl.off_part_ml);
+    p.B = B;
+    p.T = T;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.TG = T * p.G;
+    p.d = d;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.bps = pl.bps;
+    p.max_splits = pl.max_splits;
+    const long long wgs = (long long)B * Hkv * pl.max_splits;
+    if (wgs > 0x7FFFFFF0LL)
+        return fail(SV_ERR_SHAPE, "too many workgroups");
+    p.grid = (int)(((wgs + 7) / 8) * 8);
+    p.qscale = (float)((double)sm_scale * 1.4426950408889634);
+
+    const bool use_mfma = (algo == SV_ATTN_MFMA) || (algo == SV_ATTN_AUTO && kv_dtype != SV_KV_F32);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = use_mfma ? sv::launch_attn_mfma(p, kv_dtype, s) : sv::launch_attn_valu(p, kv_dtype, s);
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                     const float *v_scale, const int32_t *block_table, const int32_t *context_lens, float *out,
+                     int B, int T, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq, int num_blocks,
+                     int kv_dtype, float sm_scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return spec_verify_attn_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, B, T, Hq,
+                               Hkv, d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace,
+                               workspace_bytes, stream, SV_ATTN_AUTO, 0);
+}
+
+size_t spec_verify_sample_workspace_size(int B, int K, int V)
+{
+    if (B < 1 || K < 1 || K > 15 || V < 1 || V > sv::kMaxSampleChunks * sv::kSampleChunk)
+        return 0;
+    return sv::plan_sample(B, K, V).total;
+}
+
+int spec_verify_sample(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                       const float *uniforms, int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B,
+                       int K, int V, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
+        return fail(SV_ERR_NULL, "target_logits, draft_probs, draft_tokens, uniforms, num_accepted and "
+                                 "out_tokens must be non-NULL");
+    if (B < 1 || K < 1 || V < 1)
+        return fail(SV_ERR_SHAPE, "B, K and V must be >= 1 (got %d, %d, %d)", B, K, V);
+    if (K > 15)
+        return fail(SV_ERR_SHAPE, "K must be <= 15 (got %d)", K);
+    if (V > sv::kMaxSampleChunks * sv::kSampleChunk)
+        return fail(SV_ERR_UNSUPPORTED, "V must be <= %d (got %d)", sv::kMaxSampleChunks * sv::kSampleChunk, V);
+    if ((long long)B * (K + 1) * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "B*(K+1)*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk);
+    if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
+        (accept_prob && !aligned(accept_prob, 4)))
+        return fail(SV_ERR_ALIGN, "sampler arrays must be 4-byte aligned");
+    const sv::SamplePlan pl = sv::plan_sample(B, K, V);
+    if (!workspace)
+        return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.total);
+    if (!aligned(workspace, 256))
+        return fail(SV_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pl.total)
+        return fail(SV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.total);
+    sv::SampleParams p{};
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    p.logits = target_logits;
+    p.probs = draft_probs;
+    p.tokens = draft_tokens;
+    p.uniforms = uniforms;
+    p.num_accepted = num_accepted;
+    p.out_tokens = out_tokens;
+    p.accept_prob = accept_prob;
+    p.seq_state = ws + pl.off_state;
+    p.row_stats = ws + pl.off_stats;
+    p.chunk_mass = reinterpret_cast<double *>(ws + pl.off_mass);
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.nchunk = pl.nchunk;
+    p.vec4 = (V % 4 == 0) && aligned(target_logits, 16) && aligned(draft_probs, 16);
+    const hipError_t e = sv::launch_sample(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "sampler launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,442 @@
+// sample.hip -- the rejection sampler of the verify step, for gfx950.
+//
+// What is computed ("50 | Speculative Decoding" 3.1; "KV Cache + Speculative
+// Decoding" 7.1-7.3 and 7.6): p_i = softmax(target row i); draft x_i is kept
+// iff u_i * q_i(x_i) < p_i(x_i) (acceptance with probability
+// min(1, p/q)); at the first rejection n the replacement is drawn from
+// max(0, p_n - q_n) normalised, and with no rejection the bonus token is
+// drawn from p_K.  Draws use the caller's uniform u_K and the inverse CDF in
+// ascending token order.
+//
+// Three launches on the caller's stream (kernel boundaries order them, so no
+// fences or counters are needed):
+//   rowstats  grid (vocab chunk x row): one streaming pass over every target
+//             row; per chunk the maximum and sum_j exp(l_j - max) (fp32 exp,
+//             fp64 accumulation), reduced across the wave with DPP;
+//   decide    grid (vocab chunk x sequence): every workgroup merges the row
+//             statistics of its sequence, runs the (at most 15) acceptance
+//             tests in fp64, and sums the weights of the chosen row over its
+//             chunk in fp64;
+//   pick      grid (sequence): scans the chunk masses, locates the chunk
+//             holding u_K * S, rescans that chunk with a wave prefix scan
+//             and writes the outputs.
+// The decision arithmetic (p(x), weights, cumulative sums) runs in fp64 so
+// that it agrees with an exact evaluation except within ~1e-7 of a
+// threshold.
+#include "sv_device.hpp"
+#include "sv_internal.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kPer = kSampleChunk / kSampleThreads;  // 32 entries per thread
+constexpr int kNWs = kSampleThreads / kWave;
+
+struct RowStat {
+    float m;
+    float pad;
+    double z;
+};
+
+// What the draw of one sequence needs from the decide pass.
+struct SeqState {
+    int n;       // accepted drafts
+    float m;     // max logit of row n
+    double inv_z;  // 1 / sum_j exp(l_j - m) of row n
+};
+
+// Loads this thread's 32 entries of a chunk: entries tid*4 + k*1024 .. +3
+// (float4 path) or tid + k*256 (scalar path); missing entries read `fill`.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float *row, int n, float fill, float (&v)[kPer])
+{
+    const int tid = threadIdx.x;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int k = 0; k < kPer / 4; ++k) {
+            const int e = (k * kSampleThreads + tid) * 4;
+            float4 x = make_float4(fill, fill, fill, fill);
+            if (e < n)  // n is a multiple of 4 on this path
+                x = *reinterpret_cast<const float4 *>(row + e);
+            v[4 * k + 0] = x.x; v[4 * k + 1] = x.y; v[4 * k + 2] = x.z; v[4 * k + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int e = k * kSampleThreads + tid;
+            v[k] = e < n ? row[e] : fill;
+        }
+    }
+}
+
+__device__ __forceinline__ float block_max(float v, float *s_red)
+{
+    v = wave_max_f32(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        s_red[wave] = v;
+    __syncthreads();
+    float r = s_red[0];
+#pragma unroll
+    for (int i = 1; i < kNWs; ++i)
+        r = fmaxf(r, s_red[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, double *s_red)
+{
+    v = wave_sum_f64(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        s_red[wave] = v;
+    __syncthreads();
+    double r = s_red[0];
+#pragma unroll
+    for (int i = 1; i < kNWs; ++i)
+        r += s_red[i];
+    __syncthreads();
+    return r;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(SampleParams p)
+{
+    __shared__ float s_f[kNWs];
+    __shared__ double s_d[kNWs];
+    const int row = blockIdx.x / p.nchunk;
+    const int chunk = blockIdx.x - row * p.nchunk;
+    const int base = chunk * kSampleChunk;
+    const int n = min(kSampleChunk, p.V - base);
+    float v[kPer];
+    load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
+    float mx = v[0];
+#pragma unroll
+    for (int k = 1; k < kPer; ++k)
+        mx = fmaxf(mx, v[k]);
+    const float M = block_max(mx, s_f);
+    double z = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        z += (double)expf(v[k] - M);
+    z = block_sum(z, s_d);
+    if (threadIdx.x == 0) {
+        RowStat st;
+        st.m = M;
+        st.pad = 0.0f;
+        st.z = z;
+        static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
+    }
+}
+
+// Weight of entry j of the chosen row: the residual max(0, p - q) after a
+// rejection, p itself for the bonus row or the zero-mass fallback.
+__device__ __forceinline__ double target_prob(float l, float M, double invZ)
+{
+    return exp((double)l - (double)M) * invZ;
+}
+
+__device__ __forceinline__ double weight(float l, float q, float M, double invZ, bool residual)
+{
+    const double pj = target_prob(l, M, invZ);
+    if (!residual)
+        return pj;
+    const double r = pj - (double)q;
+    return r > 0.0 ? r : 0.0;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
+{
+    __shared__ float s_M[16];
+    __shared__ double s_Z[16];
+    __shared__ double s_ratio[16];
+    __shared__ int s_acc[16];
+    __shared__ int s_n;
+    __shared__ double s_d[kNWs];
+
+    const int b = blockIdx.x / p.nchunk;
+    const int chunk = blockIdx.x - b * p.nchunk;
+    const int tid = threadIdx.x;
+    const int K = p.K, K1 = K + 1, V = p.V;
+
+    // 1. Row statistics of the K+1 rows of this sequence: one wave per row,
+    //    lanes over vocabulary chunks (all loads in flight together).
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int i = wave; i < K1; i += kNWs) {
+            const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
+            float mloc = -__builtin_inff();
+            for (int c = lane; c < p.nchunk; c += kWave)
+                mloc = fmaxf(mloc, st[c].m);
+            const float M = wave_max_f32(mloc);
+            double zloc = 0.0;
+            for (int c = lane; c < p.nchunk; c += kWave) {
+                const RowStat r = st[c];
+                zloc += r.z * exp((double)r.m - (double)M);
+            }
+            const double Z = wave_sum_f64(zloc);
+            if (lane == 0) {
+                s_M[i] = M;
+                s_Z[i] = Z;
+            }
+        }
+    }
+    __syncthreads();
+    // 2. Acceptance tests u_i * q_i(x_i) < p_i(x_i).
+    if (tid < K) {
+        int x = p.tokens[(size_t)b * K + tid];
+        x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+        const float lx = p.logits[((size_t)b * K1 + tid) * V + x];
+        const double a = target_prob(lx, s_M[tid], 1.0 / s_Z[tid]);
+        const double c = (double)p.probs[((size_t)b * K + tid) * V + x];
+        const double u = (double)p.uniforms[(size_t)b * K1 + tid];
+        s_acc[tid] = (u * c < a) ? 1 : 0;
+        s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int n = K;
+        for (int i = 0; i < K; ++i)
+            if (!s_acc[i]) {
+                n = i;
+                break;
+            }
+        s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n;
+    const bool residual = n < K;
+    const float M = s_M[n];
+    const double invZ = 1.0 / s_Z[n];
+    const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
+    const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
+
+    // 3. Mass of this chunk: residual (or bonus) weights and plain target mass.
+    {
+        const int base = chunk * kSampleChunk;
+        const int cnt = min(kSampleChunk, V - base);
+        float lv[kPer], qv[kPer];
+        load_chunk<VEC>(lrow + base, cnt, -__builtin_inff(), lv);
+        if (residual)
+            load_chunk<VEC>(qrow + base, cnt, 0.0f, qv);
+        else
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                qv[k] = 0.0f;
+        double sw = 0.0, sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const double pj = target_prob(lv[k], M, invZ);
+            sp += pj;
+            if (residual) {
+                const double r = pj - (double)qv[k];
+                sw += r > 0.0 ? r : 0.0;
+            } else {
+                sw += pj;
+            }
+        }
+        sw = block_sum(sw, s_d);
+        sp = block_sum(sp, s_d);
+        if (tid == 0) {
+            p.chunk_mass[((size_t)b * p.nchunk + chunk) * 2 + 0] = sw;
+            p.chunk_mass[((size_t)b * p.nchunk + chunk) * 2 + 1] = sp;
+        }
+    }
+
+    // The first workgroup of the sequence records what the draw needs.
+    if (chunk == 0 && tid == 0) {
+        SeqState ss;
+        ss.n = n;
+        ss.m = M;
+        ss.inv_z = invZ;
+        static_cast<SeqState *>(p.seq_state)[b] = ss;
+    }
+    if (chunk == 0 && p.accept_prob && tid < K)
+        p.accept_prob[(size_t)b * K + tid] = (float)s_ratio[tid];
+}
+
+// The draw: one workgroup per sequence.  Locates the vocabulary chunk that
+// holds u_K * S from the chunk masses (scanned in order), then rescans that
+// chunk: each thread owns a contiguous run of entries, the run sums are
+// prefix-scanned across the workgroup (DPP wave scan + LDS), and the first
+// entry whose cumulative weight exceeds u_K * S is the token.
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SampleParams p)
+{
+    __shared__ double s_massbuf[2 * kMaxSampleChunks];
+    __shared__ double s_d[kNWs];
+    __shared__ int s_i[kNWs];
+    __shared__ int s_cstar, s_mode;
+    __shared__ double s_cum, s_target;
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int K = p.K, K1 = K + 1, V = p.V;
+    const SeqState ss = static_cast<const SeqState *>(p.seq_state)[b];
+    const int n = ss.n;
+    const bool residual = n < K;
+    const float M = ss.m;
+    const double invZ = ss.inv_z;
+    const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
+    const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
+
+    // Chunk masses of this sequence into LDS (parallel loads), then one
+    // thread scans them in order.
+    double *s_mass = s_massbuf;
+    const double *gmass = p.chunk_mass + (size_t)b * p.nchunk * 2;
+    for (int i = tid; i < 2 * p.nchunk; i += kSampleThreads)
+        s_mass[i] = gmass[i];
+    __syncthreads();
+    if (tid == 0) {
+        double S = 0.0;
+        for (int c = 0; c < p.nchunk; ++c)
+            S += s_mass[2 * c];
+        int mode = 0;  // 0: residual/bonus weights, 1: fallback to p_n
+        if (!(S > 0.0)) {
+            mode = 1;
+            S = 0.0;
+            for (int c = 0; c < p.nchunk; ++c)
+                S += s_mass[2 * c + 1];
+        }
+        const double tgt = (double)p.uniforms[(size_t)b * K1 + K] * S;
+        double cum = 0.0;
+        int cstar = -1;
+        for (int c = 0; c < p.nchunk; ++c) {
+            const double mc = s_mass[2 * c + mode];
+            if (cum + mc > tgt) {
+                cstar = c;
+                break;
+            }
+            cum += mc;
+        }
+        int take_last = 0;
+        if (cstar < 0) {  // rounding left u*S at or past the total: last positive weight
+            take_last = 1;
+            cum = 0.0;
+            for (int c = 0; c < p.nchunk; ++c)
+                if (s_mass[2 * c + mode] > 0.0)
+                    cstar = c;
+            for (int c = 0; c < cstar; ++c)
+                cum += s_mass[2 * c + mode];
+        }
+        s_cstar = cstar < 0 ? 0 : cstar;
+        s_cum = cum;
+        s_target = tgt;
+        s_mode = mode | (take_last << 1);
+    }
+    __syncthreads();
+    const bool use_resid = residual && !(s_mode & 1);
+    const bool take_last = (s_mode & 2) != 0;
+    const int base = s_cstar * kSampleChunk;
+    const int cnt = min(kSampleChunk, V - base);
+    // This thread's contiguous run of kPer entries of the chosen chunk.
+    const int e0 = tid * kPer;
+    double wv[kPer];
+    double seg = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = e0 + k;
+        double wk = 0.0;
+        if (e < cnt)
+            wk = weight(lrow[base + e], use_resid ? qrow[base + e] : 0.0f, M, invZ, use_resid);
+        wv[k] = wk;
+        seg += wk;
+    }
+    // Exclusive prefix of the run sums across the workgroup.
+    const double incl = wave_inclusive_scan_f64(seg);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane == 63)
+        s_d[wave] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int i = 0; i < wave; ++i)
+        before += s_d[i];
+    double run = s_cum + before + (incl - seg);
+    int cand = 0x7FFFFFFF, lastpos = -1;
+    const double tgt = s_target;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        if (wv[k] > 0.0)
+            lastpos = base + e0 + k;
+        run += wv[k];
+        if (cand == 0x7FFFFFFF && run > tgt && wv[k] > 0.0)
+            cand = base + e0 + k;
+    }
+    const int wmin = wave_min_i32(cand), wmax = wave_max_i32(lastpos);
+    if (lane == 0)
+        s_i[wave] = wmin;
+    __syncthreads();
+    int best = s_i[0];
+    for (int i = 1; i < kNWs; ++i)
+        best = min(best, s_i[i]);
+    __syncthreads();
+    if (lane == 0)
+        s_i[wave] = wmax;
+    __syncthreads();
+    int last = s_i[0];
+    for (int i = 1; i < kNWs; ++i)
+        last = max(last, s_i[i]);
+    const int token = (!take_last && best != 0x7FFFFFFF) ? best : last;
+
+    if (tid < K1) {
+        int32_t v;
+        if (tid < n) {
+            const int x = p.tokens[(size_t)b * K + tid];
+            v = x < 0 ? 0 : (x >= V ? V - 1 : x);
+        } else {
+            v = (tid == n) ? token : -1;
+        }
+        p.out_tokens[(size_t)b * K1 + tid] = v;
+    }
+    if (tid == 0)
+        p.num_accepted[b] = n;
+}
+
+__global__ void sv_fill_zero_kernel(uint4 *p, size_t n16, unsigned char *tail, size_t ntail)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (blockIdx.x == 0)
+        for (size_t i = threadIdx.x; i < ntail; i += blockDim.x)
+            tail[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
+{
+    const dim3 block(kSampleThreads);
+    const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
+    const dim3 g2((unsigned)(p.nchunk * p.B));
+    const dim3 g3((unsigned)p.B);
+    if (p.vec4) {
+        hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_decide_kernel<true>, g2, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_decide_kernel<false>, g2, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_clear(void *ptr, size_t bytes, hipStream_t stream)
+{
+    if (bytes == 0)
+        return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const size_t ntail = bytes - n16 * 16;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks < 1)
+        blocks = 1;
+    if (blocks > 4096)
+        blocks = 4096;
+    hipLaunchKernelGGL(sv_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<uint4 *>(ptr), n16, static_cast<unsigned char *>(ptr) + n16 * 16, ntail);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,76 @@
+// sv_internal.hpp -- host-side argument blocks shared by the C ABI layer and
+// the kernel launchers.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 16;          // tokens per KV page
+constexpr int kMaxRows = 64;        // T * (Hq/Hkv) per (sequence, kv head) unit
+constexpr int kMaxSplits = 128;     // context splits per unit
+constexpr int kMaxBps = 512;        // context pages per split
+constexpr int kAttnThreads = 256;   // 4 waves per workgroup
+
+// Everything one attention launch needs.  Sizes are validated by the caller.
+struct AttnParams {
+    const float *q;
+    const void *k_cache;
+    const void *v_cache;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *block_table;
+    const int32_t *context_lens;
+    float *out;
+    float *part_o;         // [B*Hkv][max_splits][TG][d]  unnormalised partial outputs
+    float *part_ml;        // [B*Hkv][max_splits][TG][2]  (running max in log2 units, sum)
+    int B, T, Hq, Hkv, G, TG, d;
+    int max_blocks, num_blocks;
+    int bps;               // context blocks per split (multiple of 8)
+    int max_splits;        // ceil(max_blocks / bps)
+    int grid;              // workgroups launched (multiple of 8)
+    float qscale;          // sm_scale * log2(e): scores are kept in base-2 units
+};
+
+struct AttnPlan {
+    int bps;
+    int max_splits;
+    size_t off_part_o, off_part_ml, total;
+};
+
+AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, int bps_request);
+
+hipError_t launch_attn_mfma(const AttnParams &p, int kv_dtype, hipStream_t stream);
+hipError_t launch_attn_valu(const AttnParams &p, int kv_dtype, hipStream_t stream);
+
+constexpr int kSampleChunk = 8192;  // vocabulary entries per sampler workgroup
+constexpr int kSampleThreads = 256;
+constexpr int kMaxSampleChunks = 2048;  // V <= 2048 * 8192
+
+struct SampleParams {
+    const float *logits;     // [B][K+1][V]
+    const float *probs;      // [B][K][V]
+    const int32_t *tokens;   // [B][K]
+    const float *uniforms;   // [B][K+1]
+    int32_t *num_accepted;   // [B]
+    int32_t *out_tokens;     // [B][K+1]
+    float *accept_prob;      // [B][K] or null
+    void *seq_state;         // [B] {accepted count, row max, 1/row sum} for the draw
+    void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
+    double *chunk_mass;      // [B][nchunk][2] {residual weight, target mass}
+    int B, K, V, nchunk;
+    int vec4;                // rows start 16-byte aligned and V % 4 == 0
+};
+
+struct SamplePlan {
+    int nchunk;
+    size_t off_state, off_stats, off_mass, total;
+};
+
+SamplePlan plan_sample(int B, int K, int V);
+hipError_t launch_sample(const SampleParams &p, hipStream_t stream);
+hipError_t launch_clear(void *ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/spec_verify.h declares, and rejects bad arguments
+with the documented status before enqueueing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decoding_verify_attn_amd as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_lists_the_calls():
+    names = declared_functions()
+    for must in ("spec_verify_attn", "spec_verify_sample", "spec_verify_attn_workspace_size",
+                 "spec_verify_sample_workspace_size", "sv_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = sv.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_abi_version_and_status_strings():
+    L = sv.lib()
+    assert L.sv_abi_version() == 1
+    assert L.sv_status_string(0) == b"ok"
+    assert L.sv_status_string(6) == b"HIP error"
+
+
+def _attn(**kw):
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    a = dict(q=base, k=base, v=base, ks=None, vs=None, table=base, lens=base, out=base,
+             B=2, T=5, Hq=32, Hkv=8, d=128, bs=16, maxb=8, nb=16, kv=1, scale=0.088,
+             ws=base, wsb=1 << 14, stream=None, algo=0, bps=0)
+    a.update(kw)
+    return L.spec_verify_attn_ex(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["table"], a["lens"], a["out"],
+                                 a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["maxb"], a["nb"],
+                                 a["kv"], a["scale"], a["ws"], a["wsb"], a["stream"], a["algo"], a["bps"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(B=0), 2),
+    (dict(T=17), 2),
+    (dict(Hq=30), 2),
+    (dict(Hq=128, Hkv=8), 3),     # T*G = 80 > 64
+    (dict(d=96), 3),
+    (dict(bs=32), 3),
+    (dict(kv=7), 3),
+    (dict(kv=2), 1),              # E4M3 without scales
+    (dict(ks=1 << 20), 2),        # scales given for bf16
+    (dict(scale=0.0), 2),
+    (dict(algo=2, kv=0), 3),      # matrix cores need bf16/E4M3
+    (dict(bps=10), 2),
+    (dict(bps=516), 2),
+    (dict(ws=None), 4),
+    (dict(wsb=16), 4),
+    (dict(q=1 << 20 | 4), 5),     # misaligned
+])
+def test_attention_argument_checks(kw, status):
+    assert _attn(**kw) == status
+    assert len(sv.lib().sv_last_error()) > 0
+
+
+def test_sample_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = (ctypes.addressof(buf) + 255) & ~255
+    assert L.spec_verify_sample(None, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 1
+    assert L.spec_verify_sample(p, p, p, p, p, p, None, 2, 16, 100, p, 1 << 14, None) == 2
+    assert L.spec_verify_sample(p, p, p, p, p, p, None, 0, 3, 100, p, 1 << 14, None) == 2
+    assert L.spec_verify_sample(p, p, p, p, p, p, None, 2, 3, 100, p, 8, None) == 4
+    assert L.spec_verify_sample(p, p, p, p, p, p, None, 2, 3, 100, None, 1 << 14, None) == 4
+    assert L.spec_verify_sample(p + 2, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
+
+
+def test_workspace_queries():
+    assert sv.attn_workspace_size(8, 6, 32, 8, 128, 256) > 0
+    assert sv.lib().spec_verify_attn_workspace_size(8, 6, 30, 8, 128, 256) == 0
+    assert sv.sample_workspace_size(8, 5, 128256) >= 8 * 6 * 16 * 16
+    assert sv.lib().spec_verify_sample_workspace_size(8, 0, 10) == 0

@@ -1,0 +1,117 @@
+"""GPU parity of spec_verify_attn against the CPU oracle (fp64).
+
+Gate (per output row r = (b,t,h)): max_c |o - o_ref| / max_c |o_ref|
+  <= 1e-3 for fp32 KV, <= 2e-2 for bf16 and E4M3 KV (E4M3 against the
+  dequantised oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verify_attn_amd as sv
+import workloads as W
+from .gpu_helpers import TOL, oracle_attn, row_rel_err, run_attn, sample_rows, upload_attn
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (seed, B, T, Hq, Hkv, d, lens, kv)
+    (1, 1, 5, 4, 1, 64, [256], "f32"),
+    (2, 3, 6, 32, 8, 128, [37, 400, 16], "bf16"),
+    (3, 2, 5, 64, 8, 128, [1000, 77], "bf16"),          # T*G = 40 (three row tiles)
+    (4, 2, 7, 64, 8, 128, [517, 7], "bf16"),            # T*G = 56, L_b = T
+    (5, 2, 8, 32, 8, 128, [300, 129], "bf16"),          # T*G = 32
+    (6, 3, 2, 8, 8, 64, [33, 64, 190], "bf16"),         # MHA (G=1), d=64
+    (7, 2, 4, 64, 4, 64, [250, 31], "bf16"),            # T*G = 64 (maximum)
+    (8, 2, 7, 64, 8, 128, [700, 45], "fp8"),
+    (9, 2, 3, 16, 2, 64, [129, 100], "fp8"),
+    (10, 2, 5, 8, 2, 64, [90, 300], "f32"),
+    (11, 1, 1, 4, 4, 128, [1], "bf16"),                 # single query row, single key
+]
+
+
+def _check(a, out, rows=None):
+    ref = oracle_attn(a, rows=rows)
+    got = out.cpu().numpy().reshape(-1, a.d)
+    if rows is not None:
+        got = got[rows]
+    err = row_rel_err(got, ref)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(err.max())
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c[0]) for c in SMALL])
+def test_small_shapes_auto(case):
+    seed, B, T, Hq, Hkv, d, lens, kv = case
+    a = W.make_attn_from_lens(seed, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=3)
+    out = run_attn(a)
+    err = _check(a, out)
+    print("case %d max row rel err %.3e" % (seed, err))
+    assert err <= TOL[a.kv_dtype]
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[7] != "f32"], ids=lambda c: str(c[0]))
+def test_small_shapes_valu(case):
+    seed, B, T, Hq, Hkv, d, lens, kv = case
+    a = W.make_attn_from_lens(seed, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=1)
+    out = run_attn(a, algo=sv.SV_ATTN_VALU)
+    err = _check(a, out)
+    assert err <= TOL[a.kv_dtype]
+
+
+@pytest.mark.parametrize("bps", [8, 16, 24, 64])
+def test_forced_splits_merge(bps):
+    a = W.make_attn_from_lens(21, 3, 6, 32, 8, 128, [1500, 80, 999], kv="bf16")
+    out = run_attn(a, blocks_per_split=bps)
+    assert _check(a, out) <= TOL[a.kv_dtype]
+    out_v = run_attn(a, algo=sv.SV_ATTN_VALU, blocks_per_split=bps)
+    assert _check(a, out_v) <= TOL[a.kv_dtype]
+
+
+def test_deterministic_and_workspace_reusable():
+    # a workspace full of garbage must not matter: nothing in it is read before written
+    a = W.make_attn_from_lens(22, 4, 5, 64, 8, 128, [2000, 33, 700, 1024], kv="bf16")
+    t = upload_attn(a)
+    ws = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, 16), t["q"].device)
+    ws.fill_(0xAB)
+    o1 = run_attn(a, t, blocks_per_split=16, ws=ws).clone()
+    for _ in range(5):
+        o2 = run_attn(a, t, blocks_per_split=16, ws=ws)
+        assert torch.equal(o1, o2)
+
+
+def test_physical_placement_is_invisible():
+    a1 = W.make_attn_from_lens(23, 2, 5, 32, 8, 128, [300, 517], kv="bf16", identity_table=True)
+    o1 = run_attn(a1).cpu()
+    a2 = W.make_attn_from_lens(23, 2, 5, 32, 8, 128, [300, 517], kv="bf16", identity_table=True)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(a2.num_blocks)
+    k2 = np.empty_like(a2.k_cache)
+    v2 = np.empty_like(a2.v_cache)
+    k2[perm] = a2.k_cache
+    v2[perm] = a2.v_cache
+    a2.k_cache, a2.v_cache = k2, v2
+    a2.block_table = perm[a2.block_table].astype(np.int32)
+    o2 = run_attn(a2).cpu()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5a", "c5b"])
+def test_config_full_size(name):
+    a = W.make_attn(name, seed=0)
+    out = run_attn(a)
+    rows = None if name == "c1" else sample_rows(a, 384, seed=1)
+    err = _check(a, out, rows)
+    print("%s max row rel err %.3e over %s rows" % (name, err, "all" if rows is None else len(rows)))
+    assert err <= TOL[a.kv_dtype]
+    assert torch.isfinite(out).all()
+
+
+def test_config_ragged_full_size():
+    a = W.make_attn("c4", seed=0)
+    out = run_attn(a)
+    rows = sample_rows(a, 384, seed=2)
+    err = _check(a, out, rows)
+    print("c4 max row rel err %.3e" % err)
+    assert err <= TOL[a.kv_dtype]
+    assert torch.isfinite(out).all()

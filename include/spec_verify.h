@@ -119,7 +119,10 @@ int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache,
  * by the caller (for measurement).  blocks_per_split = 0 lets the planner
  * choose; otherwise it must be a positive multiple of 4, at most 512, with
  * ceil(max_blocks_per_seq / blocks_per_split) <= 128.  The workspace must
- * then hold spec_verify_attn_workspace_size_ex(..., blocks_per_split) bytes. */
+ * then hold spec_verify_attn_workspace_size_ex(..., blocks_per_split) bytes.
+ * main_done_event: optional hipEvent_t (NULL to skip), recorded on `stream`
+ * after the main attention kernel and before the split merge, so a caller
+ * can time the main kernel on its own. */
 size_t spec_verify_attn_workspace_size_ex(int B, int T, int Hq, int Hkv, int d,
                                           int max_blocks_per_seq, int blocks_per_split);
 
@@ -130,7 +133,8 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
                         int B, int T, int Hq, int Hkv, int d, int block_size,
                         int max_blocks_per_seq, int num_blocks, int kv_dtype,
                         float sm_scale, void *workspace, size_t workspace_bytes,
-                        void *stream, int algo, int blocks_per_split);
+                        void *stream, int algo, int blocks_per_split,
+                        void *main_done_event);
 
 /* ------------------------------------------------------------------------
  * spec_verify_sample: the rejection sampler of the verify step.

@@ -57,7 +57,7 @@ def lib():
         L.spec_verify_attn.restype = I
         L.spec_verify_attn.argtypes = attn_args
         L.spec_verify_attn_ex.restype = I
-        L.spec_verify_attn_ex.argtypes = attn_args + [I, I]
+        L.spec_verify_attn_ex.argtypes = attn_args + [I, I, P]
         L.spec_verify_sample_workspace_size.restype = S
         L.spec_verify_sample_workspace_size.argtypes = [I] * 3
         L.spec_verify_sample.restype = I
@@ -122,13 +122,14 @@ def workspace_clear(ws: torch.Tensor, stream=None):
 
 def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, workspace, *,
                      k_scale=None, v_scale=None, sm_scale=None, kv_dtype=None, stream=None,
-                     algo=SV_ATTN_AUTO, blocks_per_split=0):
+                     algo=SV_ATTN_AUTO, blocks_per_split=0, main_done_event=None):
     """Paged GQA verify attention (see include/spec_verify.h).
 
     q [B,T,Hq,d] f32; k_cache/v_cache [num_blocks,16,Hkv,d] (f32, bf16, or E4M3
     codes as uint8 / float8_e4m3fn); block_table [B,max_blocks] i32;
     context_lens [B] i32; out [B,T,Hq,d] f32; workspace: uint8 device tensor of
-    at least attn_workspace_size(...) bytes, zero-filled before first use.
+    at least attn_workspace_size(...) bytes.  main_done_event: optional raw
+    hipEvent_t handle recorded between the main kernel and the split merge.
     """
     B, T, Hq, d = q.shape
     num_blocks, bs, Hkv, d2 = k_cache.shape
@@ -140,7 +141,7 @@ def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, worksp
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         _ptr(context_lens), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
         kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream_handle(stream, q.device), int(algo), int(blocks_per_split)))
+        _stream_handle(stream, q.device), int(algo), int(blocks_per_split), main_done_event))
     return out
 
 

@@ -809,7 +809,9 @@ hipError_t launch_valu_d(const AttnParams &p, int kv, hipStream_t s)
     }
 }
 
-hipError_t launch_merge(const AttnParams &p, hipStream_t stream)
+}  // namespace
+
+hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
 {
     if (p.max_splits <= 1)
         return hipSuccess;
@@ -822,23 +824,17 @@ hipError_t launch_merge(const AttnParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-}  // namespace
-
 hipError_t launch_attn_mfma(const AttnParams &p, int kv_dtype, hipStream_t stream)
 {
     const bool fp8 = kv_dtype == 2;
-    hipError_t e;
     if (p.d == 64)
-        e = fp8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
-    else
-        e = fp8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
-    return e != hipSuccess ? e : launch_merge(p, stream);
+        return fp8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
+    return fp8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
 }
 
 hipError_t launch_attn_valu(const AttnParams &p, int kv_dtype, hipStream_t stream)
 {
-    const hipError_t e = p.d == 64 ? launch_valu_d<64>(p, kv_dtype, stream) : launch_valu_d<128>(p, kv_dtype, stream);
-    return e != hipSuccess ? e : launch_merge(p, stream);
+    return p.d == 64 ? launch_valu_d<64>(p, kv_dtype, stream) : launch_valu_d<128>(p, kv_dtype, stream);
 }
 
 }  // namespace sv

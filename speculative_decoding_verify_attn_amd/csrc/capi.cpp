@@ -173,7 +173,8 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
                         const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
                         float *out, int B, int T, int Hq, int Hkv, int d, int block_size,
                         int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale, void *workspace,
-                        size_t workspace_bytes, void *stream, int algo, int blocks_per_split)
+                        size_t workspace_bytes, void *stream, int algo, int blocks_per_split,
+                        void *main_done_event)
 {
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(SV_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and out must be non-NULL");
@@ -252,9 +253,17 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
 
     const bool use_mfma = (algo == SV_ATTN_MFMA) || (algo == SV_ATTN_AUTO && kv_dtype != SV_KV_F32);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = use_mfma ? sv::launch_attn_mfma(p, kv_dtype, s) : sv::launch_attn_valu(p, kv_dtype, s);
+    hipError_t e = use_mfma ? sv::launch_attn_mfma(p, kv_dtype, s) : sv::launch_attn_valu(p, kv_dtype, s);
     if (e != hipSuccess)
         return fail(SV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    if (main_done_event) {
+        e = hipEventRecord(static_cast<hipEvent_t>(main_done_event), s);
+        if (e != hipSuccess)
+            return fail(SV_ERR_HIP, "recording main_done_event: %s", hipGetErrorString(e));
+    }
+    e = sv::launch_attn_merge(p, s);
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "split-merge launch: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -265,7 +274,7 @@ int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache, c
 {
     return spec_verify_attn_ex(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, B, T, Hq,
                                Hkv, d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace,
-                               workspace_bytes, stream, SV_ATTN_AUTO, 0);
+                               workspace_bytes, stream, SV_ATTN_AUTO, 0, nullptr);
 }
 
 size_t spec_verify_sample_workspace_size(int B, int K, int V)

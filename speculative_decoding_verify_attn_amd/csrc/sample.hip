@@ -11,17 +11,18 @@
 // Three launches on the caller's stream (kernel boundaries order them, so no
 // fences or counters are needed):
 //   rowstats  grid (vocab chunk x row): one streaming pass over every target
-//             row; per chunk the maximum and sum_j exp(l_j - max) (fp32 exp,
-//             fp64 accumulation), reduced across the wave with DPP;
+//             row; per chunk the maximum and sum_j exp(l_j - max) (hardware
+//             exp2, fp64 accumulation), reduced across the wave with DPP;
 //   decide    grid (vocab chunk x sequence): every workgroup merges the row
 //             statistics of its sequence, runs the (at most 15) acceptance
 //             tests in fp64, and sums the weights of the chosen row over its
 //             chunk in fp64;
-//   pick      grid (sequence): scans the chunk masses, locates the chunk
-//             holding u_K * S, rescans that chunk with a wave prefix scan
-//             and writes the outputs.
-// The decision arithmetic (p(x), weights, cumulative sums) runs in fp64 so
-// that it agrees with an exact evaluation except within ~1e-7 of a
+//   pick      grid (sequence): one wave prefix-scans the chunk masses and
+//             locates the chunk holding u_K * S; the workgroup rescans that
+//             chunk with a prefix scan and writes the outputs.
+// The acceptance tests run in fp64; the weights take fp32 exp of an exactly
+// split argument (about 1e-7 relative) and every sum runs in fp64, so the
+// decisions agree with an exact evaluation except within ~1e-7 of a
 // threshold.
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
@@ -115,10 +116,13 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     for (int k = 1; k < kPer; ++k)
         mx = fmaxf(mx, v[k]);
     const float M = block_max(mx, s_f);
+    // exp(v - M) = 2^((v - M) log2 e) with the hardware exp2; terms summed in
+    // fp64 (the rounding of the scaled argument, |v - M| * 2^-24 relative,
+    // is largest for the terms that matter least).
     double z = 0.0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-        z += (double)expf(v[k] - M);
+        z += (double)__builtin_amdgcn_exp2f((v[k] - M) * kLog2e);
     z = block_sum(z, s_d);
     if (threadIdx.x == 0) {
         RowStat st;
@@ -129,16 +133,31 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     }
 }
 
-// Weight of entry j of the chosen row: the residual max(0, p - q) after a
-// rejection, p itself for the bonus row or the zero-mass fallback.
+// Target probability of entry j from its logit, the row maximum M and 1/Z,
+// to about one fp32 ulp: the difference l - M is split exactly into hi + lo
+// (TwoSum), exp(hi) comes from the accurate fp32 exp, exp(lo) = 1 + lo to
+// second order (|lo| <= ulp(hi)/2), and the products are taken in fp64.
+__device__ __forceinline__ double target_prob_fast(float l, float M, double invZ)
+{
+    const float hi = l - M;
+    if (!(hi > -104.0f))
+        return 0.0;  // underflows in fp32 (and catches l = -inf)
+    const float bb = hi - l;
+    const float lo = (l - (hi - bb)) + (-M - bb);
+    return (double)expf(hi) * (1.0 + (double)lo) * invZ;
+}
+
+// Same quantity in fp64 throughout (used for the K acceptance tests).
 __device__ __forceinline__ double target_prob(float l, float M, double invZ)
 {
     return exp((double)l - (double)M) * invZ;
 }
 
+// Weight of entry j of the chosen row: the residual max(0, p - q) after a
+// rejection, p itself for the bonus row or the zero-mass fallback.
 __device__ __forceinline__ double weight(float l, float q, float M, double invZ, bool residual)
 {
-    const double pj = target_prob(l, M, invZ);
+    const double pj = target_prob_fast(l, M, invZ);
     if (!residual)
         return pj;
     const double r = pj - (double)q;
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         double sw = 0.0, sp = 0.0;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
-            const double pj = target_prob(lv[k], M, invZ);
+            const double pj = target_prob_fast(lv[k], M, invZ);
             sp += pj;
             if (residual) {
                 const double r = pj - (double)qv[k];
@@ -264,7 +283,6 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SampleParams p)
 {
-    __shared__ double s_massbuf[2 * kMaxSampleChunks];
     __shared__ double s_d[kNWs];
     __shared__ int s_i[kNWs];
     __shared__ int s_cstar, s_mode;
@@ -281,49 +299,57 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
     const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
 
-    // Chunk masses of this sequence into LDS (parallel loads), then one
-    // thread scans them in order.
-    double *s_mass = s_massbuf;
-    const double *gmass = p.chunk_mass + (size_t)b * p.nchunk * 2;
-    for (int i = tid; i < 2 * p.nchunk; i += kSampleThreads)
-        s_mass[i] = gmass[i];
-    __syncthreads();
-    if (tid == 0) {
-        double S = 0.0;
-        for (int c = 0; c < p.nchunk; ++c)
-            S += s_mass[2 * c];
+    // Wave 0 locates the chunk: totals by DPP sums, then an in-order DPP
+    // prefix scan over the chunk masses, 64 chunks at a time.
+    if (tid < kWave) {
+        const int lane = tid;
+        const double *gmass = p.chunk_mass + (size_t)b * p.nchunk * 2;
+        double sw = 0.0, sp = 0.0;
+        for (int c = lane; c < p.nchunk; c += kWave) {
+            sw += gmass[2 * c];
+            sp += gmass[2 * c + 1];
+        }
+        double S = wave_sum_f64(sw);
         int mode = 0;  // 0: residual/bonus weights, 1: fallback to p_n
         if (!(S > 0.0)) {
             mode = 1;
-            S = 0.0;
-            for (int c = 0; c < p.nchunk; ++c)
-                S += s_mass[2 * c + 1];
+            S = wave_sum_f64(sp);
         }
         const double tgt = (double)p.uniforms[(size_t)b * K1 + K] * S;
-        double cum = 0.0;
-        int cstar = -1;
-        for (int c = 0; c < p.nchunk; ++c) {
-            const double mc = s_mass[2 * c + mode];
-            if (cum + mc > tgt) {
-                cstar = c;
+        double carry = 0.0, cum = 0.0;
+        int cstar = -1, lastpos = -1;
+        double cum_last = 0.0;
+        for (int c0 = 0; c0 < p.nchunk; c0 += kWave) {
+            const int c = c0 + lane;
+            const double mc = c < p.nchunk ? gmass[2 * c + mode] : 0.0;
+            const double incl = wave_inclusive_scan_f64(mc) + carry;
+            const uint64_t hit = __ballot(c < p.nchunk && incl > tgt);
+            const uint64_t pos = __ballot(c < p.nchunk && mc > 0.0);
+            if (pos) {
+                const int ll = 63 - __builtin_clzll(pos);
+                lastpos = c0 + ll;
+                cum_last = readlane_f64(incl - mc, ll);
+            }
+            if (hit) {
+                const int fl = __builtin_ctzll(hit);
+                cstar = c0 + fl;
+                cum = readlane_f64(incl - mc, fl);
                 break;
             }
-            cum += mc;
+            carry = readlane_f64(incl, 63);
         }
         int take_last = 0;
         if (cstar < 0) {  // rounding left u*S at or past the total: last positive weight
             take_last = 1;
-            cum = 0.0;
-            for (int c = 0; c < p.nchunk; ++c)
-                if (s_mass[2 * c + mode] > 0.0)
-                    cstar = c;
-            for (int c = 0; c < cstar; ++c)
-                cum += s_mass[2 * c + mode];
+            cstar = lastpos < 0 ? 0 : lastpos;
+            cum = cum_last;
         }
-        s_cstar = cstar < 0 ? 0 : cstar;
-        s_cum = cum;
-        s_target = tgt;
-        s_mode = mode | (take_last << 1);
+        if (lane == 0) {
+            s_cstar = cstar;
+            s_cum = cum;
+            s_target = tgt;
+            s_mode = mode | (take_last << 1);
+        }
     }
     __syncthreads();
     const bool use_resid = residual && !(s_mode & 1);
@@ -332,16 +358,34 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const int cnt = min(kSampleChunk, V - base);
     // This thread's contiguous run of kPer entries of the chosen chunk.
     const int e0 = tid * kPer;
+    float lv[kPer], qv[kPer];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int k = 0; k < kPer; k += 4) {
+            float4 x = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e0 + k < cnt) {  // cnt is a multiple of 4 on this path
+                x = *reinterpret_cast<const float4 *>(lrow + base + e0 + k);
+                if (use_resid)
+                    y = *reinterpret_cast<const float4 *>(qrow + base + e0 + k);
+            }
+            lv[k] = x.x; lv[k + 1] = x.y; lv[k + 2] = x.z; lv[k + 3] = x.w;
+            qv[k] = y.x; qv[k + 1] = y.y; qv[k + 2] = y.z; qv[k + 3] = y.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const bool ok = e0 + k < cnt;
+            lv[k] = ok ? lrow[base + e0 + k] : -__builtin_inff();
+            qv[k] = (ok && use_resid) ? qrow[base + e0 + k] : 0.0f;
+        }
+    }
     double wv[kPer];
     double seg = 0.0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int e = e0 + k;
-        double wk = 0.0;
-        if (e < cnt)
-            wk = weight(lrow[base + e], use_resid ? qrow[base + e] : 0.0f, M, invZ, use_resid);
-        wv[k] = wk;
-        seg += wk;
+        wv[k] = weight(lv[k], qv[k], M, invZ, use_resid);
+        seg += wv[k];
     }
     // Exclusive prefix of the run sums across the workgroup.
     const double incl = wave_inclusive_scan_f64(seg);

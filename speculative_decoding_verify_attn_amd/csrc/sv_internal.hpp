@@ -42,8 +42,11 @@ struct AttnPlan {
 
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, int bps_request);
 
+// The main attention kernel of each implementation, and the split merge
+// (a no-op launch-wise when max_splits == 1).
 hipError_t launch_attn_mfma(const AttnParams &p, int kv_dtype, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnParams &p, int kv_dtype, hipStream_t stream);
+hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream);
 
 constexpr int kSampleChunk = 8192;  // vocabulary entries per sampler workgroup
 constexpr int kSampleThreads = 256;

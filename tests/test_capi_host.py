@@ -50,11 +50,11 @@ def _attn(**kw):
     base = (ctypes.addressof(buf) + 255) & ~255
     a = dict(q=base, k=base, v=base, ks=None, vs=None, table=base, lens=base, out=base,
              B=2, T=5, Hq=32, Hkv=8, d=128, bs=16, maxb=8, nb=16, kv=1, scale=0.088,
-             ws=base, wsb=1 << 14, stream=None, algo=0, bps=0)
+             ws=base, wsb=1 << 14, stream=None, algo=0, bps=0, ev=None)
     a.update(kw)
     return L.spec_verify_attn_ex(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["table"], a["lens"], a["out"],
                                  a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["maxb"], a["nb"],
-                                 a["kv"], a["scale"], a["ws"], a["wsb"], a["stream"], a["algo"], a["bps"])
+                                 a["kv"], a["scale"], a["ws"], a["wsb"], a["stream"], a["algo"], a["bps"], a["ev"])
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -7,6 +7,12 @@ call (the rejection sampler over the K+1 target rows), on seeded synthetic
 inputs already resident in HBM.  Several copies of the inputs are rotated so
 that every step reads cold data (the 256 MiB Infinity Cache cannot hold them).
 
+Two timed passes of --steps steps each: an eager pass with HIP events
+around every call on the launch stream (per-kernel times, from which the
+roofline figure of the main attention kernel comes), then a pass that
+replays each step from a captured HIP graph (one graph per input copy; the
+headline steps/s, since a serving loop would replay the step the same way).
+
 Prints one JSON line.  Default workload: the LLaMA-3-8B-style layer (B=8,
 Hq=32, Hkv=8, d=128, context 4096, 16-token pages, K=5, bf16 KV, V=128256).
 """
@@ -39,6 +45,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0: enough to defeat the MALL)")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 vector ALU, 2 matrix cores")
     ap.add_argument("--bps", type=int, default=0, help="context pages per split (0: planner)")
+    ap.add_argument("--no-graph", action="store_true", help="headline from the eager pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
     ap.add_argument("--probe", choices=["none", "copy"], default="none",
@@ -168,6 +175,12 @@ def main():
         if ev is not None:
             hev.record(ev[3], sh)
 
+    def step_on(st, strm):
+        sv.spec_verify_attn(st["q"], st["k"], st["v"], st["table"], st["lens"], out, ws_a,
+                            k_scale=st.get("ks"), v_scale=st.get("vs"), kv_dtype=a.kv_dtype,
+                            stream=strm, algo=args.algo, blocks_per_split=args.bps)
+        sv.spec_verify_sample(st["logits"], st["probs"], st["tokens"], st["u"], n_acc, toks, ws_s, stream=strm)
+
     for i in range(args.warmup):
         step(sets[i % copies])
     torch.cuda.synchronize()
@@ -181,10 +194,46 @@ def main():
         step(sets[i % copies], evs[i])
     hev.record(t1, sh)
     torch.cuda.synchronize()
-    ms_step = hev.ms(t0, t1) / args.steps
+    eager_ms_step = hev.ms(t0, t1) / args.steps
     main_ms = np.array([hev.ms(e[0], e[1]) for e in evs])   # main attention kernel
     attn_ms = np.array([hev.ms(e[0], e[2]) for e in evs])   # attention call (main + split merge)
     samp_ms = np.array([hev.ms(e[2], e[3]) for e in evs])   # sampler call
+    print("# eager pass: %.1f us/step" % (eager_ms_step * 1e3), file=sys.stderr, flush=True)
+
+    graph_ms_step = None
+    if not args.no_graph:
+        graphs = []
+        side = torch.cuda.Stream(dev)  # default priority
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for st in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step_on(st, side)
+                graphs.append(g)
+        stream.wait_stream(side)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        g0, g1 = hev.create(), hev.create()
+        hev.record(g0, sh)
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        hev.record(g1, sh)
+        torch.cuda.synchronize()
+        graph_ms_step = hev.ms(g0, g1) / args.steps
+        # the last replayed copy must reproduce the eager result of that copy
+        last = (args.steps - 1) % copies
+        step(sets[last])
+        torch.cuda.synchronize()
+        ref = (n_acc.clone(), toks.clone())
+        graphs[last].replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(ref[0], n_acc) and torch.equal(ref[1], toks)):
+            raise RuntimeError("graph replay disagrees with the eager step")
+        del graphs
+        print("# graph pass: %.1f us/step" % (graph_ms_step * 1e3), file=sys.stderr, flush=True)
+    ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     hev.close()
     n_rej = int((n_acc.cpu().numpy() < s.K).sum())
     samp_bytes = W.sample_algorithmic_bytes(s, n_rej)
@@ -206,6 +255,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "timing": "HIP graph replay per step" if graph_ms_step is not None else "eager launches",
+        "eager_ms_per_step": eager_ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -13,9 +13,13 @@ SOURCES = ["capi.cpp", "attn.hip", "sample.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc emits no packed fp32 add/mul/fma (v_pk_*_f32).
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-result"]
+# amdgpu-mfma-vgpr-form: matrix-core accumulators live in ordinary VGPRs, so
+# the attention loop's rare rescale branch does not force a copy of every
+# accumulator between the AGPR and VGPR files on each iteration.
+COMPILE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                 "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                 "-Wall", "-Wno-unused-result"]
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
@@ -28,8 +32,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") or src.endswith(".cpp") else []
-        cmd = ["hipcc", *FLAGS[:-2], "-c", *lang, os.path.join(CSRC, src), "-o", obj]
-        cmd = [c for c in cmd if c != "-shared"]
+        cmd = ["hipcc", *COMPILE_FLAGS, "-c", *lang, os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -122,12 +122,16 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 
 // Split merge (flash-decoding second pass): one wave per (unit, row).
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s o_s 2^(m_s - M) / L.
-// Lanes first hold one split each (statistics, reduced with DPP), then
-// slices of the head dim; eight splits' partial rows are in flight at once.
+// Lanes hold one split's statistics each (reduced with DPP) and slices of
+// the head dim.  The context length, the statistics and the partial rows of
+// the first eight splits are requested together (all lie inside the
+// workspace), so the common case costs one round trip to memory; entries of
+// splits past the context are discarded.
 template <int D>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
     constexpr int PER = D / 64;  // floats per lane
+    constexpr int NB = 8;        // splits whose partial rows are requested at once
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int units = p.B * p.Hkv;
@@ -135,35 +139,68 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
         return;
     const int unit = gw / p.TG, row = gw - unit * p.TG;
     const int b = unit / p.Hkv, g = unit - b * p.Hkv;
-    int L = p.context_lens[b];
-    L = L < 0 ? 0 : (L > p.max_blocks * kBlock ? p.max_blocks * kBlock : L);
+    const int msp = p.max_splits;
+    const float ninf = -__builtin_inff();
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + (size_t)unit * msp * p.TG + row;
+    const float *po = p.part_o + ((size_t)unit * msp * p.TG + row) * D + lane * PER;
+    const size_t sstride = (size_t)p.TG * D;  // floats between splits' partial rows
+
+    const int Lraw = p.context_lens[b];
+    const float2 st0 = lane < msp ? ml[(size_t)lane * p.TG] : make_float2(ninf, 0.0f);
+    float o[NB][PER];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            o[j][k] = 0.0f;
+        if (j < msp) {
+            if constexpr (PER == 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(po + j * sstride);
+                o[j][0] = v.x;
+                o[j][1] = v.y;
+            } else {
+                o[j][0] = po[j * sstride];
+            }
+        }
+    }
+    const int L = Lraw < 0 ? 0 : (Lraw > p.max_blocks * kBlock ? p.max_blocks * kBlock : Lraw);
     const int nblk = (L + kBlock - 1) / kBlock;
     const int ns = (nblk + p.bps - 1) / p.bps;
     if (ns <= 1)
         return;  // written directly by the attention kernel
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + (size_t)unit * p.max_splits * p.TG + row;
-    const float ninf = -__builtin_inff();
-    float M = ninf;
-    for (int s = lane; s < ns; s += kWave)
-        M = fmaxf(M, ml[(size_t)s * p.TG].x);
-    M = wave_max_f32(M);
+
+    float mloc = lane < ns ? st0.x : ninf;
+    for (int s = lane + kWave; s < ns; s += kWave)
+        mloc = fmaxf(mloc, ml[(size_t)s * p.TG].x);
+    const float M = wave_max_f32(mloc);
     double Lsum = 0.0;
-    for (int s = lane; s < ns; s += kWave) {
+    if (lane < ns && st0.x != ninf)
+        Lsum = (double)(st0.y * __builtin_amdgcn_exp2f(st0.x - M));
+    for (int s = lane + kWave; s < ns; s += kWave) {
         const float2 v = ml[(size_t)s * p.TG];
         if (v.x != ninf)
             Lsum += (double)(v.y * __builtin_amdgcn_exp2f(v.x - M));
     }
     const float inv = (float)(1.0 / wave_sum_f64(Lsum));
-    const float *po = p.part_o + ((size_t)unit * p.max_splits * p.TG + row) * D + lane * PER;
+
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k)
         acc[k] = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-        float o[8][PER];
-        float f[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
+        if (j < ns) {  // uniform
+            const float mj = readlane_f32(st0.x, j);
+            const float f = (mj == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                acc[k] += f * o[j][k];
+        }
+    }
+    for (int s0 = NB; s0 < ns; s0 += NB) {
+        float f[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
             const int s = s0 + j;
             f[j] = 0.0f;
 #pragma unroll
@@ -173,16 +210,16 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
                 const float ms = ml[(size_t)s * p.TG].x;
                 f[j] = (ms == ninf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
                 if constexpr (PER == 2) {
-                    const float2 v = *reinterpret_cast<const float2 *>(po + (size_t)s * p.TG * D);
+                    const float2 v = *reinterpret_cast<const float2 *>(po + s * sstride);
                     o[j][0] = v.x;
                     o[j][1] = v.y;
                 } else {
-                    o[j][0] = po[(size_t)s * p.TG * D];
+                    o[j][0] = po[s * sstride];
                 }
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int k = 0; k < PER; ++k)
                 acc[k] += f[j] * o[j][k];
@@ -218,21 +255,21 @@ __device__ __forceinline__ int4v page_desc(const unsigned char *base, int page, 
 }
 
 // Direct HBM -> LDS copy (gfx950 buffer_load ... lds): every lane moves BYTES
-// bytes from desc + voff + soff to LDS address lds + lane * BYTES.  Issued
-// from inline assembly so that the kernel, not the compiler, decides how
-// many copies stay in flight; completion is awaited with wait_dma<N>().
-// m0 holds the LDS address of the copy; no other instruction in these
-// kernels reads m0.  lgkmcnt(0) first: the copy may overwrite LDS that this
-// wave has only just finished reading.
+// bytes from desc + voff + soff to LDS address lds + lane * BYTES (the LDS
+// base travels in m0, which the "{m0}" operand hands to the compiler).
+// Issued from inline assembly so that the kernel, not the compiler, decides
+// how many copies stay in flight; completion is awaited with wait_dma<N>().
+// lgkmcnt(0) first: the copy may overwrite LDS that this wave has only just
+// finished reading.
 template <int BYTES>
 __device__ __forceinline__ void dma_to_lds(uint32_t lds, int4v desc, int voff, int soff)
 {
     if constexpr (BYTES == 16)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :: "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds) : "memory");
     else
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                     :: "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // Waits until at most N of this wave's memory loads are outstanding (they
@@ -240,8 +277,16 @@ __device__ __forceinline__ void dma_to_lds(uint32_t lds, int4v desc, int voff, i
 template <int N>
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
+// All-ones if V slot `key` (absolute position) is part of the context,
+// else zero: slots past the context may hold anything, NaN included, and
+// are cleared with a mask (no branch) before they reach the PV product.
+__device__ __forceinline__ uint32_t slot_keep(bool tail, int key, int L)
+{
+    return (tail && key >= L) ? 0u : 0xFFFFFFFFu;
+}
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+
 // Eight stored values -> four packed bf16 pairs.
-__device__ __forceinline__ uint4 to_bf16x8(uint4 v) { return v; }
 __device__ __forceinline__ uint4 to_bf16x8(uint2 v)
 {
     const uint2 lo = e4m3x4_to_bf16x4(v.x);
@@ -277,6 +322,50 @@ struct PageGeom {
     }
 };
 
+// Merges the kNW waves' tiles of one workgroup and stores the result:
+// normalised output when the unit has a single split, else the unnormalised
+// partial (o, max, sum) for the merge kernel.  tiles: kNW x [RG*16][D+4]
+// floats; sm/sl: per-wave row max (base-2 units) and row sum.
+template <int D, int RG>
+__device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles,
+                                                      const float (*sm)[64], const float (*sl)[64],
+                                                      int unit, int split, int b, int g, int nsplit)
+{
+    constexpr int OP = D + 4;
+    constexpr int C4 = D / 4;
+    constexpr int WT = RG * 16 * OP;  // floats per wave tile
+    const float ninf = -__builtin_inff();
+    const int TG = p.TG, G = p.G;
+    const size_t pbase = ((size_t)unit * p.max_splits + split) * TG;
+    for (int idx = threadIdx.x; idx < TG * C4; idx += kAttnThreads) {
+        const int row = idx / C4, c4 = idx - row * C4;
+        float M = sm[0][row];
+#pragma unroll
+        for (int v = 1; v < kNW; ++v)
+            M = fmaxf(M, sm[v][row]);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float Ls = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kNW; ++v) {
+            const float mv = sm[v][row];
+            const float f = (mv == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * WT + row * OP + c4 * 4);
+            o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
+            Ls += f * sl[v][row];
+        }
+        if (nsplit == 1) {
+            const float inv = 1.0f / Ls;
+            o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+            const int t = row / G, hh = row - t * G;
+            *reinterpret_cast<float4 *>(p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)g * G + hh) * D + c4 * 4) = o;
+        } else {
+            *reinterpret_cast<float4 *>(p.part_o + (pbase + row) * D + c4 * 4) = o;
+            if (c4 == 0)
+                reinterpret_cast<float2 *>(p.part_ml)[pbase + row] = make_float2(M, Ls);
+        }
+    }
+}
+
 template <int D, int RG, bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParams p)
 {
@@ -287,50 +376,85 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
     constexpr int EB = PG::EB;
     constexpr int OP = D + 4;
     constexpr int RING = kNW * NS * PG::STAGE;
-    constexpr int OBUF_BYTES = RG * 16 * OP * 4;
-    // smem holds, in turn: the waves' page rings, then the merged output tile.
+    constexpr int OBUF_BYTES = kNW * RG * 16 * OP * 4;
+    // smem holds, in turn: the waves' page rings, then each wave's
+    // unnormalised output tile.
     constexpr int SMEM = RING > OBUF_BYTES ? RING : OBUF_BYTES;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    __shared__ float s_m[kNW][64], s_l[kNW][64], s_mrow[64], s_lrow[64];
+    __shared__ float s_m[kNW][64], s_l[kNW][64];
     __shared__ int s_pages[kMaxBps];
 
-    UnitWork w;
-    if (!decode_work(p, w))
+    // Work item from the block index alone (see decode_work), so that every
+    // load of the prologue below can be in flight at once.
+    const int per_xcd = p.grid >> 3;
+    const int wg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int unit = wg / p.max_splits;
+    if (unit >= p.B * p.Hkv)
         return;
+    const int split = wg - unit * p.max_splits;
+    const int b = unit / p.Hkv, g = unit - b * p.Hkv;
+    const int blk_begin = split * p.bps;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int lane = tid & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int T = p.T, G = p.G, TG = p.TG, Hkv = p.Hkv;
-    const int L = w.L;
-    const int npg = w.blk_end - w.blk_begin;
     const float ninf = -__builtin_inff();
 
-    // physical pages of this split, fetched once with one coalesced read
-    for (int i = tid; i < npg; i += kAttnThreads)
-        s_pages[i] = clamp_block(p.block_table[(size_t)w.b * p.max_blocks + w.blk_begin + i], p.num_blocks);
+    // ---- prologue: one round trip to memory.  The context length, the
+    // split's page ids (into LDS, and this wave's first NS-1 directly) and Q
+    // are all requested before any of them is used.  Table entries past the
+    // context are read (they are in bounds) but never used.
+    const int32_t *trow = p.block_table + (size_t)b * p.max_blocks + blk_begin;
+    const int avail = min(p.bps, p.max_blocks - blk_begin);
+    const int Lraw = p.context_lens[b];
+    int first[NS - 1];
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) {
+        const int i = wave + k * kNW;
+        first[k] = i < avail ? trow[i] : 0;
+    }
+    for (int i = tid; i < avail; i += kAttnThreads)
+        s_pages[i] = clamp_block(trow[i], p.num_blocks);
+    float4 qraw[RG][NDC][2];
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt) {
+        const int row = rt * 16 + l16;
+        const bool valid = row < TG;
+        const int t = valid ? row / G : 0;
+        const int hh = valid ? row - t * G : 0;
+        const float *src = p.q + (((size_t)b * T + t) * p.Hq + (size_t)g * G + hh) * D;
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            qraw[rt][dc][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+            qraw[rt][dc][1] = qraw[rt][dc][0];
+            if (valid) {
+                qraw[rt][dc][0] = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4));
+                qraw[rt][dc][1] = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4) + 4);
+            }
+        }
+    }
+    const int L = Lraw < 0 ? 0 : (Lraw > p.max_blocks * kBlock ? p.max_blocks * kBlock : Lraw);
+    const int nblk = (L + kBlock - 1) / kBlock;
+    if (blk_begin >= nblk)
+        return;  // uniform over the workgroup: nothing of this split is visible
+    const int npg = min(blk_begin + p.bps, nblk) - blk_begin;
+    const int nsplit = (nblk + p.bps - 1) / p.bps;
 
-    // Q tile of this unit as the B operand of S^T = K Q^T (row = l16, eight dims).
+    // Q tile as the B operand of S^T = K Q^T (row = l16, eight dims), bf16,
+    // pre-scaled into base-2 units.
     bf16x8 qf[RG][NDC];
     int lim[RG];
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
         const int row = rt * 16 + l16;
-        const bool valid = row < TG;
-        const int t = valid ? row / G : T - 1;
-        const int hh = valid ? row - (row / G) * G : 0;
-        lim[rt] = L - T + t;
-        const float *src = p.q + (((size_t)w.b * T + t) * p.Hq + (size_t)w.g * G + hh) * D;
+        lim[rt] = L - T + (row < TG ? row / G : T - 1);
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
-            if (valid) {
-                a = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4));
-                c = *reinterpret_cast<const float4 *>(src + PG::qdim(dc, q4) + 4);
-            }
             const float sc = p.qscale;
+            const float4 a = qraw[rt][dc][0], c = qraw[rt][dc][1];
             uint4 u;
             u.x = f32x2_to_bf16x2(a.x * sc, a.y * sc);
             u.y = f32x2_to_bf16x2(a.z * sc, a.w * sc);
@@ -339,7 +463,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             qf[rt][dc] = __builtin_bit_cast(bf16x8, u);
         }
     }
-    __syncthreads();  // s_pages ready
 
     // Running state per row tile: reference maximum m (base-2 units), the
     // row sums and the unnormalised outputs O^T (lane: dims 4*q4+i of tile
@@ -364,7 +487,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
     const unsigned char *vbase = static_cast<const unsigned char *>(p.v_cache);
     const int slot_stride = Hkv * D * EB;                          // bytes between slots of a page
     const uint32_t page_bytes = (uint32_t)slot_stride * kBlock;    // bytes of one page (all heads)
-    const int head_off = w.g * D * EB;
+    const int head_off = g * D * EB;
     // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
     const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
     // V copy: lane -> slot group va (VS slots), dim group vc
@@ -386,10 +509,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * NS * PG::STAGE;
     unsigned char *ring = smem + wave * NS * PG::STAGE;
 
-    // This wave's pages are w.blk_begin + wave + k*kNW, k = 0, 1, ...
+    // This wave's pages are blk_begin + wave + k*kNW, k = 0, 1, ...
     const int nk = npg > wave ? (npg - wave + kNW - 1) / kNW : 0;
-    auto issue = [&](int k) {
-        const int ph = s_pages[wave + k * kNW];
+    auto issue = [&](int k, int ph) {
         const int stage = k % NS;
         const uint32_t lds = ring_lds + stage * PG::STAGE;
         const int4v dk = page_desc(kbase, __builtin_amdgcn_readfirstlane(ph), page_bytes);
@@ -399,15 +521,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             dma_to_lds<16>(lds + i * 1024, dk, k_voff, FP8 ? i * 64 : i * 32 * EB);
 #pragma unroll
         for (int j = 0; j < PG::NVI; ++j)
-            dma_to_lds<PG::VBYTES>(lds + PG::PT + j * 64 * PG::VBYTES, dv, v_voff,
-                                   (PG::VBYTES == 4 || FP8) ? j * slot_stride : j * slot_stride);
+            dma_to_lds<PG::VBYTES>(lds + PG::PT + j * 64 * PG::VBYTES, dv, v_voff, j * slot_stride);
     };
-    for (int k = 0; k < NS - 1 && k < nk; ++k)
-        issue(k);
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+        if (k < nk)
+            issue(k, clamp_block(first[k], p.num_blocks));
+    __syncthreads();  // s_pages ready
 
     for (int k = 0; k < nk; ++k) {
         if (k + NS - 1 < nk)
-            issue(k + NS - 1);
+            issue(k + NS - 1, s_pages[wave + (k + NS - 1) * kNW]);
         // wait for page k: the copies of up to NS-1 younger pages may stay in flight
         const int younger = (nk - 1 - k) < (NS - 1) ? (nk - 1 - k) : (NS - 1);
         if (younger >= 3)
@@ -419,7 +543,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         else
             wait_dma<0>();
         const int pg = wave + k * kNW;
-        const int key0 = (w.blk_begin + pg) * kBlock;
+        const int key0 = (blk_begin + pg) * kBlock;
         const int ph = s_pages[pg];
         unsigned char *st = ring + (k % NS) * PG::STAGE;
 
@@ -462,8 +586,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 wv[j] = e4m3x4_to_bf16x4(raw[j]);
-                if (tail && key0 + va * 4 + j >= L)
-                    wv[j] = make_uint2(0u, 0u);
+                const uint32_t keep = slot_keep(tail, key0 + va * 4 + j, L);
+                wv[j].x &= keep;
+                wv[j].y &= keep;
             }
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
@@ -482,8 +607,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             for (int j = 0; j < 2; ++j) {
                 wv[j][0] = to_bf16x8(make_uint2(raw[j].x, raw[j].y));
                 wv[j][1] = to_bf16x8(make_uint2(raw[j].z, raw[j].w));
-                if (tail && key0 + va * 2 + j >= L)
-                    wv[j][0] = wv[j][1] = make_uint4(0u, 0u, 0u, 0u);
+                const uint32_t keep = slot_keep(tail, key0 + va * 2 + j, L);
+                wv[j][0] = and4(wv[j][0], keep);
+                wv[j][1] = and4(wv[j][1], keep);
             }
 #pragma unroll
             for (int g = 0; g < 2; ++g)
@@ -498,11 +624,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             constexpr int VS = PG::VS;
             uint4 wv[VS];
 #pragma unroll
-            for (int j = 0; j < VS; ++j) {
+            for (int j = 0; j < VS; ++j)
                 wv[j] = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
-                if (tail && key0 + va * VS + j >= L)
-                    wv[j] = make_uint4(0u, 0u, 0u, 0u);
-            }
+#pragma unroll
+            for (int j = 0; j < VS; ++j)
+                wv[j] = and4(wv[j], slot_keep(tail, key0 + va * VS + j, L));
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
                 const int de = vc * 8 + 2 * wd;
@@ -598,9 +724,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         }
     }
 
-    // ---- merge the four waves of the workgroup (LDS) ----
+    // ---- epilogue: every wave parks its unnormalised tile and (max, sum)
+    // in LDS; one pass then merges the waves and writes the result.
     wait_dma<0>();
-    __syncthreads();  // every wave is done with its ring; smem becomes obuf
+    __syncthreads();  // every wave is done with its ring; smem becomes the tiles
+    float *obuf = reinterpret_cast<float *>(smem) + wave * (RG * 16 * OP);
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
         float ls;
@@ -615,49 +743,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             s_m[wave][rt * 16 + l16] = m[rt];
             s_l[wave][rt * 16 + l16] = ls;
         }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const floatx4 a = acc[dt][rt];
+            *reinterpret_cast<float4 *>(obuf + (rt * 16 + l16) * OP + dt * 16 + q4 * 4) =
+                make_float4(a[0], a[1], a[2], a[3]);
+        }
     }
     __syncthreads();
-    float fac[RG];
-#pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
-        const int row = rt * 16 + l16;
-        float M = s_m[0][row];
-#pragma unroll
-        for (int v2 = 1; v2 < kNW; ++v2)
-            M = fmaxf(M, s_m[v2][row]);
-        fac[rt] = (m[rt] == ninf) ? 0.0f : __builtin_amdgcn_exp2f(m[rt] - M);
-        if (wave == 0 && q4 == 0) {
-            float Ls = 0.0f;
-#pragma unroll
-            for (int v2 = 0; v2 < kNW; ++v2)
-                if (s_m[v2][row] != ninf)
-                    Ls += s_l[v2][row] * __builtin_amdgcn_exp2f(s_m[v2][row] - M);
-            s_mrow[row] = M;
-            s_lrow[row] = Ls;
-        }
-    }
-    float *obuf = reinterpret_cast<float *>(smem);
-#pragma unroll
-    for (int v2 = 0; v2 < kNW; ++v2) {
-        if (wave == v2) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int rt = 0; rt < RG; ++rt) {
-                    float4 *dst = reinterpret_cast<float4 *>(obuf + (rt * 16 + l16) * OP + dt * 16 + q4 * 4);
-                    const floatx4 a = acc[dt][rt] * fac[rt];
-                    if (v2 == 0) {
-                        *dst = make_float4(a[0], a[1], a[2], a[3]);
-                    } else {
-                        float4 o = *dst;
-                        o.x += a[0]; o.y += a[1]; o.z += a[2]; o.w += a[3];
-                        *dst = o;
-                    }
-                }
-        }
-        __syncthreads();
-    }
-    finish_unit<D>(p, w, obuf, s_mrow, s_lrow);
+    merge_waves_and_store<D, RG>(p, reinterpret_cast<const float *>(smem), s_m, s_l, unit, split, b, g, nsplit);
 }
 
 // ---------------------------------------------------------------- VALU kernel

@@ -88,8 +88,10 @@ SamplePlan plan_sample(int B, int K, int V)
     off = align256(off + (size_t)B * 16);
     pl.off_stats = off;
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 16);
+    pl.off_rowx = off;
+    off = align256(off + (size_t)B * K * 8);
     pl.off_mass = off;
-    off = align256(off + (size_t)B * pl.nchunk * 2 * 8);
+    off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
     pl.total = off;
     return pl;
 }
@@ -297,8 +299,10 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
         return fail(SV_ERR_SHAPE, "K must be <= 15 (got %d)", K);
     if (V > sv::kMaxSampleChunks * sv::kSampleChunk)
         return fail(SV_ERR_UNSUPPORTED, "V must be <= %d (got %d)", sv::kMaxSampleChunks * sv::kSampleChunk, V);
-    if ((long long)B * (K + 1) * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL)
-        return fail(SV_ERR_SHAPE, "B*(K+1)*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk);
+    if ((long long)B * (K + 1) * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL ||
+        (long long)B * ((V + sv::kSampleSub - 1) / sv::kSampleSub) > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "B*(K+1)*ceil(V/%d) or B*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk,
+                    sv::kSampleSub);
     if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
         (accept_prob && !aligned(accept_prob, 4)))
@@ -321,7 +325,8 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
     p.accept_prob = accept_prob;
     p.seq_state = ws + pl.off_state;
     p.row_stats = ws + pl.off_stats;
-    p.chunk_mass = reinterpret_cast<double *>(ws + pl.off_mass);
+    p.row_x = ws + pl.off_rowx;
+    p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
     p.B = B;
     p.K = K;
     p.V = V;

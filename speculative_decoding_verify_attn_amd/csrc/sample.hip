@@ -12,14 +12,17 @@
 // fences or counters are needed):
 //   rowstats  grid (vocab chunk x row): one streaming pass over every target
 //             row; per chunk the maximum and sum_j exp(l_j - max) (hardware
-//             exp2, fp64 accumulation), reduced across the wave with DPP;
-//   decide    grid (vocab chunk x sequence): every workgroup merges the row
-//             statistics of its sequence, runs the (at most 15) acceptance
-//             tests in fp64, and sums the weights of the chosen row over its
-//             chunk in fp64;
-//   pick      grid (sequence): one wave prefix-scans the chunk masses and
-//             locates the chunk holding u_K * S; the workgroup rescans that
-//             chunk with a prefix scan and writes the outputs.
+//             exp2, fp64 accumulation), reduced across the wave with DPP.
+//             The first chunk's workgroup of draft row i also records the
+//             target logit and draft probability of x_i;
+//   decide    grid (1024-entry sub-chunk x sequence): every workgroup merges
+//             the row statistics of its sequence, runs the (at most 15)
+//             acceptance tests in fp64, and sums the weights of the chosen
+//             row over its sub-chunk in fp64;
+//   pick      grid (sequence): one wave prefix-scans the sub-chunk masses and
+//             locates the sub-chunk holding u_K * S; the workgroup rescans
+//             that sub-chunk (four entries per thread) with a prefix scan and
+//             writes the outputs.
 // The acceptance tests run in fp64; the weights take fp32 exp of an exactly
 // split argument (about 1e-7 relative) and every sum runs in fp64, so the
 // decisions agree with an exact evaluation except within ~1e-7 of a
@@ -32,11 +35,18 @@ namespace {
 
 constexpr int kPer = kSampleChunk / kSampleThreads;  // 32 entries per thread
 constexpr int kNWs = kSampleThreads / kWave;
+static_assert(kSampleSub == 4 * kSampleThreads, "a sub-chunk is four entries per thread");
 
 struct RowStat {
     float m;
     float pad;
     double z;
+};
+
+// Target logit and draft probability of draft token x_i.
+struct RowX {
+    float lx;
+    float qx;
 };
 
 // What the draw of one sequence needs from the decide pass.
@@ -100,6 +110,8 @@ __device__ __forceinline__ double block_sum(double v, double *s_red)
     return r;
 }
 
+__device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(SampleParams p)
 {
@@ -107,10 +119,20 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     __shared__ double s_d[kNWs];
     const int row = blockIdx.x / p.nchunk;
     const int chunk = blockIdx.x - row * p.nchunk;
+    const int K = p.K, K1 = K + 1;
+    const int b = row / K1, i = row - b * K1;
     const int base = chunk * kSampleChunk;
     const int n = min(kSampleChunk, p.V - base);
     float v[kPer];
     load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
+    // x_i's own entries, fetched while the chunk streams in.
+    const bool rec = chunk == 0 && i < K;
+    RowX rx{0.0f, 0.0f};
+    if (rec) {
+        const int x = clamp_token(p.tokens[(size_t)b * K + i], p.V);
+        rx.lx = p.logits[(size_t)row * p.V + x];
+        rx.qx = p.probs[((size_t)b * K + i) * p.V + x];
+    }
     float mx = v[0];
 #pragma unroll
     for (int k = 1; k < kPer; ++k)
@@ -130,6 +152,8 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
         st.pad = 0.0f;
         st.z = z;
         static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
+        if (rec)
+            static_cast<RowX *>(p.row_x)[(size_t)b * K + i] = rx;
     }
 }
 
@@ -164,6 +188,24 @@ __device__ __forceinline__ double weight(float l, float q, float M, double invZ,
     return r > 0.0 ? r : 0.0;
 }
 
+// Loads this thread's four consecutive entries tid*4 .. tid*4+3 of a
+// sub-chunk of n entries; missing entries read `fill`.
+template <bool VEC>
+__device__ __forceinline__ void load_sub(const float *row, int n, float fill, float (&v)[4])
+{
+    const int e0 = threadIdx.x * 4;
+    if constexpr (VEC) {
+        float4 x = make_float4(fill, fill, fill, fill);
+        if (e0 < n)  // n is a multiple of 4 on this path
+            x = *reinterpret_cast<const float4 *>(row + e0);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = e0 + k < n ? row[e0 + k] : fill;
+    }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
 {
@@ -172,45 +214,47 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     __shared__ double s_ratio[16];
     __shared__ int s_acc[16];
     __shared__ int s_n;
-    __shared__ double s_d[kNWs];
+    __shared__ double s_part[kNWs][2];
 
-    const int b = blockIdx.x / p.nchunk;
-    const int chunk = blockIdx.x - b * p.nchunk;
+    const int nsub = (p.V + kSampleSub - 1) / kSampleSub;
+    const int b = blockIdx.x / nsub;
+    const int sub = blockIdx.x - b * nsub;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int K = p.K, K1 = K + 1, V = p.V;
 
-    // 1. Row statistics of the K+1 rows of this sequence: one wave per row,
-    //    lanes over vocabulary chunks (all loads in flight together).
-    {
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int i = wave; i < K1; i += kNWs) {
-            const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
-            float mloc = -__builtin_inff();
-            for (int c = lane; c < p.nchunk; c += kWave)
-                mloc = fmaxf(mloc, st[c].m);
-            const float M = wave_max_f32(mloc);
-            double zloc = 0.0;
-            for (int c = lane; c < p.nchunk; c += kWave) {
-                const RowStat r = st[c];
-                zloc += r.z * exp((double)r.m - (double)M);
-            }
-            const double Z = wave_sum_f64(zloc);
-            if (lane == 0) {
-                s_M[i] = M;
-                s_Z[i] = Z;
-            }
+    // 1. Row statistics of the K+1 rows of this sequence (one wave per row,
+    //    lanes over vocabulary chunks) and the draft tokens' entries, all
+    //    requested together.
+    RowX rx{0.0f, 0.0f};
+    float u = 0.0f;
+    if (tid < K) {
+        rx = static_cast<const RowX *>(p.row_x)[(size_t)b * K + tid];
+        u = p.uniforms[(size_t)b * K1 + tid];
+    }
+    for (int i = wave; i < K1; i += kNWs) {
+        const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
+        float mloc = -__builtin_inff();
+        for (int c = lane; c < p.nchunk; c += kWave)
+            mloc = fmaxf(mloc, st[c].m);
+        const float M = wave_max_f32(mloc);
+        double zloc = 0.0;
+        for (int c = lane; c < p.nchunk; c += kWave) {
+            const RowStat r = st[c];
+            zloc += r.z * exp((double)r.m - (double)M);
+        }
+        const double Z = wave_sum_f64(zloc);
+        if (lane == 0) {
+            s_M[i] = M;
+            s_Z[i] = Z;
         }
     }
     __syncthreads();
     // 2. Acceptance tests u_i * q_i(x_i) < p_i(x_i).
     if (tid < K) {
-        int x = p.tokens[(size_t)b * K + tid];
-        x = x < 0 ? 0 : (x >= V ? V - 1 : x);
-        const float lx = p.logits[((size_t)b * K1 + tid) * V + x];
-        const double a = target_prob(lx, s_M[tid], 1.0 / s_Z[tid]);
-        const double c = (double)p.probs[((size_t)b * K + tid) * V + x];
-        const double u = (double)p.uniforms[(size_t)b * K1 + tid];
-        s_acc[tid] = (u * c < a) ? 1 : 0;
+        const double a = target_prob(rx.lx, s_M[tid], 1.0 / s_Z[tid]);
+        const double c = (double)rx.qx;
+        s_acc[tid] = ((double)u * c < a) ? 1 : 0;
         s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
     }
     __syncthreads();
@@ -228,58 +272,59 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     const bool residual = n < K;
     const float M = s_M[n];
     const double invZ = 1.0 / s_Z[n];
-    const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
-    const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
 
-    // 3. Mass of this chunk: residual (or bonus) weights and plain target mass.
-    {
-        const int base = chunk * kSampleChunk;
-        const int cnt = min(kSampleChunk, V - base);
-        float lv[kPer], qv[kPer];
-        load_chunk<VEC>(lrow + base, cnt, -__builtin_inff(), lv);
-        if (residual)
-            load_chunk<VEC>(qrow + base, cnt, 0.0f, qv);
-        else
+    // 3. Mass of this sub-chunk: residual (or bonus) weights and plain
+    //    target mass.
+    const int base = sub * kSampleSub;
+    const int cnt = min(kSampleSub, V - base);
+    float lv[4], qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    load_sub<VEC>(p.logits + ((size_t)b * K1 + n) * V + base, cnt, -__builtin_inff(), lv);
+    if (residual)
+        load_sub<VEC>(p.probs + ((size_t)b * K + n) * V + base, cnt, 0.0f, qv);
+    double sw = 0.0, sp = 0.0;
 #pragma unroll
-            for (int k = 0; k < kPer; ++k)
-                qv[k] = 0.0f;
-        double sw = 0.0, sp = 0.0;
+    for (int k = 0; k < 4; ++k) {
+        const double pj = target_prob_fast(lv[k], M, invZ);
+        sp += pj;
+        if (residual) {
+            const double r = pj - (double)qv[k];
+            sw += r > 0.0 ? r : 0.0;
+        } else {
+            sw += pj;
+        }
+    }
+    sw = wave_sum_f64(sw);
+    sp = wave_sum_f64(sp);
+    if (lane == 0) {
+        s_part[wave][0] = sw;
+        s_part[wave][1] = sp;
+    }
+    __syncthreads();
+    if (tid < 2) {
+        double t = s_part[0][tid];
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const double pj = target_prob_fast(lv[k], M, invZ);
-            sp += pj;
-            if (residual) {
-                const double r = pj - (double)qv[k];
-                sw += r > 0.0 ? r : 0.0;
-            } else {
-                sw += pj;
-            }
-        }
-        sw = block_sum(sw, s_d);
-        sp = block_sum(sp, s_d);
-        if (tid == 0) {
-            p.chunk_mass[((size_t)b * p.nchunk + chunk) * 2 + 0] = sw;
-            p.chunk_mass[((size_t)b * p.nchunk + chunk) * 2 + 1] = sp;
-        }
+        for (int w = 1; w < kNWs; ++w)
+            t += s_part[w][tid];
+        p.sub_mass[((size_t)b * nsub + sub) * 2 + tid] = t;
     }
 
     // The first workgroup of the sequence records what the draw needs.
-    if (chunk == 0 && tid == 0) {
+    if (sub == 0 && tid == 0) {
         SeqState ss;
         ss.n = n;
         ss.m = M;
         ss.inv_z = invZ;
         static_cast<SeqState *>(p.seq_state)[b] = ss;
     }
-    if (chunk == 0 && p.accept_prob && tid < K)
+    if (sub == 0 && p.accept_prob && tid < K)
         p.accept_prob[(size_t)b * K + tid] = (float)s_ratio[tid];
 }
 
-// The draw: one workgroup per sequence.  Locates the vocabulary chunk that
-// holds u_K * S from the chunk masses (scanned in order), then rescans that
-// chunk: each thread owns a contiguous run of entries, the run sums are
-// prefix-scanned across the workgroup (DPP wave scan + LDS), and the first
-// entry whose cumulative weight exceeds u_K * S is the token.
+// The draw: one workgroup per sequence.  Wave 0 prefix-scans the sub-chunk
+// masses in order (DPP scan, 64 sub-chunks at a time) and locates the one
+// holding u_K * S; the workgroup then rescans it, each thread owning four
+// consecutive entries, with a workgroup prefix scan, and the first entry
+// whose cumulative weight exceeds u_K * S is the token.
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SampleParams p)
 {
@@ -290,7 +335,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int K = p.K, K1 = K + 1, V = p.V;
+    const int nsub = (V + kSampleSub - 1) / kSampleSub;
     const SeqState ss = static_cast<const SeqState *>(p.seq_state)[b];
     const int n = ss.n;
     const bool residual = n < K;
@@ -299,13 +346,10 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
     const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
 
-    // Wave 0 locates the chunk: totals by DPP sums, then an in-order DPP
-    // prefix scan over the chunk masses, 64 chunks at a time.
     if (tid < kWave) {
-        const int lane = tid;
-        const double *gmass = p.chunk_mass + (size_t)b * p.nchunk * 2;
+        const double *gmass = p.sub_mass + (size_t)b * nsub * 2;
         double sw = 0.0, sp = 0.0;
-        for (int c = lane; c < p.nchunk; c += kWave) {
+        for (int c = lane; c < nsub; c += kWave) {
             sw += gmass[2 * c];
             sp += gmass[2 * c + 1];
         }
@@ -319,12 +363,12 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
         double carry = 0.0, cum = 0.0;
         int cstar = -1, lastpos = -1;
         double cum_last = 0.0;
-        for (int c0 = 0; c0 < p.nchunk; c0 += kWave) {
+        for (int c0 = 0; c0 < nsub; c0 += kWave) {
             const int c = c0 + lane;
-            const double mc = c < p.nchunk ? gmass[2 * c + mode] : 0.0;
+            const double mc = c < nsub ? gmass[2 * c + mode] : 0.0;
             const double incl = wave_inclusive_scan_f64(mc) + carry;
-            const uint64_t hit = __ballot(c < p.nchunk && incl > tgt);
-            const uint64_t pos = __ballot(c < p.nchunk && mc > 0.0);
+            const uint64_t hit = __ballot(c < nsub && incl > tgt);
+            const uint64_t pos = __ballot(c < nsub && mc > 0.0);
             if (pos) {
                 const int ll = 63 - __builtin_clzll(pos);
                 lastpos = c0 + ll;
@@ -354,42 +398,37 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     __syncthreads();
     const bool use_resid = residual && !(s_mode & 1);
     const bool take_last = (s_mode & 2) != 0;
-    const int base = s_cstar * kSampleChunk;
-    const int cnt = min(kSampleChunk, V - base);
-    // This thread's contiguous run of kPer entries of the chosen chunk.
-    const int e0 = tid * kPer;
-    float lv[kPer], qv[kPer];
+    const int base = s_cstar * kSampleSub;
+    const int cnt = min(kSampleSub, V - base);
+    const int e0 = tid * 4;
+    float lv[4], qv[4];
     if constexpr (VEC) {
-#pragma unroll
-        for (int k = 0; k < kPer; k += 4) {
-            float4 x = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
-            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e0 + k < cnt) {  // cnt is a multiple of 4 on this path
-                x = *reinterpret_cast<const float4 *>(lrow + base + e0 + k);
-                if (use_resid)
-                    y = *reinterpret_cast<const float4 *>(qrow + base + e0 + k);
-            }
-            lv[k] = x.x; lv[k + 1] = x.y; lv[k + 2] = x.z; lv[k + 3] = x.w;
-            qv[k] = y.x; qv[k + 1] = y.y; qv[k + 2] = y.z; qv[k + 3] = y.w;
+        float4 x = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e0 < cnt) {  // cnt is a multiple of 4 on this path
+            x = *reinterpret_cast<const float4 *>(lrow + base + e0);
+            if (use_resid)
+                y = *reinterpret_cast<const float4 *>(qrow + base + e0);
         }
+        lv[0] = x.x; lv[1] = x.y; lv[2] = x.z; lv[3] = x.w;
+        qv[0] = y.x; qv[1] = y.y; qv[2] = y.z; qv[3] = y.w;
     } else {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
+        for (int k = 0; k < 4; ++k) {
             const bool ok = e0 + k < cnt;
             lv[k] = ok ? lrow[base + e0 + k] : -__builtin_inff();
             qv[k] = (ok && use_resid) ? qrow[base + e0 + k] : 0.0f;
         }
     }
-    double wv[kPer];
+    double wv[4];
     double seg = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
+    for (int k = 0; k < 4; ++k) {
         wv[k] = weight(lv[k], qv[k], M, invZ, use_resid);
         seg += wv[k];
     }
     // Exclusive prefix of the run sums across the workgroup.
     const double incl = wave_inclusive_scan_f64(seg);
-    const int wave = tid >> 6, lane = tid & 63;
     if (lane == 63)
         s_d[wave] = incl;
     __syncthreads();
@@ -400,7 +439,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     int cand = 0x7FFFFFFF, lastpos = -1;
     const double tgt = s_target;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
+    for (int k = 0; k < 4; ++k) {
         if (wv[k] > 0.0)
             lastpos = base + e0 + k;
         run += wv[k];
@@ -425,12 +464,10 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
 
     if (tid < K1) {
         int32_t v;
-        if (tid < n) {
-            const int x = p.tokens[(size_t)b * K + tid];
-            v = x < 0 ? 0 : (x >= V ? V - 1 : x);
-        } else {
+        if (tid < n)
+            v = clamp_token(p.tokens[(size_t)b * K + tid], V);
+        else
             v = (tid == n) ? token : -1;
-        }
         p.out_tokens[(size_t)b * K1 + tid] = v;
     }
     if (tid == 0)
@@ -453,7 +490,7 @@ hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
 {
     const dim3 block(kSampleThreads);
     const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
-    const dim3 g2((unsigned)(p.nchunk * p.B));
+    const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
     const dim3 g3((unsigned)p.B);
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);

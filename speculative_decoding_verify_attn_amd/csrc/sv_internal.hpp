@@ -49,6 +49,7 @@ hipError_t launch_attn_valu(const AttnParams &p, int kv_dtype, hipStream_t strea
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream);
 
 constexpr int kSampleChunk = 8192;  // vocabulary entries per sampler workgroup
+constexpr int kSampleSub = 1024;    // entries per sub-chunk (unit of the draw's rescan)
 constexpr int kSampleThreads = 256;
 constexpr int kMaxSampleChunks = 2048;  // V <= 2048 * 8192
 
@@ -62,14 +63,15 @@ struct SampleParams {
     float *accept_prob;      // [B][K] or null
     void *seq_state;         // [B] {accepted count, row max, 1/row sum} for the draw
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
-    double *chunk_mass;      // [B][nchunk][2] {residual weight, target mass}
+    void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
+    double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}
     int B, K, V, nchunk;
     int vec4;                // rows start 16-byte aligned and V % 4 == 0
 };
 
 struct SamplePlan {
     int nchunk;
-    size_t off_state, off_stats, off_mass, total;
+    size_t off_state, off_stats, off_rowx, off_mass, total;
 };
 
 SamplePlan plan_sample(int B, int K, int V);

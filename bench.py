@@ -186,19 +186,50 @@ def main():
     torch.cuda.synchronize()
     print("# warmup done (%d copies of %.1f MB)" % (copies, step_in_bytes / 1e6), file=sys.stderr, flush=True)
 
+    # A spin kernel holds the stream while the host enqueues the timed steps,
+    # so the GPU then runs them back to back and the events bracket GPU work,
+    # not host launch latency.
+    c0, c1 = hev.create(), hev.create()
+    hev.record(c0, sh)
+    torch.cuda._sleep(1 << 20)
+    hev.record(c1, sh)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(hev.ms(c0, c1), 1e-3)
+
+    def gate(n_steps):
+        torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.25 * n_steps)))
+
     evs = [[hev.create() for _ in range(4)] for _ in range(args.steps)]
     t0, t1 = hev.create(), hev.create()
     torch.cuda.synchronize()
+    gate(args.steps)
     hev.record(t0, sh)
     for i in range(args.steps):
         step(sets[i % copies], evs[i])
     hev.record(t1, sh)
     torch.cuda.synchronize()
     eager_ms_step = hev.ms(t0, t1) / args.steps
-    main_ms = np.array([hev.ms(e[0], e[1]) for e in evs])   # main attention kernel
+    main_ev_ms = np.array([hev.ms(e[0], e[1]) for e in evs])  # main attention kernel, per-step events
     attn_ms = np.array([hev.ms(e[0], e[2]) for e in evs])   # attention call (main + split merge)
     samp_ms = np.array([hev.ms(e[2], e[3]) for e in evs])   # sampler call
     print("# eager pass: %.1f us/step" % (eager_ms_step * 1e3), file=sys.stderr, flush=True)
+
+    # The main attention kernel alone: --steps back-to-back launches between
+    # two events on the launch stream (no event between launches, so the
+    # average is the kernel's own duration, as a kernel trace reports it).
+    k0, k1 = hev.create(), hev.create()
+    torch.cuda.synchronize()
+    gate(args.steps)
+    hev.record(k0, sh)
+    for i in range(args.steps):
+        st = sets[i % copies]
+        sv.spec_verify_attn(st["q"], st["k"], st["v"], st["table"], st["lens"], out, ws_a,
+                            k_scale=st.get("ks"), v_scale=st.get("vs"), kv_dtype=a.kv_dtype,
+                            stream=stream, algo=args.algo | sv.SV_ATTN_MAIN_ONLY, blocks_per_split=args.bps)
+    hev.record(k1, sh)
+    torch.cuda.synchronize()
+    main_ms = hev.ms(k0, k1) / args.steps
+    print("# main attention kernel: %.1f us per launch" % (main_ms * 1e3), file=sys.stderr, flush=True)
 
     graph_ms_step = None
     if not args.no_graph:
@@ -216,6 +247,7 @@ def main():
             graphs[i % copies].replay()
         torch.cuda.synchronize()
         g0, g1 = hev.create(), hev.create()
+        gate(args.steps)
         hev.record(g0, sh)
         for i in range(args.steps):
             graphs[i % copies].replay()
@@ -238,7 +270,7 @@ def main():
     n_rej = int((n_acc.cpu().numpy() < s.K).sum())
     samp_bytes = W.sample_algorithmic_bytes(s, n_rej)
 
-    attn_gbs = attn_bytes / (main_ms.mean() * 1e-3) / 1e9
+    attn_gbs = attn_bytes / (main_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -268,7 +300,8 @@ def main():
             "B": a.B, "K": s.K, "V": s.V, "context": int(a.context_lens.max()),
             "rotating_copies": copies,
         },
-        "attn_main_kernel_us": float(main_ms.mean() * 1e3),
+        "attn_main_kernel_us": float(main_ms * 1e3),
+        "attn_main_kernel_us_step_events": float(main_ev_ms.mean() * 1e3),
         "attn_us": float(attn_ms.mean() * 1e3),
         "attn_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
         "sample_us": float(samp_ms.mean() * 1e3),

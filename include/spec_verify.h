@@ -58,7 +58,12 @@ typedef enum {
 typedef enum {
     SV_ATTN_AUTO = 0,  /* matrix cores for bf16/fp8 storage, vector ALU for fp32  */
     SV_ATTN_VALU = 1,  /* vector-ALU kernel, any storage type                      */
-    SV_ATTN_MFMA = 2   /* matrix-core kernel (bf16 and fp8 storage only)           */
+    SV_ATTN_MFMA = 2,  /* matrix-core kernel (bf16 and fp8 storage only)           */
+    /* Flag, OR-ed into one of the above, for measurement only: enqueue just
+     * the main attention kernel.  When the context is split (see
+     * spec_verify_attn_ex) `out` is then NOT written; the unnormalised
+     * partials stay in the workspace. */
+    SV_ATTN_MAIN_ONLY = 0x100
 } sv_attn_algo;
 
 int sv_abi_version(void);

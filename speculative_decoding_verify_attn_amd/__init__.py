@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK = 0
 SV_KV_F32, SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1, 2
 SV_ATTN_AUTO, SV_ATTN_VALU, SV_ATTN_MFMA = 0, 1, 2
+SV_ATTN_MAIN_ONLY = 0x100  # measurement flag: main kernel only (out not written when split)
 BLOCK_SIZE = 16
 
 _lib = None

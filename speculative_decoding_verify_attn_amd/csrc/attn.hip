@@ -44,7 +44,6 @@
 namespace sv {
 namespace {
 
-constexpr int kNW = 4;  // waves per workgroup
 constexpr float kSlack = 8.0f;  // base-2 headroom before the running max is moved
 
 struct UnitWork {
@@ -233,10 +232,6 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 
 // ---------------------------------------------------------------- MFMA kernel
 
-// Swizzled row of head dim `dim` in a transposed V tile: rows are grouped by
-// eight, and inside a group the row index is XORed with the group index.
-__device__ __forceinline__ int vt_row(int dim) { return (dim & ~7) | ((dim & 7) ^ ((dim >> 3) & 7)); }
-
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
@@ -284,7 +279,6 @@ __device__ __forceinline__ uint32_t slot_keep(bool tail, int key, int L)
 {
     return (tail && key >= L) ? 0u : 0xFFFFFFFFu;
 }
-__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 
 // Eight stored values -> four packed bf16 pairs.
 __device__ __forceinline__ uint4 to_bf16x8(uint2 v)
@@ -295,26 +289,39 @@ __device__ __forceinline__ uint4 to_bf16x8(uint2 v)
 }
 
 // Geometry of one 16-token page of one KV head as it travels HBM -> LDS.
+// Every lane reads back from LDS exactly the bytes its own copies wrote, so
+// the only synchronisation a page needs is the wave's own vmcnt wait.
 //   K: lane l = (slot l%16, lane group q4 = l/16) carries the A operand of
 //      S^T = K Q^T for every 32-wide head-dim chunk dc (eight dims per lane).
 //      bf16: one 16-byte copy per chunk; E4M3: one 16-byte copy carries two
 //      chunks (sixteen dims), so the chunk -> dim map is permuted the same way
 //      on the Q side.
-//   V: lane l carries VS consecutive slots x (8 * DG) dims, which the lane
-//      transposes into the [dim][slot] bf16 tile the PV product reads.
+//   V: lane l = (dim group m = l%16, key group q4 = l/16) carries, for each
+//      of the keys 4*q4 .. 4*q4+3, the NDT = D/16 consecutive head dims
+//      NDT*m .. NDT*m+NDT-1.  Row m of PV dim tile t is head dim NDT*m + t,
+//      so the A operand of tile t (four keys of one dim) is gathered from the
+//      lane's own registers with byte permutes: no transpose through LDS.
+//      16 bytes per key and lane (bf16, d=128) travel in one 16-byte copy;
+//      otherwise in 4-byte copies (the LDS copy has no 8-byte form).
+//   E4M3 scales: the page's K and V scales follow as two 4-byte copies in
+//      which every lane fetches the same word, so each lane reads its own
+//      copy back.  (A plain load would make the compiler wait for every
+//      copy in flight before the scale could be used.)
 template <int D, bool FP8>
 struct PageGeom {
     static constexpr int EB = FP8 ? 1 : 2;
-    static constexpr int PT = 16 * D * EB;        // bytes of one tensor's page slice
-    static constexpr int STAGE = 2 * PT;           // K slice, then V slice
-    static constexpr int NDC = D / 32;            // MFMA chunks of the head dim
+    static constexpr int PT = 16 * D * EB;             // bytes of one tensor's page slice
+    static constexpr int SCB = FP8 ? 2 * 256 : 0;      // scale copies (E4M3)
+    static constexpr int STAGE = 2 * PT + SCB;          // K slice, V slice, scales
+    static constexpr int NDC = D / 32;                 // MFMA chunks of the head dim (S)
     static constexpr int NKI = FP8 ? D / 64 : D / 32;  // 16-byte K copies per page
-    // V copies
-    static constexpr int VBYTES = (FP8 && D == 64) ? 4 : 16;  // bytes per lane per copy
-    static constexpr int NVI = PT / (64 * VBYTES);            // copies per page
-    static constexpr int VS = FP8 ? (D == 64 ? 4 : 2) : (D == 128 ? 4 : 2);  // slots per lane
-    static constexpr int DG = FP8 ? (D == 64 ? 0 : 2) : 1;    // 8-dim groups per lane (0: four dims)
-    static constexpr int NI = NKI + NVI;                      // copies per page
+    static constexpr int NDT = D / 16;                 // PV dim tiles = dims per lane and key
+    static constexpr int VKB = NDT * EB;               // V bytes per lane and key: 16, 8 or 4
+    static constexpr int VBYTES = VKB >= 16 ? 16 : 4;  // V copy width
+    static constexpr int VPK = VKB / VBYTES;           // V copies per key
+    static constexpr int NVI = 4 * VPK;                // V copies per page
+    static constexpr int NI = NKI + NVI + (FP8 ? 2 : 0);  // copies per page
+    static_assert(NVI * 64 * VBYTES == PT, "V copies cover the page slice");
     // first head dim of lane group q4 in MFMA chunk dc
     static __device__ __forceinline__ int qdim(int dc, int q4)
     {
@@ -322,34 +329,51 @@ struct PageGeom {
     }
 };
 
-// Merges the kNW waves' tiles of one workgroup and stores the result:
-// normalised output when the unit has a single split, else the unnormalised
-// partial (o, max, sum) for the merge kernel.  tiles: kNW x [RG*16][D+4]
-// floats; sm/sl: per-wave row max (base-2 units) and row sum.
+// Stores a wave's unnormalised O tile (lane: rows rt*16 + l16, head dims
+// NDT*(4*q4 + i) + t) into an LDS tile [RG*16][D+4].
 template <int D, int RG>
-__device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles,
+__device__ __forceinline__ void tile_store(float *tile, const floatx4 (&acc)[D / 16][RG], int l16, int q4)
+{
+    constexpr int OP = D + 4;
+    constexpr int NDT = D / 16;
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t0 = 0; t0 < NDT; t0 += 4)
+                *reinterpret_cast<float4 *>(tile + (rt * 16 + l16) * OP + NDT * (4 * q4 + i) + t0) =
+                    make_float4(acc[t0][rt][i], acc[t0 + 1][rt][i], acc[t0 + 2][rt][i], acc[t0 + 3][rt][i]);
+}
+
+// Merges the NT wave tiles of one workgroup and stores the result:
+// normalised output when the unit has a single split, else the unnormalised
+// partial (o, max, sum) for the merge kernel.  tiles: NT tiles [RG*16][D+4]
+// floats, `pitch` floats apart; sm/sl: per-tile row max (base-2 units) and
+// row sum.
+template <int D, int RG, int NT>
+__device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles, int pitch,
                                                       const float (*sm)[64], const float (*sl)[64],
                                                       int unit, int split, int b, int g, int nsplit)
 {
     constexpr int OP = D + 4;
     constexpr int C4 = D / 4;
-    constexpr int WT = RG * 16 * OP;  // floats per wave tile
     const float ninf = -__builtin_inff();
     const int TG = p.TG, G = p.G;
     const size_t pbase = ((size_t)unit * p.max_splits + split) * TG;
-    for (int idx = threadIdx.x; idx < TG * C4; idx += kAttnThreads) {
+    for (int idx = threadIdx.x; idx < TG * C4; idx += blockDim.x) {
         const int row = idx / C4, c4 = idx - row * C4;
         float M = sm[0][row];
 #pragma unroll
-        for (int v = 1; v < kNW; ++v)
+        for (int v = 1; v < NT; ++v)
             M = fmaxf(M, sm[v][row]);
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         float Ls = 0.0f;
 #pragma unroll
-        for (int v = 0; v < kNW; ++v) {
+        for (int v = 0; v < NT; ++v) {
             const float mv = sm[v][row];
             const float f = (mv == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * WT + row * OP + c4 * 4);
+            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * pitch + row * OP + c4 * 4);
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
             Ls += f * sl[v][row];
         }
@@ -366,27 +390,38 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
     }
 }
 
+// Waves per workgroup of the matrix-core kernel.  (Eight waves with
+// two-stage rings streamed no faster and cost a second merge round.)
+constexpr int kMfmaWaves = 4;
+
 template <int D, int RG, bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnParams p)
 {
     typedef PageGeom<D, FP8> PG;
+    constexpr int NW = kMfmaWaves;
+    constexpr int NT = 64 * NW;          // threads
     constexpr int NDC = PG::NDC;
-    constexpr int NDT = D / 16;          // 16-wide dim tiles of PV
-    constexpr int NS = 4;                // LDS stages per wave (pages in flight + 1)
+    constexpr int NDT = PG::NDT;
+    // Ring stages per wave: about 8 KB of copies in flight behind the page
+    // being computed.  (Deeper rings measured slower: more requests queue at
+    // the memory controllers without raising the stream rate.)
+    constexpr int NS0 = 1 + (8192 + PG::STAGE - 1) / PG::STAGE;
+    constexpr int NS = NS0 > 4 ? 4 : NS0;
     constexpr int EB = PG::EB;
     constexpr int OP = D + 4;
-    constexpr int RING = kNW * NS * PG::STAGE;
-    constexpr int OBUF_BYTES = kNW * RG * 16 * OP * 4;
-    // smem holds, in turn: the waves' page rings, then each wave's
-    // unnormalised output tile.
-    constexpr int SMEM = RING > OBUF_BYTES ? RING : OBUF_BYTES;
+    constexpr int WT = RG * 16 * OP;     // floats of one wave's O tile
+    // Each wave's LDS region holds its page ring, and at the end its O tile.
+    constexpr int RW0 = NS * PG::STAGE > WT * 4 ? NS * PG::STAGE : WT * 4;
+    constexpr int RW = (RW0 + 15) & ~15;
+    constexpr int SMEM = NW * RW;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    __shared__ float s_m[kNW][64], s_l[kNW][64];
+    __shared__ float s_m[NW][64], s_l[NW][64];
     __shared__ int s_pages[kMaxBps];
 
-    // Work item from the block index alone (see decode_work), so that every
-    // load of the prologue below can be in flight at once.
+    // Work item from the block index alone (workgroups go to the eight XCDs
+    // round robin; the remap gives each XCD a contiguous range of units), so
+    // that every load of the prologue below can be in flight at once.
     const int per_xcd = p.grid >> 3;
     const int wg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     const int unit = wg / p.max_splits;
@@ -413,10 +448,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
     int first[NS - 1];
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
-        const int i = wave + k * kNW;
+        const int i = wave + k * NW;
         first[k] = i < avail ? trow[i] : 0;
     }
-    for (int i = tid; i < avail; i += kAttnThreads)
+    for (int i = tid; i < avail; i += NT)
         s_pages[i] = clamp_block(trow[i], p.num_blocks);
     float4 qraw[RG][NDC][2];
 #pragma unroll
@@ -465,10 +500,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
     }
 
     // Running state per row tile: reference maximum m (base-2 units), the
-    // row sums and the unnormalised outputs O^T (lane: dims 4*q4+i of tile
-    // dt, row l16).  bf16 storage gets its row sums from one extra MFMA with
-    // an all-ones A operand; E4M3 storage scales P per page, so it sums P on
-    // the VALU.
+    // row sums and the unnormalised outputs O^T (lane: dims NDT*(4*q4+i)+t of
+    // tile t, row l16).  bf16 storage gets its row sums from one extra MFMA
+    // with an all-ones A operand; E4M3 storage scales P per page, so it sums
+    // P on the VALU.
     float m[RG], lpart[RG];
     floatx4 lsum[RG];
     floatx4 acc[NDT][RG];
@@ -490,27 +525,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
     const int head_off = g * D * EB;
     // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
     const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
-    // V copy: lane -> slot group va (VS slots), dim group vc
-    int vc, va, v_voff;
-    if constexpr (PG::VBYTES == 4) {           // E4M3, d = 64: four dims per lane, four slots
-        vc = lane & 15;
-        va = lane >> 4;
-        v_voff = head_off + (va * 4) * slot_stride + vc * 4;
-    } else if constexpr (FP8) {                 // E4M3, d = 128: sixteen dims, two slots
-        vc = lane & 7;
-        va = lane >> 3;
-        v_voff = head_off + (va * 2) * slot_stride + vc * 16;
-    } else {                                    // bf16: eight dims, VS slots
-        vc = lane % (D / 8);
-        va = lane / (D / 8);
-        v_voff = head_off + (va * PG::VS) * slot_stride + vc * 16;
-    }
+    // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK)
+    const int v_voff = head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
     const uint32_t ring_lds =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * NS * PG::STAGE;
-    unsigned char *ring = smem + wave * NS * PG::STAGE;
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * RW;
+    unsigned char *ring = smem + wave * RW;
+    int4v dks{}, dvs{};
+    if constexpr (FP8) {
+        dks = page_desc(reinterpret_cast<const unsigned char *>(p.k_scale), 0, (uint32_t)p.num_blocks * 4u);
+        dvs = page_desc(reinterpret_cast<const unsigned char *>(p.v_scale), 0, (uint32_t)p.num_blocks * 4u);
+    }
 
-    // This wave's pages are blk_begin + wave + k*kNW, k = 0, 1, ...
-    const int nk = npg > wave ? (npg - wave + kNW - 1) / kNW : 0;
+    // This wave's pages are blk_begin + wave + k*NW, k = 0, 1, ...
+    const int nk = npg > wave ? (npg - wave + NW - 1) / NW : 0;
     auto issue = [&](int k, int ph) {
         const int stage = k % NS;
         const uint32_t lds = ring_lds + stage * PG::STAGE;
@@ -520,8 +547,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         for (int i = 0; i < PG::NKI; ++i)
             dma_to_lds<16>(lds + i * 1024, dk, k_voff, FP8 ? i * 64 : i * 32 * EB);
 #pragma unroll
-        for (int j = 0; j < PG::NVI; ++j)
-            dma_to_lds<PG::VBYTES>(lds + PG::PT + j * 64 * PG::VBYTES, dv, v_voff, j * slot_stride);
+        for (int n = 0; n < PG::NVI; ++n)
+            dma_to_lds<PG::VBYTES>(lds + PG::PT + n * 64 * PG::VBYTES, dv, v_voff,
+                                   (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
+        if constexpr (FP8) {
+            const int soff = __builtin_amdgcn_readfirstlane(ph) * 4;
+            dma_to_lds<4>(lds + 2 * PG::PT, dks, 0, soff);
+            dma_to_lds<4>(lds + 2 * PG::PT + 256, dvs, 0, soff);
+        }
     };
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k)
@@ -531,7 +564,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
 
     for (int k = 0; k < nk; ++k) {
         if (k + NS - 1 < nk)
-            issue(k + NS - 1, s_pages[wave + (k + NS - 1) * kNW]);
+            issue(k + NS - 1, s_pages[wave + (k + NS - 1) * NW]);
         // wait for page k: the copies of up to NS-1 younger pages may stay in flight
         const int younger = (nk - 1 - k) < (NS - 1) ? (nk - 1 - k) : (NS - 1);
         if (younger >= 3)
@@ -542,12 +575,38 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             wait_dma<PG::NI>();
         else
             wait_dma<0>();
-        const int pg = wave + k * kNW;
+        const int pg = wave + k * NW;
         const int key0 = (blk_begin + pg) * kBlock;
-        const int ph = s_pages[pg];
-        unsigned char *st = ring + (k % NS) * PG::STAGE;
+        const unsigned char *st = ring + (k % NS) * PG::STAGE;
 
-        // 1. S^T = K Q^T (keys on M, rows on N); K operands read back from LDS.
+        // 1. Read back this lane's K and V bytes of the page.
+        uint4 kraw[PG::NKI];
+#pragma unroll
+        for (int i = 0; i < PG::NKI; ++i)
+            kraw[i] = *reinterpret_cast<const uint4 *>(st + i * 1024 + lane * 16);
+        uint32_t vr[4][NDT / 2];  // [key j][dims 2w, 2w+1 as bf16]
+        if constexpr (PG::VBYTES == 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
+                vr[j][0] = x.x; vr[j][1] = x.y; vr[j][2] = x.z; vr[j][3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < PG::NVI; ++n) {
+                const uint32_t x = *reinterpret_cast<const uint32_t *>(st + PG::PT + n * 256 + lane * 4);
+                const int j = n / PG::VPK, h = n % PG::VPK;
+                if constexpr (FP8) {
+                    const uint2 y = e4m3x4_to_bf16x4(x);
+                    vr[j][2 * h] = y.x;
+                    vr[j][2 * h + 1] = y.y;
+                } else {
+                    vr[j][h] = x;
+                }
+            }
+        }
+
+        // 2. S^T = K Q^T (keys on M, rows on N).
         floatx4 s[RG];
 #pragma unroll
         for (int rt = 0; rt < RG; ++rt)
@@ -555,9 +614,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < PG::NKI; ++i) {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(st + i * 1024 + lane * 16);
-                const bf16x8 k0 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(raw.x, raw.y)));
-                const bf16x8 k1 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(raw.z, raw.w)));
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(kraw[i].x, kraw[i].y)));
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(kraw[i].z, kraw[i].w)));
 #pragma unroll
                 for (int rt = 0; rt < RG; ++rt) {
                     s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[rt][2 * i], s[rt], 0, 0, 0);
@@ -567,94 +625,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         } else {
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(st + dc * 1024 + lane * 16));
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, kraw[dc]);
 #pragma unroll
                 for (int rt = 0; rt < RG; ++rt)
                     s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][dc], s[rt], 0, 0, 0);
             }
         }
 
-        // 2. V slice -> registers -> transposed, swizzled bf16 tile [dim][slot]
-        //    written over this stage (K has been read).
+        // 3. V operands: slots past the context are cleared, then tile t's
+        //    A operand (dim NDT*l16 + t of keys 4*q4 .. 4*q4+3) is gathered.
         const bool tail = key0 + kBlock > L;
-        if constexpr (PG::VBYTES == 4) {
-            uint32_t raw[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                raw[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + j * 256 + lane * 4);
-            uint2 wv[4];  // slot j: four dims as bf16
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t keep = slot_keep(tail, key0 + 4 * q4 + j, L);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                wv[j] = e4m3x4_to_bf16x4(raw[j]);
-                const uint32_t keep = slot_keep(tail, key0 + va * 4 + j, L);
-                wv[j].x &= keep;
-                wv[j].y &= keep;
-            }
+            for (int w2 = 0; w2 < NDT / 2; ++w2)
+                vr[j][w2] &= keep;
+        }
+        short4v va4[NDT];
 #pragma unroll
-            for (int wd = 0; wd < 2; ++wd) {
-                const int de = vc * 4 + 2 * wd;
-                const uint32_t e0 = (&wv[0].x)[wd], e1 = (&wv[1].x)[wd], e2 = (&wv[2].x)[wd], e3 = (&wv[3].x)[wd];
-                *reinterpret_cast<uint2 *>(st + vt_row(de) * 32 + va * 8) = make_uint2(pack_lo16(e0, e1), pack_lo16(e2, e3));
-                *reinterpret_cast<uint2 *>(st + vt_row(de + 1) * 32 + va * 8) = make_uint2(pack_hi16(e0, e1), pack_hi16(e2, e3));
-            }
-        } else if constexpr (FP8) {
-            uint4 raw[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                raw[j] = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
-            uint4 wv[2][2];  // [slot j][dim group g] bf16
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wv[j][0] = to_bf16x8(make_uint2(raw[j].x, raw[j].y));
-                wv[j][1] = to_bf16x8(make_uint2(raw[j].z, raw[j].w));
-                const uint32_t keep = slot_keep(tail, key0 + va * 2 + j, L);
-                wv[j][0] = and4(wv[j][0], keep);
-                wv[j][1] = and4(wv[j][1], keep);
-            }
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-#pragma unroll
-                for (int wd = 0; wd < 4; ++wd) {
-                    const int de = vc * 16 + g * 8 + 2 * wd;
-                    const uint32_t e0 = (&wv[0][g].x)[wd], e1 = (&wv[1][g].x)[wd];
-                    *reinterpret_cast<uint32_t *>(st + vt_row(de) * 32 + va * 4) = pack_lo16(e0, e1);
-                    *reinterpret_cast<uint32_t *>(st + vt_row(de + 1) * 32 + va * 4) = pack_hi16(e0, e1);
-                }
-        } else {
-            constexpr int VS = PG::VS;
-            uint4 wv[VS];
-#pragma unroll
-            for (int j = 0; j < VS; ++j)
-                wv[j] = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
-#pragma unroll
-            for (int j = 0; j < VS; ++j)
-                wv[j] = and4(wv[j], slot_keep(tail, key0 + va * VS + j, L));
-#pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-                const int de = vc * 8 + 2 * wd;
-                const uint32_t e0 = (&wv[0].x)[wd], e1 = (&wv[1].x)[wd];
-                if constexpr (VS == 4) {
-                    const uint32_t e2 = (&wv[2].x)[wd], e3 = (&wv[3].x)[wd];
-                    *reinterpret_cast<uint2 *>(st + vt_row(de) * 32 + va * 8) =
-                        make_uint2(pack_lo16(e0, e1), pack_lo16(e2, e3));
-                    *reinterpret_cast<uint2 *>(st + vt_row(de + 1) * 32 + va * 8) =
-                        make_uint2(pack_hi16(e0, e1), pack_hi16(e2, e3));
-                } else {
-                    *reinterpret_cast<uint32_t *>(st + vt_row(de) * 32 + va * 4) = pack_lo16(e0, e1);
-                    *reinterpret_cast<uint32_t *>(st + vt_row(de + 1) * 32 + va * 4) = pack_hi16(e0, e1);
-                }
-            }
+        for (int t = 0; t < NDT; ++t) {
+            const int w2 = t >> 1;
+            const uint32_t lo = (t & 1) ? pack_hi16(vr[0][w2], vr[1][w2]) : pack_lo16(vr[0][w2], vr[1][w2]);
+            const uint32_t hi = (t & 1) ? pack_hi16(vr[2][w2], vr[3][w2]) : pack_lo16(vr[2][w2], vr[3][w2]);
+            va4[t] = __builtin_bit_cast(short4v, make_uint2(lo, hi));
         }
 
         float vsc = 1.0f;
         if constexpr (FP8) {
-            const float ksc = p.k_scale[ph];
-            vsc = p.v_scale[ph];
+            const float ksc = *reinterpret_cast<const float *>(st + 2 * PG::PT + lane * 4);
+            vsc = *reinterpret_cast<const float *>(st + 2 * PG::PT + 256 + lane * 4);
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
                 s[rt] *= ksc;
         }
-        // 3. Causal / length mask (only the last pages of a sequence need it).
+        // 4. Causal / length mask (only the last pages of a sequence need it).
         if (key0 + kBlock - 1 > L - T) {
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
@@ -663,7 +668,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
                     if (key0 + q4 * 4 + i > lim[rt])
                         s[rt][i] = ninf;
         }
-        // 4. Online softmax.  The common path only checks that no score of
+        // 5. Online softmax.  The common path only checks that no score of
         //    this lane exceeds its row's reference maximum by more than
         //    kSlack; only then (a wave-uniform, rarely taken branch) are the
         //    row maxima reduced across lanes and the accumulators rescaled.
@@ -705,18 +710,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             pb[rt] = __builtin_bit_cast(short4v, make_uint2(f32x2_to_bf16x2(pr[0] * vsc, pr[1] * vsc),
                                                              f32x2_to_bf16x2(pr[2] * vsc, pr[3] * vsc)));
         }
-        // 5. O^T += V^T P^T over the page's 16 keys: A = V^T (dim l16, slots
-        //    4*q4..+3), B = P^T (slots 4*q4..+3, row l16), exactly the S^T
-        //    output layout.
-        short4v va4[NDT];
+        // 6. O^T += V^T P^T over the page's 16 keys: A = V^T (dim row l16 of
+        //    tile t, keys 4*q4..+3), B = P^T (keys 4*q4..+3, row l16), exactly
+        //    the S^T output layout.
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            va4[dt] = __builtin_bit_cast(short4v, *reinterpret_cast<const uint2 *>(st + vt_row(dt * 16 + l16) * 32 + q4 * 8));
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int t = 0; t < NDT; ++t)
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
-                acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[dt], pb[rt], acc[dt][rt], 0, 0, 0);
+                acc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[t], pb[rt], acc[t][rt], 0, 0, 0);
         if constexpr (!FP8) {
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
@@ -724,11 +725,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
         }
     }
 
-    // ---- epilogue: every wave parks its unnormalised tile and (max, sum)
-    // in LDS; one pass then merges the waves and writes the result.
+    // ---- epilogue: each wave parks its (max, sum) rows and unnormalised
+    // tile in its own LDS region (its ring is idle once its copies have
+    // landed), and after one barrier a single pass merges the waves and
+    // writes the result.
     wait_dma<0>();
-    __syncthreads();  // every wave is done with its ring; smem becomes the tiles
-    float *obuf = reinterpret_cast<float *>(smem) + wave * (RG * 16 * OP);
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
         float ls;
@@ -743,15 +744,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sv_attn_mfma_kernel(AttnParam
             s_m[wave][rt * 16 + l16] = m[rt];
             s_l[wave][rt * 16 + l16] = ls;
         }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const floatx4 a = acc[dt][rt];
-            *reinterpret_cast<float4 *>(obuf + (rt * 16 + l16) * OP + dt * 16 + q4 * 4) =
-                make_float4(a[0], a[1], a[2], a[3]);
-        }
     }
+    tile_store<D, RG>(reinterpret_cast<float *>(ring), acc, l16, q4);
     __syncthreads();
-    merge_waves_and_store<D, RG>(p, reinterpret_cast<const float *>(smem), s_m, s_l, unit, split, b, g, nsplit);
+    merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, unit, split, b,
+                                     g, nsplit);
 }
 
 // ---------------------------------------------------------------- VALU kernel
@@ -881,15 +878,23 @@ hipError_t launch(Kernel k, const AttnParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int D, int RG, bool FP8>
+hipError_t launch_mfma_rg(const AttnParams &p, hipStream_t s)
+{
+    auto kern = sv_attn_mfma_kernel<D, RG, FP8>;
+    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * kMfmaWaves), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int D, bool FP8>
 hipError_t launch_mfma_d(const AttnParams &p, hipStream_t s)
 {
     const int rg = (p.TG + 15) / 16;
     switch (rg) {
-    case 1: return launch(sv_attn_mfma_kernel<D, 1, FP8>, p, s);
-    case 2: return launch(sv_attn_mfma_kernel<D, 2, FP8>, p, s);
-    case 3: return launch(sv_attn_mfma_kernel<D, 3, FP8>, p, s);
-    default: return launch(sv_attn_mfma_kernel<D, 4, FP8>, p, s);
+    case 1: return launch_mfma_rg<D, 1, FP8>(p, s);
+    case 2: return launch_mfma_rg<D, 2, FP8>(p, s);
+    case 3: return launch_mfma_rg<D, 3, FP8>(p, s);
+    default: return launch_mfma_rg<D, 4, FP8>(p, s);
     }
 }
 

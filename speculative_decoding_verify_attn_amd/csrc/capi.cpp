@@ -196,6 +196,8 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
         return fail(SV_ERR_SHAPE, "k_scale / v_scale must be NULL unless kv_dtype is E4M3");
     if (!(std::isfinite(sm_scale)) || sm_scale <= 0.0f)
         return fail(SV_ERR_SHAPE, "sm_scale must be finite and positive");
+    const bool main_only = (algo & SV_ATTN_MAIN_ONLY) != 0;
+    algo &= ~SV_ATTN_MAIN_ONLY;
     if (algo != SV_ATTN_AUTO && algo != SV_ATTN_VALU && algo != SV_ATTN_MFMA)
         return fail(SV_ERR_UNSUPPORTED, "unknown algo %d", algo);
     if (algo == SV_ATTN_MFMA && kv_dtype == SV_KV_F32)
@@ -263,6 +265,8 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
         if (e != hipSuccess)
             return fail(SV_ERR_HIP, "recording main_done_event: %s", hipGetErrorString(e));
     }
+    if (main_only)
+        return ok();
     e = sv::launch_attn_merge(p, s);
     if (e != hipSuccess)
         return fail(SV_ERR_HIP, "split-merge launch: %s", hipGetErrorString(e));

@@ -91,8 +91,8 @@ int spec_verify_workspace_clear(void *workspace, size_t bytes, void *stream);
  * q            [B,T,Hq,d] float32, 16-byte aligned.
  * k_cache      [num_blocks,16,Hkv,d] in kv_dtype, 16-byte aligned (8 for fp8).
  * v_cache      same shape and type as k_cache.
- * k_scale      [num_blocks] float32 per-block scales; required for
- * v_scale        SV_KV_FP8_E4M3, must be NULL otherwise.
+ * k_scale      [num_blocks] float32 per-block scales, positive and finite;
+ * v_scale        required for SV_KV_FP8_E4M3, must be NULL otherwise.
  * block_table  [B,max_blocks_per_seq] int32 physical block ids in
  *              [0,num_blocks); entries at and past ceil(L_b/16) are never read.
  * context_lens [B] int32, T <= L_b <= 16*max_blocks_per_seq.

@@ -634,13 +634,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
 
         // 3. V operands: slots past the context are cleared, then tile t's
         //    A operand (dim NDT*l16 + t of keys 4*q4 .. 4*q4+3) is gathered.
-        const bool tail = key0 + kBlock > L;
+        if (key0 + kBlock > L) {  // wave-uniform: only a sequence's last page
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t keep = slot_keep(tail, key0 + 4 * q4 + j, L);
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t keep = slot_keep(true, key0 + 4 * q4 + j, L);
 #pragma unroll
-            for (int w2 = 0; w2 < NDT / 2; ++w2)
-                vr[j][w2] &= keep;
+                for (int w2 = 0; w2 < NDT / 2; ++w2)
+                    vr[j][w2] &= keep;
+            }
         }
         short4v va4[NDT];
 #pragma unroll
@@ -651,13 +652,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
             va4[t] = __builtin_bit_cast(short4v, make_uint2(lo, hi));
         }
 
-        float vsc = 1.0f;
+        // E4M3 page scales: K's multiplies the scores (folded into the
+        // exponent below; scales are positive, so the maximum of the scaled
+        // scores is the scaled maximum), V's multiplies P.
+        float ksc = 1.0f, vsc = 1.0f;
         if constexpr (FP8) {
-            const float ksc = *reinterpret_cast<const float *>(st + 2 * PG::PT + lane * 4);
+            ksc = *reinterpret_cast<const float *>(st + 2 * PG::PT + lane * 4);
             vsc = *reinterpret_cast<const float *>(st + 2 * PG::PT + 256 + lane * 4);
-#pragma unroll
-            for (int rt = 0; rt < RG; ++rt)
-                s[rt] *= ksc;
         }
         // 4. Causal / length mask (only the last pages of a sequence need it).
         if (key0 + kBlock - 1 > L - T) {
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
         bool need = false;
 #pragma unroll
         for (int rt = 0; rt < RG; ++rt) {
-            mloc[rt] = fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
+            mloc[rt] = ksc * fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
             need = need || (mloc[rt] > m[rt] + kSlack);
         }
         if (__builtin_expect(__ballot(need) != 0, 0)) {
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                pr[i] = __builtin_amdgcn_exp2f(s[rt][i] - msafe);
+                pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], ksc, -msafe));
             if constexpr (FP8)
                 lpart[rt] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
             pb[rt] = __builtin_bit_cast(short4v, make_uint2(f32x2_to_bf16x2(pr[0] * vsc, pr[1] * vsc),

@@ -4,7 +4,7 @@
 // (quad_perm, row_shr, row_mirror, row_half_mirror) and the GFX9 row
 // broadcasts (row_bcast:15, row_bcast:31) to cross rows; the final value is
 // read from lane 63 with v_readlane.  64-bit values move as two 32-bit
-// halves.  fp8 E4M3 decode uses the hardware fp8 -> fp32 conversion.
+// halves.  fp8 E4M3 decode uses the hardware fp8 -> bf16 conversion.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -152,21 +152,16 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Four OCP E4M3 codes (one dword) -> four bf16 (two dwords), exact: the
-// hardware converts each byte to fp32 (v_cvt_f32_fp8 with a byte select),
-// and every E4M3 value has at most four significant bits, so the upper half
-// of the fp32 is the value in bf16.  One conversion per byte: hipcc's
-// extraction of the second lane of the packed two-byte conversion
-// (cvt_pk_f32_fp8) returned the first lane, so that form is not used.
+// Four OCP E4M3 codes (bytes 0..3 of `codes`) -> four bf16 values as two
+// packed pairs {byte 0, byte 1}, {byte 2, byte 3}.  gfx950's packed
+// conversion with a unit scale is exact (every E4M3 value is a bf16 value);
+// its scale operand contributes only its exponent, so per-page scales are
+// applied separately.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t codes)
 {
-    const uint32_t f0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8((int)codes, 0));
-    const uint32_t f1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8((int)codes, 1));
-    const uint32_t f2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8((int)codes, 2));
-    const uint32_t f3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8((int)codes, 3));
     uint2 r;
-    r.x = pack_hi16(f0, f1);
-    r.y = pack_hi16(f2, f3);
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
     return r;
 }
 

@@ -42,6 +42,14 @@ def _bind(lib):
     lib.oracle_sample.restype = c.c_int
     lib.oracle_sample.argtypes = (
         [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_encode_bf16.restype = c.c_uint16
+    lib.oracle_encode_bf16.argtypes = [c.c_float]
+    lib.oracle_encode_e4m3.restype = c.c_uint8
+    lib.oracle_encode_e4m3.argtypes = [c.c_float, c.c_float]
+    lib.oracle_kv_append.restype = c.c_int
+    lib.oracle_kv_append.argtypes = [c.c_void_p] * 8 + [c.c_int] * 7
+    lib.oracle_rollback.restype = None
+    lib.oracle_rollback.argtypes = [c.c_void_p] * 3 + [c.c_int] * 2
     return lib
 
 
@@ -177,3 +185,50 @@ def kv_cache_bytes(ctx_len, n_layers, n_kv_heads, head_dim, bytes_per_elem, batc
     Inference" 3.3; "Speculative decoding and KV cache optimisation" 3.1).
     The query-head count never enters."""
     return 2 * ctx_len * n_layers * n_kv_heads * head_dim * bytes_per_elem * batch
+
+
+def encode_bf16(x):
+    """float32 array -> bfloat16 bit patterns (uint16), element by element."""
+    L = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    return np.array([L.oracle_encode_bf16(float(v)) for v in x], dtype=np.uint16)
+
+
+def encode_e4m3(x, scale):
+    """float32 arrays x, scale (broadcast) -> E4M3 codes of x / scale (uint8)."""
+    L = _load()
+    x, scale = np.broadcast_arrays(np.asarray(x, dtype=np.float32), np.asarray(scale, dtype=np.float32))
+    return np.array([L.oracle_encode_e4m3(float(a), float(s)) for a, s in zip(x.ravel(), scale.ravel())],
+                    dtype=np.uint8).reshape(x.shape)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens, kv_dtype, k_scale=None, v_scale=None):
+    """Writes the T new positions into copies of the caches and returns them
+    (k_cache, v_cache).  k_new/v_new [B,T,Hkv,d] float32; caches as stored
+    (float32, uint16 bf16 bits or uint8 E4M3 codes) [num_blocks,16,Hkv,d]."""
+    L = _load()
+    k_new = np.ascontiguousarray(k_new, dtype=np.float32)
+    v_new = np.ascontiguousarray(v_new, dtype=np.float32)
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, T, Hkv, d = k_new.shape
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = None if v_scale is None else np.ascontiguousarray(v_scale, dtype=np.float32)
+    p = lambda a: None if a is None else a.ctypes.data
+    rc = L.oracle_kv_append(p(k_new), p(v_new), p(kc), p(vc), p(ks), p(vs), p(table), p(lens),
+                            B, T, Hkv, d, table.shape[1], kc.shape[0], kv_dtype)
+    if rc != 0:
+        raise ValueError("oracle_kv_append: position or page id out of range")
+    return kc, vc
+
+
+def rollback(num_accepted, context_lens, K):
+    """Returns (new context_lens, pages_in_use) after keeping the accepted drafts."""
+    L = _load()
+    n = np.ascontiguousarray(num_accepted, dtype=np.int32)
+    lens = np.array(context_lens, dtype=np.int32, copy=True)
+    pages = np.zeros_like(lens)
+    L.oracle_rollback(n.ctypes.data, lens.ctypes.data, pages.ctypes.data, len(lens), K)
+    return lens, pages

@@ -428,3 +428,107 @@ int oracle_sample(const float *target_logits, const float *draft_probs,
     }
     return rc;
 }
+
+/* ------------------------------------------------------- paged append / rollback
+ *
+ * Appending the verify positions to the paged cache and truncating it after
+ * the sampler ([KV] 6.1 naive append, 6.2 paged data structure, 7.6 the loop
+ * and its note that a paged cache rolls back by changing table entries;
+ * [L10] 9.2).
+ */
+
+/* float -> bfloat16 bits, round to nearest, ties to even, from the format
+ * definition: the 16 dropped fraction bits decide; NaN stays NaN (quiet). */
+uint16_t oracle_encode_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep = u >> 16, drop = u & 0xFFFFu;
+    if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u)))
+        keep += 1u;
+    return (uint16_t)keep;
+}
+
+/* float -> OCP E4M3 ("fn") code for the value x / scale.  The quotient is
+ * rounded to float first (as a float division does), then mapped to the
+ * nearest E4M3 value by direct search over the 127 non-negative finite codes;
+ * a tie goes to the code with an even last fraction bit.  Magnitudes above
+ * 448 (infinity included) saturate to 448; NaN maps to the NaN code. */
+uint8_t oracle_encode_e4m3(float x, float scale)
+{
+    float qf = x / scale;
+    if (isnan(qf))
+        return 0x7F;
+    uint8_t sign = signbit(qf) ? 0x80 : 0x00;
+    double a = fabs((double)qf);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    int best = 0;
+    double bestd = a;   /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(oracle_decode_e4m3((uint8_t)c) - a);
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* k_new, v_new [B][T][Hkv][d] float; caches [num_blocks][16][Hkv][d] of
+ * kv_dtype, written in place.  For every (b, t, g): position
+ * p = L_b - T + t, page = block_table[b][p / 16], slot = p % 16.  Returns -1
+ * (writing nothing) if any position or page id is out of range. */
+int oracle_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
+                     const float *k_scale, const float *v_scale, const int32_t *block_table,
+                     const int32_t *context_lens, int B, int T, int Hkv, int d, int max_blocks,
+                     int num_blocks, int kv_dtype)
+{
+    for (int b = 0; b < B; ++b) {
+        if (context_lens[b] < T || context_lens[b] > max_blocks * 16)
+            return -1;
+        for (int t = 0; t < T; ++t) {
+            int p = context_lens[b] - T + t;
+            int page = block_table[(int64_t)b * max_blocks + p / 16];
+            if (page < 0 || page >= num_blocks)
+                return -1;
+        }
+    }
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < T; ++t) {
+            int p = context_lens[b] - T + t;
+            int64_t page = block_table[(int64_t)b * max_blocks + p / 16];
+            int slot = p % 16;
+            for (int g = 0; g < Hkv; ++g)
+                for (int c = 0; c < d; ++c) {
+                    int64_t src = (((int64_t)b * T + t) * Hkv + g) * d + c;
+                    int64_t dst = ((page * 16 + slot) * Hkv + g) * d + c;
+                    for (int which = 0; which < 2; ++which) {
+                        const float x = which ? v_new[src] : k_new[src];
+                        void *cache = which ? v_cache : k_cache;
+                        if (kv_dtype == OR_KV_F32)
+                            ((float *)cache)[dst] = x;
+                        else if (kv_dtype == OR_KV_BF16)
+                            ((uint16_t *)cache)[dst] = oracle_encode_bf16(x);
+                        else
+                            ((uint8_t *)cache)[dst] =
+                                oracle_encode_e4m3(x, which ? v_scale[page] : k_scale[page]);
+                    }
+                }
+        }
+    return 0;
+}
+
+/* After the sampler: keep the last committed token and the n_b accepted
+ * drafts of the T = K + 1 verify positions, i.e. L_b <- L_b - K + n_b, and
+ * report the pages the shorter context still uses, ceil(L_b / 16). */
+void oracle_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K)
+{
+    for (int b = 0; b < B; ++b) {
+        int L = context_lens[b] - K + num_accepted[b];
+        context_lens[b] = L;
+        pages_in_use[b] = (L + 15) / 16;
+    }
+}

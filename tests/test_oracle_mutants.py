@@ -12,6 +12,7 @@ import pytest
 import oracle
 from . import test_oracle_attention as TA
 from . import test_oracle_sampler as TS
+from . import test_oracle_kvcache as TK
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -29,6 +30,16 @@ SAMPLE_PINS = [
     TS.test_residual_mass_identity_on_config_rows, TS.test_accept_ratio_matches_library_softmax,
     TS.test_draft_equal_to_target_accepts_all_and_draws_bonus,
     lambda: TS.test_mean_tokens_per_round_closed_form(4, 0.6),
+]
+
+KV_PINS = [
+    TK.test_bf16_encoder_matches_library_cast, TK.test_e4m3_encoder_matches_library_cast_within_range,
+    TK.test_e4m3_encoder_round_trips_every_finite_code_and_saturates, TK.test_e4m3_encoder_divides_by_the_scale_in_float,
+    lambda: TK.test_append_writes_exactly_the_new_positions("f32"),
+    lambda: TK.test_append_writes_exactly_the_new_positions("bf16"),
+    lambda: TK.test_append_writes_exactly_the_new_positions("fp8"),
+    TK.test_append_then_attention_equals_attention_on_the_full_cache,
+    TK.test_rollback_keeps_the_loop_invariant, TK.test_rollback_extremes,
 ]
 
 # (name, original text, replacement, pins expected to catch it)
@@ -56,6 +67,14 @@ MUTANTS = [
      "        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
      "        oracle_softmax_row(lrow - V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
      SAMPLE_PINS),
+    ("bf16 ties away from zero", "if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u)))", "if (drop >= 0x8000u)", KV_PINS),
+    ("e4m3 ties to odd", "if (d < bestd || (d == bestd && (c & 1) == 0)) {", "if (d < bestd || (d == bestd && (c & 1) == 1)) {", KV_PINS),
+    ("e4m3 overflow to NaN", "    if (a >= 448.0)\n        return (uint8_t)(sign | 0x7E);", "    if (a > 464.0)\n        return (uint8_t)(sign | 0x7F);", KV_PINS),
+    ("e4m3 scale multiplied", "float qf = x / scale;", "float qf = x * scale;", KV_PINS),
+    ("append slot shifted", "int slot = p % 16;", "int slot = (p + 1) % 16;", KV_PINS),
+    ("append K and V swapped", "const float x = which ? v_new[src] : k_new[src];", "const float x = which ? k_new[src] : v_new[src];", KV_PINS),
+    ("rollback drops one more", "int L = context_lens[b] - K + num_accepted[b];", "int L = context_lens[b] - K - 1 + num_accepted[b];", KV_PINS),
+    ("pages in use rounded down", "pages_in_use[b] = (L + 15) / 16;", "pages_in_use[b] = L / 16;", KV_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

@@ -48,7 +48,8 @@ CONFIGS = {
                 V=128256, target_sigma=3.0, noise=1.0),
 }
 
-_STREAMS = ("perm", "ctx", "q", "k", "v", "logits", "noise", "noise_scale", "draft_draw", "uniforms")
+_STREAMS = ("perm", "ctx", "q", "k", "v", "logits", "noise", "noise_scale", "draft_draw", "uniforms",
+            "append", "accepted")
 
 
 def streams(seed: int):
@@ -326,3 +327,67 @@ def sample_algorithmic_bytes(s: SampleInputs, n_rejected: int) -> int:
     rejected sequence, plus tokens, uniforms and outputs."""
     B, K, V = s.B, s.K, s.V
     return 4 * V * B * (K + 1) + 4 * V * int(n_rejected) + 4 * B * K * 2 + 4 * B * (K + 1) * 2 + 4 * B
+
+
+# ------------------------------------------------------------------ paged append
+
+@dataclass
+class AppendInputs:
+    cache: AttnInputs          # caches, table and lengths (lengths include the T new positions)
+    k_new: np.ndarray          # [B,T,Hkv,d] float32
+    v_new: np.ndarray
+    num_accepted: np.ndarray   # [B] int32 in [0, T-1], for the rollback that follows
+
+
+def make_append(seed, B, T, Hkv, d, lens, kv="bf16", extremes=False, extra_blocks=0):
+    """Inputs for appending the T verify positions of every sequence: a paged
+    cache whose last T positions per sequence are NaN-poisoned (the old
+    contents the append must overwrite), fresh float32 K/V for those
+    positions, and accepted counts for the rollback.  E4M3 values are drawn at
+    the scale of their destination page (about 1% of them beyond +-448 times
+    the scale, so saturation is exercised); `extremes` plants +-inf, NaN,
+    zero, denormals and huge values."""
+    a = make_attn_from_lens(seed, B, T, Hkv, Hkv, d, lens, kv=kv, poison=True, extra_blocks=extra_blocks)
+    st = streams(seed)
+    lens = a.context_lens.astype(np.int64)
+    # poison the positions about to be written
+    for b in range(B):
+        for t in range(T):
+            pos = int(lens[b]) - T + t
+            page, slot = a.block_table[b, pos // BLOCK], pos % BLOCK
+            for c in (a.k_cache, a.v_cache):
+                if a.kv_dtype == KV_F32:
+                    c[page, slot] = np.nan
+                elif a.kv_dtype == KV_BF16:
+                    c[page, slot] = BF16_NAN
+                else:
+                    c[page, slot] = E4M3_NAN
+    rng = st["append"]
+    k_new = rng.standard_normal((B, T, Hkv, d), dtype=np.float32)
+    v_new = rng.standard_normal((B, T, Hkv, d), dtype=np.float32)
+    if a.kv_dtype == KV_FP8_E4M3:
+        for b in range(B):
+            for t in range(T):
+                pos = int(lens[b]) - T + t
+                page = a.block_table[b, pos // BLOCK]
+                k_new[b, t] *= np.float32(a.k_scale[page] * 130.0)
+                v_new[b, t] *= np.float32(a.v_scale[page] * 130.0)
+    if extremes:
+        flat_k, flat_v = k_new.reshape(-1), v_new.reshape(-1)
+        specials = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, 1e-40, -3e-39, 3e38, -1e30, 65504.0],
+                            dtype=np.float32)
+        idx = rng.choice(flat_k.size, size=min(flat_k.size, 4 * len(specials)), replace=False)
+        flat_k[idx] = np.resize(specials, len(idx))
+        flat_v[idx[::-1]] = np.resize(specials, len(idx))
+    n = st["accepted"].integers(0, T, size=B).astype(np.int32)
+    return AppendInputs(cache=a, k_new=k_new, v_new=v_new, num_accepted=n)
+
+
+def append_algorithmic_bytes(ap: AppendInputs) -> int:
+    """fp32 K/V in, stored K/V out, the table entries and lengths read (+ page
+    scales for E4M3)."""
+    a = ap.cache
+    elems = ap.k_new.size
+    out_b = {KV_F32: 4, KV_BF16: 2, KV_FP8_E4M3: 1}[a.kv_dtype]
+    extra = 8 * a.B * ap.k_new.shape[1] if a.kv_dtype == KV_FP8_E4M3 else 0
+    return 2 * elems * (4 + out_b) + 4 * a.B * ap.k_new.shape[1] + 4 * a.B + extra

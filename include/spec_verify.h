@@ -6,6 +6,9 @@
  * scoring K+1 positions against its paged KV cache) followed by one
  * spec_verify_sample call on the target logits (the rejection sampler that
  * decides how many of the K draft tokens survive and draws one more token).
+ * Around it, spec_verify_kv_append writes the K+1 positions' K/V into the
+ * cache (per layer, before the attention) and spec_verify_rollback drops the
+ * rejected drafts' positions afterwards.
  *
  * Conventions shared by every call:
  *   - Tensor pointers are DEVICE pointers, row-major, dense, owned by the
@@ -171,6 +174,54 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs,
                        int32_t *num_accepted, int32_t *out_tokens, float *accept_prob,
                        int B, int K, int V,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_kv_append: write the K/V of the T verify positions into the
+ * paged cache, before spec_verify_attn.
+ *
+ * Defines ("KV Cache + Speculative Decoding" 6.1 append, 6.2 paged data
+ * structure; "Lecture 10 - Inference" 9.2): for sequence b, verify position
+ * t in [0,T) and KV head g, with L_b = context_lens[b] (which, as for
+ * spec_verify_attn, already counts the T new positions):
+ *   p = L_b - T + t,  page = block_table[b][p/16],  slot = p % 16
+ *   k_cache[page][slot][g][:] = enc(k_new[b][t][g][:]);  v likewise.
+ * enc: SV_KV_F32 stores the float; SV_KV_BF16 rounds to nearest, ties to
+ * even (NaN stays NaN); SV_KV_FP8_E4M3 stores the OCP E4M3 code of
+ * x / scale[page] (the quotient rounded to float, then to nearest E4M3 with
+ * ties to even; magnitudes above 448, infinities included, saturate to
+ * +-448; NaN gives the NaN code 0x7F).  The page scales belong to the
+ * caller: they are read, never written.  No other byte of the caches is
+ * touched.
+ *
+ * k_new, v_new [B,T,Hkv,d] float32, 16-byte aligned; k_cache/v_cache as for
+ * spec_verify_attn, aligned to 16 (fp32), 8 (bf16) or 4 (E4M3) bytes.
+ * k_scale, v_scale: [num_blocks] float32, positive and finite, required for
+ * SV_KV_FP8_E4M3, NULL otherwise.  1 <= T <= 16; d % 4 == 0; block_size ==
+ * 16.  The pages the new positions fall in must already be in the table
+ * (allocation is the caller's).  Device-data preconditions: T <= L_b <=
+ * 16*max_blocks_per_seq, page ids in [0,num_blocks).
+ * ------------------------------------------------------------------------ */
+int spec_verify_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
+                          const float *k_scale, const float *v_scale, const int32_t *block_table,
+                          const int32_t *context_lens, int B, int T, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int kv_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_rollback: truncate the cache after the sampler, in O(1) per
+ * sequence ("KV Cache + Speculative Decoding" 7.6: keep the last committed
+ * token and the accepted drafts; the drawn token enters the cache in the
+ * next round; a paged cache rolls back by changing its table, not its data).
+ *
+ *   context_lens[b] <- context_lens[b] - K + num_accepted[b]
+ *   pages_in_use[b]  = ceil(context_lens[b] / 16)      (optional, NULL to skip)
+ * Table entries from pages_in_use[b] on no longer hold live positions; the
+ * caller may return them to its page pool.  num_accepted[b] is clamped to
+ * [0,K]; context_lens must count the T = K+1 verify positions on entry.
+ * num_accepted [B] int32 (as written by spec_verify_sample); context_lens [B]
+ * int32, updated in place; pages_in_use [B] int32.  1 <= K <= 15.
+ * ------------------------------------------------------------------------ */
+int spec_verify_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
+                         void *stream);
 
 #ifdef __cplusplus
 }

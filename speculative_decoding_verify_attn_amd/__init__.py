@@ -6,8 +6,10 @@ There is no fallback: if the library is missing or a call fails, this module
 raises.
 
 Calls (same names as the C ABI in include/spec_verify.h):
-    spec_verify_attn(...)    paged GQA attention for the K+1 verify rows
-    spec_verify_sample(...)  the accept / residual / bonus rejection sampler
+    spec_verify_kv_append(...)  write the K+1 verify positions' K/V into the paged cache
+    spec_verify_attn(...)       paged GQA attention for the K+1 verify rows
+    spec_verify_sample(...)     the accept / residual / bonus rejection sampler
+    spec_verify_rollback(...)   drop the rejected drafts' positions (context_lens in place)
 """
 import ctypes
 import os
@@ -63,6 +65,10 @@ def lib():
         L.spec_verify_sample_workspace_size.argtypes = [I] * 3
         L.spec_verify_sample.restype = I
         L.spec_verify_sample.argtypes = [P] * 7 + [I] * 3 + [P, S, P]
+        L.spec_verify_kv_append.restype = I
+        L.spec_verify_kv_append.argtypes = [P] * 8 + [I] * 8 + [P]
+        L.spec_verify_rollback.restype = I
+        L.spec_verify_rollback.argtypes = [P] * 3 + [I] * 2 + [P]
         if L.sv_abi_version() != 1:
             raise ImportError("libspecverify ABI version mismatch")
         _lib = L
@@ -161,3 +167,27 @@ def spec_verify_sample(target_logits, draft_probs, draft_tokens, uniforms, num_a
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, target_logits.device)))
     return num_accepted, out_tokens
+
+
+def spec_verify_kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens, *,
+                          k_scale=None, v_scale=None, kv_dtype=None, stream=None):
+    """Writes k_new/v_new [B,T,Hkv,d] float32 into the paged caches at
+    positions context_lens[b] - T + t (see include/spec_verify.h)."""
+    B, T, Hkv, d = k_new.shape
+    num_blocks, bs = k_cache.shape[0], k_cache.shape[1]
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    _check("spec_verify_kv_append", lib().spec_verify_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), B, T, Hkv, d, bs, block_table.shape[1], num_blocks, kv_dtype,
+        _stream_handle(stream, k_new.device)))
+    return k_cache, v_cache
+
+
+def spec_verify_rollback(num_accepted, context_lens, K, pages_in_use=None, stream=None):
+    """context_lens[b] <- context_lens[b] - K + num_accepted[b], in place;
+    pages_in_use[b] = ceil(context_lens[b] / 16) if given."""
+    _check("spec_verify_rollback", lib().spec_verify_rollback(
+        _ptr(num_accepted), _ptr(context_lens), _ptr(pages_in_use), context_lens.shape[0], int(K),
+        _stream_handle(stream, context_lens.device)))
+    return context_lens, pages_in_use

@@ -342,4 +342,74 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
     return ok();
 }
 
+int spec_verify_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
+                          const float *k_scale, const float *v_scale, const int32_t *block_table,
+                          const int32_t *context_lens, int B, int T, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int kv_dtype, void *stream)
+{
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !context_lens)
+        return fail(SV_ERR_NULL, "k_new, v_new, k_cache, v_cache, block_table and context_lens must be non-NULL");
+    if (B < 1 || T < 1 || T > 16 || Hkv < 1 || d < 4 || d % 4 != 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return fail(SV_ERR_SHAPE, "need B >= 1, 1 <= T <= 16, Hkv >= 1, d a positive multiple of 4, "
+                                  "max_blocks_per_seq >= 1, num_blocks >= 1 (got %d, %d, %d, %d, %d, %d)",
+                    B, T, Hkv, d, max_blocks_per_seq, num_blocks);
+    if (block_size != sv::kBlock)
+        return fail(SV_ERR_UNSUPPORTED, "block_size must be %d (got %d)", sv::kBlock, block_size);
+    if (kv_dtype != SV_KV_F32 && kv_dtype != SV_KV_BF16 && kv_dtype != SV_KV_FP8_E4M3)
+        return fail(SV_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+    const bool fp8 = kv_dtype == SV_KV_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale))
+        return fail(SV_ERR_NULL, "k_scale and v_scale are required for SV_KV_FP8_E4M3");
+    if (!fp8 && (k_scale || v_scale))
+        return fail(SV_ERR_SHAPE, "k_scale and v_scale must be NULL unless kv_dtype is SV_KV_FP8_E4M3");
+    if ((long long)max_blocks_per_seq * sv::kBlock > 0x7FFFFFFFLL ||
+        (long long)B * max_blocks_per_seq > 0x7FFFFFFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "max_blocks_per_seq too large");
+    const size_t cache_align = kv_dtype == SV_KV_F32 ? 16 : (kv_dtype == SV_KV_BF16 ? 8 : 4);
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return fail(SV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
+    if (!aligned(k_cache, cache_align) || !aligned(v_cache, cache_align))
+        return fail(SV_ERR_ALIGN, "k_cache and v_cache must be %zu-byte aligned", cache_align);
+    if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+        return fail(SV_ERR_ALIGN, "block_table, context_lens and the scales must be 4-byte aligned");
+    const long long threads = (long long)B * T * Hkv * (d / 4);
+    if ((threads + 255) / 256 > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "B*T*Hkv*d too large");
+    sv::AppendParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.B = B;
+    p.T = T;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    const hipError_t e = sv::launch_kv_append(p, kv_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_verify_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
+                         void *stream)
+{
+    if (!num_accepted || !context_lens)
+        return fail(SV_ERR_NULL, "num_accepted and context_lens must be non-NULL");
+    if (B < 1 || K < 1 || K > 15)
+        return fail(SV_ERR_SHAPE, "need B >= 1 and 1 <= K <= 15 (got %d, %d)", B, K);
+    if (!aligned(num_accepted, 4) || !aligned(context_lens, 4) || (pages_in_use && !aligned(pages_in_use, 4)))
+        return fail(SV_ERR_ALIGN, "rollback arrays must be 4-byte aligned");
+    const hipError_t e = sv::launch_rollback(num_accepted, context_lens, pages_in_use, B, K,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "rollback launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

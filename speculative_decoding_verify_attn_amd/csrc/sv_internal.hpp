@@ -78,4 +78,21 @@ SamplePlan plan_sample(int B, int K, int V);
 hipError_t launch_sample(const SampleParams &p, hipStream_t stream);
 hipError_t launch_clear(void *ptr, size_t bytes, hipStream_t stream);
 
+// Appending the T verify positions to the paged cache.
+struct AppendParams {
+    const float *k_new;            // [B][T][Hkv][d]
+    const float *v_new;
+    void *k_cache;                 // [num_blocks][16][Hkv][d] of the storage type
+    void *v_cache;
+    const float *k_scale;          // [num_blocks] (E4M3 only)
+    const float *v_scale;
+    const int32_t *block_table;    // [B][max_blocks]
+    const int32_t *context_lens;   // [B], including the T new positions
+    int B, T, Hkv, d, max_blocks, num_blocks;
+};
+
+hipError_t launch_kv_append(const AppendParams &p, int kv_dtype, hipStream_t stream);
+hipError_t launch_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
+                           hipStream_t stream);
+
 }  // namespace sv

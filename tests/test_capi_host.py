@@ -99,3 +99,30 @@ def test_workspace_queries():
     assert sv.lib().spec_verify_attn_workspace_size(8, 6, 30, 8, 128, 256) == 0
     assert sv.sample_workspace_size(8, 5, 128256) >= 8 * 6 * 16 * 16
     assert sv.lib().spec_verify_sample_workspace_size(8, 0, 10) == 0
+
+
+def test_append_and_rollback_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = (ctypes.addressof(buf) + 255) & ~255
+    ok = dict(B=2, T=6, Hkv=8, d=128, bs=16, mb=8, nb=32, kv=1)
+
+    def app(kn=p, vn=p, kc=p, vc=p, ks=None, vs=None, tb=p, cl=p, **over):
+        a = dict(ok, **over)
+        return L.spec_verify_kv_append(kn, vn, kc, vc, ks, vs, tb, cl, a["B"], a["T"], a["Hkv"], a["d"], a["bs"],
+                                       a["mb"], a["nb"], a["kv"], None)
+
+    assert app(kn=None) == 1
+    assert app(T=17) == 2
+    assert app(T=0) == 2
+    assert app(d=130) == 2
+    assert app(bs=32) == 3
+    assert app(kv=7) == 3
+    assert app(kv=2) == 1                       # E4M3 without scales
+    assert app(ks=p, vs=p) == 2                 # scales given for bf16
+    assert app(kn=p + 4) == 5
+    assert app(kc=p + 2) == 5                   # bf16 cache must be 8-byte aligned
+    assert L.spec_verify_rollback(None, p, None, 2, 5, None) == 1
+    assert L.spec_verify_rollback(p, p, None, 2, 16, None) == 2
+    assert L.spec_verify_rollback(p, p, None, 0, 5, None) == 2
+    assert L.spec_verify_rollback(p, p + 2, None, 2, 5, None) == 5

@@ -266,6 +266,37 @@ def main():
         del graphs
         print("# graph pass: %.1f us/step" % (graph_ms_step * 1e3), file=sys.stderr, flush=True)
     ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
+
+    # The paged-cache steps on either side of the verify step (reported beside
+    # it): appending the T verify positions of one layer, and the rollback.
+    def timed_launches(fn, n):
+        e0, e1 = hev.create(), hev.create()
+        torch.cuda.synchronize()
+        gate(n)
+        hev.record(e0, sh)
+        for i in range(n):
+            fn(i)
+        hev.record(e1, sh)
+        torch.cuda.synchronize()
+        return hev.ms(e0, e1) / n
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    k_new = torch.randn((a.B, a.T, a.Hkv, a.d), generator=gen, device=dev)
+    v_new = torch.randn((a.B, a.T, a.Hkv, a.d), generator=gen, device=dev)
+    if a.kv_dtype == W.KV_FP8_E4M3:
+        k_new *= 4.0
+        v_new *= 4.0
+    st0 = sets[0]
+    append_ms = timed_launches(lambda i: sv.spec_verify_kv_append(
+        k_new, v_new, st0["k"], st0["v"], st0["table"], st0["lens"], k_scale=st0.get("ks"), v_scale=st0.get("vs"),
+        kv_dtype=a.kv_dtype, stream=stream), args.steps)
+    lens_scratch = st0["lens"].clone()
+    pages_scratch = torch.empty_like(lens_scratch)
+    rollback_ms = timed_launches(lambda i: sv.spec_verify_rollback(n_acc, lens_scratch, s.K, pages_in_use=pages_scratch,
+                                                                   stream=stream), args.steps)
+    ap_bytes = 2 * k_new.numel() * (4 + {W.KV_F32: 4, W.KV_BF16: 2, W.KV_FP8_E4M3: 1}[a.kv_dtype]) + 4 * a.B * (a.T + 1)
+    print("# append %.1f us, rollback %.1f us" % (append_ms * 1e3, rollback_ms * 1e3), file=sys.stderr, flush=True)
     hev.close()
     n_rej = int((n_acc.cpu().numpy() < s.K).sum())
     samp_bytes = W.sample_algorithmic_bytes(s, n_rej)
@@ -305,6 +336,9 @@ def main():
         "attn_us": float(attn_ms.mean() * 1e3),
         "attn_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
         "sample_us": float(samp_ms.mean() * 1e3),
+        "kv_append_us_per_layer": float(append_ms * 1e3),
+        "kv_append_bytes_per_layer": int(ap_bytes),
+        "rollback_us": float(rollback_ms * 1e3),
         "attn_bytes": attn_bytes,
         "sample_bytes": samp_bytes,
         "step_gbs": (attn_bytes + samp_bytes) / (ms_step * 1e-3) / 1e9,

@@ -54,19 +54,27 @@ struct UnitWork {
     int nsplit;     // splits of this sequence
 };
 
-// Workgroup -> (unit, split).  Workgroups are handed to the eight XCDs round
-// robin; the remap gives each XCD a contiguous range of units, so the splits
-// of one unit (and their partials) stay within one XCD's L2.
+// Workgroup -> (unit, split).  Workgroups are handed to the eight dies
+// (XCDs) round robin, block id mod 8.  Die x takes units x, x+8, x+16, ...
+// with all their splits: with 8 KV heads that is head x of every sequence, so
+// each die gets the same share of work however ragged the context lengths
+// are (a die cannot take over another die's work).  The grid holds
+// 8 * ceil(units / 8) * max_splits workgroups.
+__device__ __forceinline__ void work_item(const AttnParams &p, int &unit, int &split)
+{
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    unit = (j / p.max_splits) * 8 + x;
+    split = j - (j / p.max_splits) * p.max_splits;
+}
+
 __device__ __forceinline__ bool decode_work(const AttnParams &p, UnitWork &w)
 {
-    const int bid = blockIdx.x;
-    const int per_xcd = p.grid >> 3;
-    const int wg = (bid & 7) * per_xcd + (bid >> 3);
-    const int unit = wg / p.max_splits;
+    int unit, split;
+    work_item(p, unit, split);
     if (unit >= p.B * p.Hkv)
         return false;
     w.unit = unit;
-    w.split = wg - unit * p.max_splits;
+    w.split = split;
     w.b = unit / p.Hkv;
     w.g = unit - w.b * p.Hkv;
     int L = p.context_lens[w.b];
@@ -419,15 +427,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
     __shared__ float s_m[NW][64], s_l[NW][64];
     __shared__ int s_pages[kMaxBps];
 
-    // Work item from the block index alone (workgroups go to the eight XCDs
-    // round robin; the remap gives each XCD a contiguous range of units), so
-    // that every load of the prologue below can be in flight at once.
-    const int per_xcd = p.grid >> 3;
-    const int wg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    const int unit = wg / p.max_splits;
+    // Work item from the block index alone (see work_item), so that every
+    // load of the prologue below can be in flight at once.
+    int unit, split;
+    work_item(p, unit, split);
     if (unit >= p.B * p.Hkv)
         return;
-    const int split = wg - unit * p.max_splits;
     const int b = unit / p.Hkv, g = unit - b * p.Hkv;
     const int blk_begin = split * p.bps;
 

@@ -249,10 +249,11 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
     p.num_blocks = num_blocks;
     p.bps = pl.bps;
     p.max_splits = pl.max_splits;
-    const long long wgs = (long long)B * Hkv * pl.max_splits;
+    // 8 * ceil(units / 8) * max_splits workgroups (see work_item in attn.hip)
+    const long long wgs = ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits;
     if (wgs > 0x7FFFFFF0LL)
         return fail(SV_ERR_SHAPE, "too many workgroups");
-    p.grid = (int)(((wgs + 7) / 8) * 8);
+    p.grid = (int)wgs;
     p.qscale = (float)((double)sm_scale * 1.4426950408889634);
 
     const bool use_mfma = (algo == SV_ATTN_MFMA) || (algo == SV_ATTN_AUTO && kv_dtype != SV_KV_F32);

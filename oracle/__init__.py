@@ -42,6 +42,11 @@ def _bind(lib):
     lib.oracle_sample.restype = c.c_int
     lib.oracle_sample.argtypes = (
         [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_sample_t.restype = c.c_int
+    lib.oracle_sample_t.argtypes = (
+        [c.c_void_p] * 5 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_target_row.restype = None
+    lib.oracle_target_row.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_void_p]
     lib.oracle_encode_bf16.restype = c.c_uint16
     lib.oracle_encode_bf16.argtypes = [c.c_float]
     lib.oracle_encode_e4m3.restype = c.c_uint8
@@ -148,8 +153,10 @@ def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=No
     return out
 
 
-def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6, nthreads=None):
-    """The verify sampler by the pages' rule, in fp64.
+def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6, nthreads=None, temperature=None):
+    """The verify sampler by the pages' rule, in fp64.  temperature: [B]
+    per-sequence temperatures (None: 1; <= 0: greedy), applied to the target
+    rows only (the draft probabilities are the draft's actual distribution).
 
     Returns a dict: num_accepted [B] int32, out_tokens [B,K+1] int32,
     accept_ratio [B,K] fp64 (NaN after the first rejection), near_pos [B]
@@ -170,13 +177,23 @@ def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6,
         "near_pos": np.empty(B, dtype=np.int32),
         "resid_mass": np.empty(B, dtype=np.float64),
     }
-    rc = _load().oracle_sample(
-        _ptr(tl), _ptr(dp), _ptr(dt), _ptr(u), B, K, V, float(near_eps),
+    temp = None if temperature is None else np.ascontiguousarray(temperature, dtype=np.float32)
+    assert temp is None or temp.shape == (B,)
+    rc = _load().oracle_sample_t(
+        _ptr(tl), _ptr(dp), _ptr(dt), _ptr(u), _ptr(temp), B, K, V, float(near_eps),
         _ptr(res["num_accepted"]), _ptr(res["out_tokens"]), _ptr(res["accept_ratio"]),
         _ptr(res["near_pos"]), _ptr(res["resid_mass"]), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_sample rejected its arguments")
     return res
+
+
+def target_row(logits, temperature=1.0):
+    """p~ of one target row at a temperature (<= 0: greedy one-hot), fp64."""
+    row = np.ascontiguousarray(logits, dtype=np.float32)
+    out = np.empty(row.shape[0], dtype=np.float64)
+    _load().oracle_target_row(row.ctypes.data, row.shape[0], float(temperature), out.ctypes.data)
+    return out
 
 
 def kv_cache_bytes(ctx_len, n_layers, n_kv_heads, head_dim, bytes_per_elem, batch=1):

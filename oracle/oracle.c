@@ -243,9 +243,43 @@ void oracle_softmax_row(const float *logits, int64_t V, double *p)
         p[j] /= z;
 }
 
+/* Target distribution of one verify row at temperature tau ([KV] 7.5 and the
+ * answer on temperature there: the sampler-transformed p~ replaces p in the
+ * acceptance test, the residual and the bonus draw; p~ is proportional to
+ * p^(1/tau), i.e. softmax(logits / tau), computed as exp((l - max) / tau)
+ * normalised).  tau = 1 is oracle_softmax_row itself; tau <= 0 reads as the
+ * greedy limit: all mass on the first maximal logit. */
+void oracle_target_row(const float *logits, int64_t V, double tau, double *p)
+{
+    if (tau == 1.0) {
+        oracle_softmax_row(logits, V, p);
+        return;
+    }
+    double m = -INFINITY;
+    int64_t arg = 0;
+    for (int64_t j = 0; j < V; ++j)
+        if ((double)logits[j] > m) {
+            m = (double)logits[j];
+            arg = j;
+        }
+    if (!(tau > 0.0)) {
+        for (int64_t j = 0; j < V; ++j)
+            p[j] = j == arg ? 1.0 : 0.0;
+        return;
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+        p[j] = exp(((double)logits[j] - m) / tau);
+        z += p[j];
+    }
+    for (int64_t j = 0; j < V; ++j)
+        p[j] /= z;
+}
+
 typedef struct {
     const float *target_logits, *draft_probs, *uniforms;
     const int32_t *draft_tokens;
+    const float *temperature;
     int B, K;
     int64_t V;
     double near_eps;
@@ -276,13 +310,14 @@ static void sample_one(const sample_job *J, int b, double *p, double *w)
     const int K = J->K;
     const int64_t V = J->V;
     const float *u = J->uniforms + (int64_t)b * (K + 1);
+    const double tau = J->temperature ? (double)J->temperature[b] : 1.0;
     int n = K;
     int near = -1;
 
     for (int i = 0; i < K; ++i) {
         const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + i) * V;
         const float *qrow = J->draft_probs + ((int64_t)b * K + i) * V;
-        oracle_softmax_row(lrow, V, p);
+        oracle_target_row(lrow, V, tau, p);
         int x = J->draft_tokens[(int64_t)b * K + i];
         double a = p[x];
         double c = (double)qrow[x];
@@ -299,7 +334,7 @@ static void sample_one(const sample_job *J, int b, double *p, double *w)
         J->accept_ratio[(int64_t)b * K + i] = NAN;
 
     const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;
-    oracle_softmax_row(lrow, V, p);
+    oracle_target_row(lrow, V, tau, p);
     double S = 0.0;
     if (n < K) {
         const float *qrow = J->draft_probs + ((int64_t)b * K + n) * V;
@@ -386,11 +421,28 @@ static void *sample_worker(void *arg)
  * (positions after the first rejection are NaN), near_pos [B],
  * resid_mass [B] (S before any fallback).  Returns 0, or -1 on bad arguments.
  */
+int oracle_sample_t(const float *target_logits, const float *draft_probs,
+                    const int32_t *draft_tokens, const float *uniforms, const float *temperature,
+                    int B, int K, int64_t V, double near_eps,
+                    int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
+                    int32_t *near_pos, double *resid_mass, int nthreads);
+
 int oracle_sample(const float *target_logits, const float *draft_probs,
                   const int32_t *draft_tokens, const float *uniforms,
                   int B, int K, int64_t V, double near_eps,
                   int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
                   int32_t *near_pos, double *resid_mass, int nthreads)
+{
+    return oracle_sample_t(target_logits, draft_probs, draft_tokens, uniforms, NULL, B, K, V, near_eps,
+                           num_accepted, out_tokens, accept_ratio, near_pos, resid_mass, nthreads);
+}
+
+/* As oracle_sample, with per-sequence temperatures temperature[B] (NULL: 1). */
+int oracle_sample_t(const float *target_logits, const float *draft_probs,
+                    const int32_t *draft_tokens, const float *uniforms, const float *temperature,
+                    int B, int K, int64_t V, double near_eps,
+                    int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
+                    int32_t *near_pos, double *resid_mass, int nthreads)
 {
     if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted ||
         !out_tokens || !accept_ratio || !near_pos || !resid_mass)
@@ -400,7 +452,7 @@ int oracle_sample(const float *target_logits, const float *draft_probs,
     for (int64_t i = 0; i < (int64_t)B * K; ++i)
         if (draft_tokens[i] < 0 || draft_tokens[i] >= V)
             return -1;
-    sample_job J = {target_logits, draft_probs, uniforms, draft_tokens, B, K, V, near_eps,
+    sample_job J = {target_logits, draft_probs, uniforms, draft_tokens, temperature, B, K, V, near_eps,
                     num_accepted, out_tokens, near_pos, accept_ratio, resid_mass};
     if (nthreads < 1)
         nthreads = 1;

@@ -13,6 +13,7 @@ import oracle
 from . import test_oracle_attention as TA
 from . import test_oracle_sampler as TS
 from . import test_oracle_kvcache as TK
+from . import test_oracle_temperature as TT
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -42,6 +43,11 @@ KV_PINS = [
     TK.test_rollback_keeps_the_loop_invariant, TK.test_rollback_extremes,
 ]
 
+TEMP_PINS = [
+    TT.test_target_row_matches_library_softmax, TT.test_greedy_limit_is_greedy_decoding,
+    TT.test_temperature_rescales_the_logits, lambda: TT.test_every_emitted_position_follows_tempered_target(0.5, 0.5),
+]
+
 # (name, original text, replacement, pins expected to catch it)
 MUTANTS = [
     ("head map h % Hkv", "const int g = h / G;", "const int g = h % Hkv;", ATTN_PINS),
@@ -61,8 +67,8 @@ MUTANTS = [
     ("acceptance ratio inverted", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * a < c)) {", SAMPLE_PINS),
     ("non-strict acceptance", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * c <= a)) {", SAMPLE_PINS),
     ("inverse CDF >=", "if (C > target) {", "if (C >= target) {", SAMPLE_PINS),
-    ("final row always 0", "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;\n    oracle_softmax_row",
-     "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + 0) * V;\n    oracle_softmax_row", SAMPLE_PINS),
+    ("final row always 0", "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;\n    oracle_target_row",
+     "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + 0) * V;\n    oracle_target_row", SAMPLE_PINS),
     ("bonus from draft-free row K-1",
      "        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
      "        oracle_softmax_row(lrow - V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
@@ -75,6 +81,11 @@ MUTANTS = [
     ("append K and V swapped", "const float x = which ? v_new[src] : k_new[src];", "const float x = which ? k_new[src] : v_new[src];", KV_PINS),
     ("rollback drops one more", "int L = context_lens[b] - K + num_accepted[b];", "int L = context_lens[b] - K - 1 + num_accepted[b];", KV_PINS),
     ("pages in use rounded down", "pages_in_use[b] = (L + 15) / 16;", "pages_in_use[b] = L / 16;", KV_PINS),
+    ("temperature multiplies", "p[j] = exp(((double)logits[j] - m) / tau);", "p[j] = exp(((double)logits[j] - m) * tau);", TEMP_PINS),
+    ("greedy takes the last maximum", "        if ((double)logits[j] > m) {\n            m = (double)logits[j];\n            arg = j;",
+     "        if ((double)logits[j] >= m) {\n            m = (double)logits[j];\n            arg = j;", TEMP_PINS),
+    ("temperature on the draft row too", "const double tau = J->temperature ? (double)J->temperature[b] : 1.0;",
+     "const double tau = J->temperature ? (double)J->temperature[b] * 0.5 : 1.0;", TEMP_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

@@ -175,6 +175,23 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs,
                        int B, int K, int V,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* As spec_verify_sample with a target temperature per sequence ("KV Cache +
+ * Speculative Decoding" 7.5: exactness holds with the sampler-transformed
+ * target p~ in place of p, whatever distribution the draft sampled from):
+ * every target row of sequence b becomes p~ = softmax(target_logits / T_b),
+ * in the acceptance tests, the residual and the bonus draw.  draft_probs are
+ * the draft's actual (already transformed) distribution and are used as
+ * given.  T_b <= 0 (or NaN) is the greedy limit: all mass on the first
+ * maximal logit of the row, so a draft is accepted iff it is that token and
+ * the drawn token is the argmax of row n.  temperature: [B] float32, or
+ * NULL for T = 1 (identical to spec_verify_sample).  Same workspace. */
+int spec_verify_sample_ex(const float *target_logits, const float *draft_probs,
+                          const int32_t *draft_tokens, const float *uniforms,
+                          const float *temperature,
+                          int32_t *num_accepted, int32_t *out_tokens, float *accept_prob,
+                          int B, int K, int V,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * spec_verify_kv_append: write the K/V of the T verify positions into the
  * paged cache, before spec_verify_attn.

@@ -85,7 +85,7 @@ SamplePlan plan_sample(int B, int K, int V)
     pl.nchunk = ceil_div(V, kSampleChunk);
     size_t off = 0;
     pl.off_state = off;
-    off = align256(off + (size_t)B * 16);
+    off = align256(off + (size_t)B * 32);
     pl.off_stats = off;
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 16);
     pl.off_rowx = off;
@@ -295,6 +295,15 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
                        const float *uniforms, int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B,
                        int K, int V, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return spec_verify_sample_ex(target_logits, draft_probs, draft_tokens, uniforms, nullptr, num_accepted,
+                                 out_tokens, accept_prob, B, K, V, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                          const float *uniforms, const float *temperature, int32_t *num_accepted,
+                          int32_t *out_tokens, float *accept_prob, int B, int K, int V, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
     if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
         return fail(SV_ERR_NULL, "target_logits, draft_probs, draft_tokens, uniforms, num_accepted and "
                                  "out_tokens must be non-NULL");
@@ -310,7 +319,7 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
                     sv::kSampleSub);
     if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
-        (accept_prob && !aligned(accept_prob, 4)))
+        (accept_prob && !aligned(accept_prob, 4)) || (temperature && !aligned(temperature, 4)))
         return fail(SV_ERR_ALIGN, "sampler arrays must be 4-byte aligned");
     const sv::SamplePlan pl = sv::plan_sample(B, K, V);
     if (!workspace)
@@ -325,6 +334,7 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
     p.probs = draft_probs;
     p.tokens = draft_tokens;
     p.uniforms = uniforms;
+    p.temperature = temperature;
     p.num_accepted = num_accepted;
     p.out_tokens = out_tokens;
     p.accept_prob = accept_prob;

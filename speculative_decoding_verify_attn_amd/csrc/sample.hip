@@ -23,10 +23,15 @@
 //             locates the sub-chunk holding u_K * S; the workgroup rescans
 //             that sub-chunk (four entries per thread) with a prefix scan and
 //             writes the outputs.
-// The acceptance tests run in fp64; the weights take fp32 exp of an exactly
-// split argument (about 1e-7 relative) and every sum runs in fp64, so the
-// decisions agree with an exact evaluation except within ~1e-7 of a
-// threshold.
+// The acceptance tests run in fp64; the weights take fp32 exp of an argument
+// formed in fp64 and split exactly (about 1e-7 relative) and every sum runs
+// in fp64, so the decisions agree with an exact evaluation except within
+// ~1e-7 of a threshold.
+//
+// Temperature ("KV Cache + Speculative Decoding" 7.5): with a per-sequence T,
+// every target row is p~ = softmax(logits / T) (the draft probabilities are
+// taken as the draft's actual distribution); T <= 0 is the greedy limit,
+// all mass on the first maximal logit of the row.
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -39,8 +44,8 @@ static_assert(kSampleSub == 4 * kSampleThreads, "a sub-chunk is four entries per
 
 struct RowStat {
     float m;
-    float pad;
-    double z;
+    int arg;     // first index of the chunk's maximum (greedy rows only)
+    double z;    // sum over the chunk of exp((l - m) / T)
 };
 
 // Target logit and draft probability of draft token x_i.
@@ -51,10 +56,34 @@ struct RowX {
 
 // What the draw of one sequence needs from the decide pass.
 struct SeqState {
-    int n;       // accepted drafts
-    float m;     // max logit of row n
-    double inv_z;  // 1 / sum_j exp(l_j - m) of row n
+    int n;         // accepted drafts
+    float m;       // max logit of row n
+    double inv_z;  // 1 / sum_j exp((l_j - m) / T) of row n
+    double inv_t;  // 1 / T
+    int greedy;    // T <= 0: all mass on the first maximal logit ...
+    int arg;       // ... which is this index
 };
+
+// Temperature of sequence b: 1 without a temperature array; T <= 0 (or NaN)
+// is the greedy limit.
+struct Temp {
+    bool greedy;
+    double inv;    // 1 / T in fp64
+    float c_hi;    // log2(e) / T split into two floats for the exponent
+    float c_lo;
+};
+
+__device__ __forceinline__ Temp temp_of(const SampleParams &p, int b)
+{
+    Temp t;
+    const float T = p.temperature ? p.temperature[b] : 1.0f;
+    t.greedy = !(T > 0.0f);
+    t.inv = t.greedy ? 1.0 : 1.0 / (double)T;
+    const double c = 1.4426950408889634074 * t.inv;
+    t.c_hi = (float)c;
+    t.c_lo = (float)(c - (double)t.c_hi);
+    return t;
+}
 
 // Loads this thread's 32 entries of a chunk: entries tid*4 + k*1024 .. +3
 // (float4 path) or tid + k*256 (scalar path); missing entries read `fill`.
@@ -138,50 +167,83 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     for (int k = 1; k < kPer; ++k)
         mx = fmaxf(mx, v[k]);
     const float M = block_max(mx, s_f);
-    // exp(v - M) = 2^((v - M) log2 e) with the hardware exp2; terms summed in
-    // fp64 (the rounding of the scaled argument, |v - M| * 2^-24 relative,
-    // is largest for the terms that matter least).
-    double z = 0.0;
+    const Temp tp = temp_of(p, b);
+    RowStat st;
+    st.m = M;
+    st.arg = 0;
+    st.z = 0.0;
+    if (tp.greedy) {
+        // first index of the maximum within the chunk
+        int first = 0x7FFFFFFF;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        z += (double)__builtin_amdgcn_exp2f((v[k] - M) * kLog2e);
-    z = block_sum(z, s_d);
+        for (int k = 0; k < kPer; ++k) {
+            const int e = VEC ? ((k >> 2) * kSampleThreads + (int)threadIdx.x) * 4 + (k & 3)
+                              : k * kSampleThreads + (int)threadIdx.x;
+            if (v[k] == M && e < first)
+                first = e;
+        }
+        first = wave_min_i32(first);
+        __shared__ int s_i[kNWs];
+        if ((threadIdx.x & 63) == 0)
+            s_i[threadIdx.x >> 6] = first;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kNWs; ++w)
+            first = min(first, s_i[w]);
+        st.arg = base + first;
+    } else {
+        // exp((v - M) / T) = 2^((v - M) log2(e) / T) with the hardware exp2;
+        // the constant log2(e) / T enters as two floats, so the scaled
+        // argument carries one rounding; terms are summed in fp64.  The clamp
+        // sends -inf entries (and a chunk that is -inf throughout, where
+        // v - M is NaN) to a finite difference whose term is 0, whatever the
+        // sign of the low part of the constant.
+        double z = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const float dv = fmaxf(v[k] - M, -3.0e38f);
+            z += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo));
+        }
+        st.z = block_sum(z, s_d);
+    }
     if (threadIdx.x == 0) {
-        RowStat st;
-        st.m = M;
-        st.pad = 0.0f;
-        st.z = z;
         static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
         if (rec)
             static_cast<RowX *>(p.row_x)[(size_t)b * K + i] = rx;
     }
 }
 
-// Target probability of entry j from its logit, the row maximum M and 1/Z,
-// to about one fp32 ulp: the difference l - M is split exactly into hi + lo
-// (TwoSum), exp(hi) comes from the accurate fp32 exp, exp(lo) = 1 + lo to
-// second order (|lo| <= ulp(hi)/2), and the products are taken in fp64.
-__device__ __forceinline__ double target_prob_fast(float l, float M, double invZ)
+// Target probability p~_j of entry j from its logit, the row maximum M, 1/Z
+// and the temperature, to about one fp32 ulp: the argument (l - M) / T is
+// formed in fp64 and split into a float hi and the remainder lo; exp(hi)
+// comes from the accurate fp32 exp and exp(lo) = 1 + lo to second order
+// (|lo| <= ulp(hi)/2); products in fp64.  Greedy rows are one-hot at `arg`.
+__device__ __forceinline__ double target_prob_fast(float l, int j, float M, double invZ, const Temp &tp, int arg)
 {
-    const float hi = l - M;
-    if (!(hi > -104.0f))
+    if (tp.greedy)
+        return j == arg ? 1.0 : 0.0;
+    const double a = ((double)l - (double)M) * tp.inv;
+    if (!(a > -104.0))
         return 0.0;  // underflows in fp32 (and catches l = -inf)
-    const float bb = hi - l;
-    const float lo = (l - (hi - bb)) + (-M - bb);
-    return (double)expf(hi) * (1.0 + (double)lo) * invZ;
+    const float hi = (float)a;
+    const double lo = a - (double)hi;
+    return (double)expf(hi) * (1.0 + lo) * invZ;
 }
 
 // Same quantity in fp64 throughout (used for the K acceptance tests).
-__device__ __forceinline__ double target_prob(float l, float M, double invZ)
+__device__ __forceinline__ double target_prob(float l, int j, float M, double invZ, const Temp &tp, int arg)
 {
-    return exp((double)l - (double)M) * invZ;
+    if (tp.greedy)
+        return j == arg ? 1.0 : 0.0;
+    return exp(((double)l - (double)M) * tp.inv) * invZ;
 }
 
-// Weight of entry j of the chosen row: the residual max(0, p - q) after a
-// rejection, p itself for the bonus row or the zero-mass fallback.
-__device__ __forceinline__ double weight(float l, float q, float M, double invZ, bool residual)
+// Weight of entry j of the chosen row: the residual max(0, p~ - q) after a
+// rejection, p~ itself for the bonus row or the zero-mass fallback.
+__device__ __forceinline__ double weight(float l, float q, int j, float M, double invZ, bool residual, const Temp &tp,
+                                         int arg)
 {
-    const double pj = target_prob_fast(l, M, invZ);
+    const double pj = target_prob_fast(l, j, M, invZ, tp, arg);
     if (!residual)
         return pj;
     const double r = pj - (double)q;
@@ -211,6 +273,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
 {
     __shared__ float s_M[16];
     __shared__ double s_Z[16];
+    __shared__ int s_A[16];
     __shared__ double s_ratio[16];
     __shared__ int s_acc[16];
     __shared__ int s_n;
@@ -226,11 +289,14 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     // 1. Row statistics of the K+1 rows of this sequence (one wave per row,
     //    lanes over vocabulary chunks) and the draft tokens' entries, all
     //    requested together.
+    const Temp tp = temp_of(p, b);
     RowX rx{0.0f, 0.0f};
     float u = 0.0f;
+    int x = 0;
     if (tid < K) {
         rx = static_cast<const RowX *>(p.row_x)[(size_t)b * K + tid];
         u = p.uniforms[(size_t)b * K1 + tid];
+        x = clamp_token(p.tokens[(size_t)b * K + tid], V);
     }
     for (int i = wave; i < K1; i += kNWs) {
         const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
@@ -239,20 +305,29 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
             mloc = fmaxf(mloc, st[c].m);
         const float M = wave_max_f32(mloc);
         double zloc = 0.0;
+        int aloc = 0x7FFFFFFF;
         for (int c = lane; c < p.nchunk; c += kWave) {
             const RowStat r = st[c];
-            zloc += r.z * exp((double)r.m - (double)M);
+            if (tp.greedy) {
+                if (r.m == M && r.arg < aloc)
+                    aloc = r.arg;  // chunks are in index order: the first maximal chunk
+            } else {
+                if (r.z > 0.0)  // a chunk that is -inf throughout adds nothing
+                    zloc += r.z * exp(((double)r.m - (double)M) * tp.inv);
+            }
         }
         const double Z = wave_sum_f64(zloc);
+        const int A = wave_min_i32(aloc);
         if (lane == 0) {
             s_M[i] = M;
             s_Z[i] = Z;
+            s_A[i] = A;
         }
     }
     __syncthreads();
-    // 2. Acceptance tests u_i * q_i(x_i) < p_i(x_i).
+    // 2. Acceptance tests u_i * q_i(x_i) < p~_i(x_i).
     if (tid < K) {
-        const double a = target_prob(rx.lx, s_M[tid], 1.0 / s_Z[tid]);
+        const double a = target_prob(rx.lx, x, s_M[tid], 1.0 / s_Z[tid], tp, s_A[tid]);
         const double c = (double)rx.qx;
         s_acc[tid] = ((double)u * c < a) ? 1 : 0;
         s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
@@ -272,6 +347,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     const bool residual = n < K;
     const float M = s_M[n];
     const double invZ = 1.0 / s_Z[n];
+    const int arg = s_A[n];
 
     // 3. Mass of this sub-chunk: residual (or bonus) weights and plain
     //    target mass.
@@ -284,7 +360,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     double sw = 0.0, sp = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const double pj = target_prob_fast(lv[k], M, invZ);
+        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, tp, arg);
         sp += pj;
         if (residual) {
             const double r = pj - (double)qv[k];
@@ -314,6 +390,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         ss.n = n;
         ss.m = M;
         ss.inv_z = invZ;
+        ss.inv_t = tp.inv;
+        ss.greedy = tp.greedy ? 1 : 0;
+        ss.arg = arg;
         static_cast<SeqState *>(p.seq_state)[b] = ss;
     }
     if (sub == 0 && p.accept_prob && tid < K)
@@ -343,6 +422,10 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const bool residual = n < K;
     const float M = ss.m;
     const double invZ = ss.inv_z;
+    Temp tp;
+    tp.greedy = ss.greedy != 0;
+    tp.inv = ss.inv_t;
+    tp.c_hi = tp.c_lo = 0.0f;  // (row sums are not recomputed here)
     const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
     const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
 
@@ -424,7 +507,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     double seg = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        wv[k] = weight(lv[k], qv[k], M, invZ, use_resid);
+        wv[k] = weight(lv[k], qv[k], base + e0 + k, M, invZ, use_resid, tp, ss.arg);
         seg += wv[k];
     }
     // Exclusive prefix of the run sums across the workgroup.

@@ -58,10 +58,11 @@ struct SampleParams {
     const float *probs;      // [B][K][V]
     const int32_t *tokens;   // [B][K]
     const float *uniforms;   // [B][K+1]
+    const float *temperature;  // [B] or null (1)
     int32_t *num_accepted;   // [B]
     int32_t *out_tokens;     // [B][K+1]
     float *accept_prob;      // [B][K] or null
-    void *seq_state;         // [B] {accepted count, row max, 1/row sum} for the draw
+    void *seq_state;         // [B] {accepted count, row max, 1/row sum, 1/T, greedy, argmax} (32 B)
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
     void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_lists_the_calls():
     names = declared_functions()
-    for must in ("spec_verify_attn", "spec_verify_sample", "spec_verify_attn_workspace_size",
+    for must in ("spec_verify_attn", "spec_verify_sample", "spec_verify_sample_ex", "spec_verify_attn_workspace_size",
                  "spec_verify_sample_workspace_size", "sv_last_error"):
         assert must in names
 
@@ -92,6 +92,11 @@ def test_sample_argument_checks():
     assert L.spec_verify_sample(p, p, p, p, p, p, None, 2, 3, 100, p, 8, None) == 4
     assert L.spec_verify_sample(p, p, p, p, p, p, None, 2, 3, 100, None, 1 << 14, None) == 4
     assert L.spec_verify_sample(p + 2, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
+    # the temperature variant: same checks, plus the temperature array's alignment
+    ex = L.spec_verify_sample_ex
+    assert ex(None, p, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 1
+    assert ex(p, p, p, p, None, p, p, None, 2, 16, 100, p, 1 << 14, None) == 2
+    assert ex(p, p, p, p, p + 1, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
 
 
 def test_workspace_queries():

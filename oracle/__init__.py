@@ -45,6 +45,11 @@ def _bind(lib):
     lib.oracle_sample_t.restype = c.c_int
     lib.oracle_sample_t.argtypes = (
         [c.c_void_p] * 5 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_sample_tp.restype = c.c_int
+    lib.oracle_sample_tp.argtypes = (
+        [c.c_void_p] * 6 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_top_p.restype = c.c_int
+    lib.oracle_top_p.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_double, c.c_void_p]
     lib.oracle_target_row.restype = None
     lib.oracle_target_row.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_void_p]
     lib.oracle_encode_bf16.restype = c.c_uint16
@@ -153,10 +158,13 @@ def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=No
     return out
 
 
-def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6, nthreads=None, temperature=None):
+def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6, nthreads=None, temperature=None,
+           top_p=None):
     """The verify sampler by the pages' rule, in fp64.  temperature: [B]
     per-sequence temperatures (None: 1; <= 0: greedy), applied to the target
     rows only (the draft probabilities are the draft's actual distribution).
+    top_p: [B] per-sequence top-p cuts of the (tempered) target rows (None,
+    >= 1 or NaN: no cut); an ambiguous cut also sets near_pos.
 
     Returns a dict: num_accepted [B] int32, out_tokens [B,K+1] int32,
     accept_ratio [B,K] fp64 (NaN after the first rejection), near_pos [B]
@@ -179,8 +187,10 @@ def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6,
     }
     temp = None if temperature is None else np.ascontiguousarray(temperature, dtype=np.float32)
     assert temp is None or temp.shape == (B,)
-    rc = _load().oracle_sample_t(
-        _ptr(tl), _ptr(dp), _ptr(dt), _ptr(u), _ptr(temp), B, K, V, float(near_eps),
+    tpp = None if top_p is None else np.ascontiguousarray(top_p, dtype=np.float32)
+    assert tpp is None or tpp.shape == (B,)
+    rc = _load().oracle_sample_tp(
+        _ptr(tl), _ptr(dp), _ptr(dt), _ptr(u), _ptr(temp), _ptr(tpp), B, K, V, float(near_eps),
         _ptr(res["num_accepted"]), _ptr(res["out_tokens"]), _ptr(res["accept_ratio"]),
         _ptr(res["near_pos"]), _ptr(res["resid_mass"]), nthreads or default_threads())
     if rc != 0:
@@ -188,12 +198,21 @@ def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6,
     return res
 
 
-def target_row(logits, temperature=1.0):
-    """p~ of one target row at a temperature (<= 0: greedy one-hot), fp64."""
+def target_row(logits, temperature=1.0, top_p=None, near_eps=1e-6, return_ambiguous=False):
+    """p~ of one target row at a temperature (<= 0: greedy one-hot), cut to
+    its top-p set and renormalised if top_p is given (not for greedy rows),
+    fp64.  With return_ambiguous, also whether the cut lies within near_eps."""
     row = np.ascontiguousarray(logits, dtype=np.float32)
     out = np.empty(row.shape[0], dtype=np.float64)
-    _load().oracle_target_row(row.ctypes.data, row.shape[0], float(temperature), out.ctypes.data)
-    return out
+    lib = _load()
+    lib.oracle_target_row(row.ctypes.data, row.shape[0], float(temperature), out.ctypes.data)
+    amb = 0
+    if top_p is not None and float(temperature) > 0:
+        amb = lib.oracle_top_p(row.ctypes.data, row.shape[0], float(np.float32(top_p)), float(near_eps),
+                               out.ctypes.data)
+        if amb < 0:
+            raise MemoryError("oracle_top_p")
+    return (out, bool(amb)) if return_ambiguous else out
 
 
 def kv_cache_bytes(ctx_len, n_layers, n_kv_heads, head_dim, bytes_per_elem, batch=1):

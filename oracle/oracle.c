@@ -276,10 +276,73 @@ void oracle_target_row(const float *logits, int64_t V, double tau, double *p)
         p[j] /= z;
 }
 
+/* Entry of the ranking used by the top-p truncation: a token and its logit. */
+typedef struct {
+    float l;
+    int64_t j;
+} ranked;
+
+static int rank_desc(const void *a, const void *b)
+{
+    const ranked *x = (const ranked *)a, *y = (const ranked *)b;
+    if (x->l != y->l)
+        return x->l > y->l ? -1 : 1;
+    return x->j < y->j ? -1 : (x->j > y->j ? 1 : 0);
+}
+
+/* Top-p truncation of a target row ([KV] 7.5 and its answer on top-p: p~ is p
+ * cut to p's own top-p set and renormalised; the rejection rule stays exact
+ * because p~ is again a distribution).  The set: tokens ranked by their
+ * logit (which orders p, as p grows with the logit), a token is kept iff the
+ * mass of the tokens ranked strictly above it is below top_p; the tokens of
+ * the highest logit are always kept, so top_p <= 0 leaves that group only.
+ * Equal logits share one decision.  top_p >= 1 or NaN keeps everything.
+ * p (the untruncated row, summing to 1) is truncated and renormalised in
+ * place.  Returns 1 if the set is decided within near_eps of top_p (the last
+ * kept or the first dropped group), 0 if not, -1 if out of memory. */
+int oracle_top_p(const float *logits, int64_t V, double top_p, double near_eps, double *p)
+{
+    if (!(top_p < 1.0))
+        return 0;
+    ranked *r = (ranked *)malloc(sizeof(ranked) * (size_t)V);
+    if (!r)
+        return -1;
+    for (int64_t j = 0; j < V; ++j) {
+        r[j].l = logits[j];
+        r[j].j = j;
+    }
+    qsort(r, (size_t)V, sizeof(ranked), rank_desc);
+    double above = 0.0, kept = 0.0;
+    int amb = 0;
+    int64_t g = 0;
+    int first = 1;
+    while (g < V) {
+        int64_t e = g;
+        double mass = 0.0;
+        while (e < V && r[e].l == r[g].l)
+            mass += p[r[e++].j];
+        const int keep = first || above < top_p;
+        if (!first && fabs(above - top_p) < near_eps)
+            amb = 1;
+        if (!keep)
+            break;
+        kept += mass;
+        above += mass;
+        first = 0;
+        g = e;
+    }
+    for (int64_t k = g; k < V; ++k)
+        p[r[k].j] = 0.0;
+    for (int64_t j = 0; j < V; ++j)
+        p[j] /= kept;
+    free(r);
+    return amb;
+}
+
 typedef struct {
     const float *target_logits, *draft_probs, *uniforms;
     const int32_t *draft_tokens;
-    const float *temperature;
+    const float *temperature, *top_p;
     int B, K;
     int64_t V;
     double near_eps;
@@ -305,19 +368,30 @@ typedef struct {
  *   threshold (acceptance: |u_i - min(1, p/q)|; final draw: u_K within
  *   near_eps of either edge of the chosen token's CDF interval), else -1.
  */
+/* p~ of row i of sequence b: temperature, then the top-p cut (skipped for
+ * greedy rows, already one-hot).  Returns 1 if the cut is ambiguous. */
+static int row_dist(const sample_job *J, int b, int i, double *p)
+{
+    const double tau = J->temperature ? (double)J->temperature[b] : 1.0;
+    const float *lrow = J->target_logits + ((int64_t)b * (J->K + 1) + i) * J->V;
+    oracle_target_row(lrow, J->V, tau, p);
+    if (!J->top_p || !(tau > 0.0))
+        return 0;
+    return oracle_top_p(lrow, J->V, (double)J->top_p[b], J->near_eps, p);
+}
+
 static void sample_one(const sample_job *J, int b, double *p, double *w)
 {
     const int K = J->K;
     const int64_t V = J->V;
     const float *u = J->uniforms + (int64_t)b * (K + 1);
-    const double tau = J->temperature ? (double)J->temperature[b] : 1.0;
     int n = K;
     int near = -1;
 
     for (int i = 0; i < K; ++i) {
-        const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + i) * V;
         const float *qrow = J->draft_probs + ((int64_t)b * K + i) * V;
-        oracle_target_row(lrow, V, tau, p);
+        if (row_dist(J, b, i, p) && near < 0)
+            near = i;
         int x = J->draft_tokens[(int64_t)b * K + i];
         double a = p[x];
         double c = (double)qrow[x];
@@ -333,8 +407,8 @@ static void sample_one(const sample_job *J, int b, double *p, double *w)
     for (int i = n + 1; i < K; ++i)
         J->accept_ratio[(int64_t)b * K + i] = NAN;
 
-    const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;
-    oracle_target_row(lrow, V, tau, p);
+    if (row_dist(J, b, n, p) && near < 0)
+        near = n;
     double S = 0.0;
     if (n < K) {
         const float *qrow = J->draft_probs + ((int64_t)b * K + n) * V;
@@ -437,12 +511,30 @@ int oracle_sample(const float *target_logits, const float *draft_probs,
                            num_accepted, out_tokens, accept_ratio, near_pos, resid_mass, nthreads);
 }
 
+int oracle_sample_tp(const float *target_logits, const float *draft_probs,
+                     const int32_t *draft_tokens, const float *uniforms, const float *temperature,
+                     const float *top_p, int B, int K, int64_t V, double near_eps,
+                     int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
+                     int32_t *near_pos, double *resid_mass, int nthreads);
+
 /* As oracle_sample, with per-sequence temperatures temperature[B] (NULL: 1). */
 int oracle_sample_t(const float *target_logits, const float *draft_probs,
                     const int32_t *draft_tokens, const float *uniforms, const float *temperature,
                     int B, int K, int64_t V, double near_eps,
                     int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
                     int32_t *near_pos, double *resid_mass, int nthreads)
+{
+    return oracle_sample_tp(target_logits, draft_probs, draft_tokens, uniforms, temperature, NULL, B, K, V,
+                            near_eps, num_accepted, out_tokens, accept_ratio, near_pos, resid_mass, nthreads);
+}
+
+/* As oracle_sample_t, with per-sequence top-p values top_p[B] (NULL: none);
+ * a top-p decision within near_eps also sets near_pos. */
+int oracle_sample_tp(const float *target_logits, const float *draft_probs,
+                     const int32_t *draft_tokens, const float *uniforms, const float *temperature,
+                     const float *top_p, int B, int K, int64_t V, double near_eps,
+                     int32_t *num_accepted, int32_t *out_tokens, double *accept_ratio,
+                     int32_t *near_pos, double *resid_mass, int nthreads)
 {
     if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted ||
         !out_tokens || !accept_ratio || !near_pos || !resid_mass)
@@ -452,7 +544,7 @@ int oracle_sample_t(const float *target_logits, const float *draft_probs,
     for (int64_t i = 0; i < (int64_t)B * K; ++i)
         if (draft_tokens[i] < 0 || draft_tokens[i] >= V)
             return -1;
-    sample_job J = {target_logits, draft_probs, uniforms, draft_tokens, temperature, B, K, V, near_eps,
+    sample_job J = {target_logits, draft_probs, uniforms, draft_tokens, temperature, top_p, B, K, V, near_eps,
                     num_accepted, out_tokens, near_pos, accept_ratio, resid_mass};
     if (nthreads < 1)
         nthreads = 1;

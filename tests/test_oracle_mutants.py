@@ -14,6 +14,7 @@ from . import test_oracle_attention as TA
 from . import test_oracle_sampler as TS
 from . import test_oracle_kvcache as TK
 from . import test_oracle_temperature as TT
+from . import test_oracle_topp as TP
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -48,6 +49,11 @@ TEMP_PINS = [
     TT.test_temperature_rescales_the_logits, lambda: TT.test_every_emitted_position_follows_tempered_target(0.5, 0.5),
 ]
 
+TOPP_PINS = [
+    TP.test_cut_matches_the_ascending_cumsum_recipe, TP.test_cut_matches_the_threshold_form_with_ties,
+    TP.test_vanishing_top_p_is_the_greedy_limit, TP.test_full_or_nan_top_p_changes_nothing,
+]
+
 # (name, original text, replacement, pins expected to catch it)
 MUTANTS = [
     ("head map h % Hkv", "const int g = h / G;", "const int g = h % Hkv;", ATTN_PINS),
@@ -67,8 +73,7 @@ MUTANTS = [
     ("acceptance ratio inverted", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * a < c)) {", SAMPLE_PINS),
     ("non-strict acceptance", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * c <= a)) {", SAMPLE_PINS),
     ("inverse CDF >=", "if (C > target) {", "if (C >= target) {", SAMPLE_PINS),
-    ("final row always 0", "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + n) * V;\n    oracle_target_row",
-     "const float *lrow = J->target_logits + ((int64_t)b * (K + 1) + 0) * V;\n    oracle_target_row", SAMPLE_PINS),
+    ("final row always 0", "if (row_dist(J, b, n, p) && near < 0)", "if (row_dist(J, b, 0, p) && near < 0)", SAMPLE_PINS),
     ("bonus from draft-free row K-1",
      "        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
      "        oracle_softmax_row(lrow - V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
@@ -86,6 +91,12 @@ MUTANTS = [
      "        if ((double)logits[j] >= m) {\n            m = (double)logits[j];\n            arg = j;", TEMP_PINS),
     ("temperature on the draft row too", "const double tau = J->temperature ? (double)J->temperature[b] : 1.0;",
      "const double tau = J->temperature ? (double)J->temperature[b] * 0.5 : 1.0;", TEMP_PINS),
+    ("top-p not renormalised", "        p[j] /= kept;", "        p[j] /= 1.0;", TOPP_PINS),
+    ("top-p splits ties", "while (e < V && r[e].l == r[g].l)", "while (e < V && e == g)", TOPP_PINS),
+    ("top-p ranks ascending", "return x->l > y->l ? -1 : 1;", "return x->l < y->l ? -1 : 1;", TOPP_PINS),
+    ("top-p may drop the top group", "const int keep = first || above < top_p;", "const int keep = above < top_p;", TOPP_PINS),
+    ("top-p counts the token itself", "const int keep = first || above < top_p;",
+     "const int keep = first || above + mass < top_p;", TOPP_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

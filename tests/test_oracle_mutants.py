@@ -76,7 +76,7 @@ MUTANTS = [
     ("final row always 0", "if (row_dist(J, b, n, p) && near < 0)", "if (row_dist(J, b, 0, p) && near < 0)", SAMPLE_PINS),
     ("bonus from draft-free row K-1",
      "        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
-     "        oracle_softmax_row(lrow - V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
+     "        oracle_softmax_row(J->target_logits + ((int64_t)b * (K + 1) + K - 1) * V, V, p);\n        for (int64_t j = 0; j < V; ++j) {\n            w[j] = p[j];\n            S += w[j];\n        }\n    }\n    J->resid_mass",
      SAMPLE_PINS),
     ("bf16 ties away from zero", "if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u)))", "if (drop >= 0x8000u)", KV_PINS),
     ("e4m3 ties to odd", "if (d < bestd || (d == bestd && (c & 1) == 0)) {", "if (d < bestd || (d == bestd && (c & 1) == 1)) {", KV_PINS),

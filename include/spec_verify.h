@@ -175,19 +175,31 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs,
                        int B, int K, int V,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* As spec_verify_sample with a target temperature per sequence ("KV Cache +
- * Speculative Decoding" 7.5: exactness holds with the sampler-transformed
- * target p~ in place of p, whatever distribution the draft sampled from):
- * every target row of sequence b becomes p~ = softmax(target_logits / T_b),
+/* As spec_verify_sample with the target rows transformed per sequence by a
+ * temperature and a top-p cut ("KV Cache + Speculative Decoding" 7.5 and its
+ * answer on temperature / top-p: exactness holds with the sampler-
+ * transformed target p~ in place of p, whatever distribution the draft
+ * sampled from).  Every target row of sequence b becomes
+ *   p~ = softmax(target_logits / T_b), then cut to its top-p set and
+ *   renormalised,
  * in the acceptance tests, the residual and the bonus draw.  draft_probs are
  * the draft's actual (already transformed) distribution and are used as
- * given.  T_b <= 0 (or NaN) is the greedy limit: all mass on the first
- * maximal logit of the row, so a draft is accepted iff it is that token and
- * the drawn token is the argmax of row n.  temperature: [B] float32, or
- * NULL for T = 1 (identical to spec_verify_sample).  Same workspace. */
+ * given.
+ *   temperature: [B] float32, or NULL for T = 1.  T_b <= 0 (or NaN) is the
+ *     greedy limit: all mass on the first maximal logit of the row, so a
+ *     draft is accepted iff it is that token and the drawn token is the
+ *     argmax of row n (top_p does not apply).
+ *   top_p: [B] float32, or NULL for no cut.  Tokens are ranked by logit; a
+ *     token is kept iff the p~-mass ranked strictly above it is below top_p_b;
+ *     the tokens of the maximal logit are always kept (so top_p_b <= 0 keeps
+ *     only them) and equal logits are kept or dropped together.
+ *     top_p_b >= 1 or NaN: no cut.  Masses are summed in 2^-43 fixed point
+ *     (deterministic), which needs V < 2^20 when top_p is given
+ *     (SV_ERR_UNSUPPORTED otherwise).  Adds one launch.
+ * With both NULL this is spec_verify_sample.  Same workspace. */
 int spec_verify_sample_ex(const float *target_logits, const float *draft_probs,
                           const int32_t *draft_tokens, const float *uniforms,
-                          const float *temperature,
+                          const float *temperature, const float *top_p,
                           int32_t *num_accepted, int32_t *out_tokens, float *accept_prob,
                           int B, int K, int V,
                           void *workspace, size_t workspace_bytes, void *stream);

@@ -66,7 +66,7 @@ def lib():
         L.spec_verify_sample.restype = I
         L.spec_verify_sample.argtypes = [P] * 7 + [I] * 3 + [P, S, P]
         L.spec_verify_sample_ex.restype = I
-        L.spec_verify_sample_ex.argtypes = [P] * 8 + [I] * 3 + [P, S, P]
+        L.spec_verify_sample_ex.argtypes = [P] * 9 + [I] * 3 + [P, S, P]
         L.spec_verify_kv_append.restype = I
         L.spec_verify_kv_append.argtypes = [P] * 8 + [I] * 8 + [P]
         L.spec_verify_rollback.restype = I
@@ -155,18 +155,20 @@ def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, worksp
 
 
 def spec_verify_sample(target_logits, draft_probs, draft_tokens, uniforms, num_accepted, out_tokens,
-                       workspace, *, accept_prob=None, stream=None, temperature=None):
+                       workspace, *, accept_prob=None, stream=None, temperature=None, top_p=None):
     """Verify sampler (see include/spec_verify.h).
 
     target_logits [B,K+1,V] f32, draft_probs [B,K,V] f32, draft_tokens [B,K] i32,
     uniforms [B,K+1] f32 in [0,1); outputs num_accepted [B] i32, out_tokens
     [B,K+1] i32, optional accept_prob [B,K] f32.  temperature: optional [B]
-    f32 target temperatures (spec_verify_sample_ex; <= 0 is greedy).
+    f32 target temperatures (<= 0 is greedy); top_p: optional [B] f32 top-p
+    cuts of the target rows (>= 1 or NaN: none).  Either routes the call to
+    spec_verify_sample_ex.
     """
     B, K1, V = target_logits.shape
     _check("spec_verify_sample", lib().spec_verify_sample_ex(
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature),
-        _ptr(num_accepted), _ptr(out_tokens), _ptr(accept_prob), B, K1 - 1, V,
+        _ptr(top_p), _ptr(num_accepted), _ptr(out_tokens), _ptr(accept_prob), B, K1 - 1, V,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, target_logits.device)))
     return num_accepted, out_tokens

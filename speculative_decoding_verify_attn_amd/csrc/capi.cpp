@@ -85,13 +85,15 @@ SamplePlan plan_sample(int B, int K, int V)
     pl.nchunk = ceil_div(V, kSampleChunk);
     size_t off = 0;
     pl.off_state = off;
-    off = align256(off + (size_t)B * 32);
+    off = align256(off + (size_t)B * kSeqStateBytes);
     pl.off_stats = off;
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 16);
     pl.off_rowx = off;
     off = align256(off + (size_t)B * K * 8);
     pl.off_mass = off;
     off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
+    pl.off_cut = off;
+    off = align256(off + (size_t)B * (K + 1) * kRowCutBytes);
     pl.total = off;
     return pl;
 }
@@ -295,14 +297,14 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
                        const float *uniforms, int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B,
                        int K, int V, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return spec_verify_sample_ex(target_logits, draft_probs, draft_tokens, uniforms, nullptr, num_accepted,
-                                 out_tokens, accept_prob, B, K, V, workspace, workspace_bytes, stream);
+    return spec_verify_sample_ex(target_logits, draft_probs, draft_tokens, uniforms, nullptr, nullptr,
+                                 num_accepted, out_tokens, accept_prob, B, K, V, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
-                          const float *uniforms, const float *temperature, int32_t *num_accepted,
-                          int32_t *out_tokens, float *accept_prob, int B, int K, int V, void *workspace,
-                          size_t workspace_bytes, void *stream)
+                          const float *uniforms, const float *temperature, const float *top_p,
+                          int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B, int K, int V,
+                          void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
         return fail(SV_ERR_NULL, "target_logits, draft_probs, draft_tokens, uniforms, num_accepted and "
@@ -313,13 +315,16 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
         return fail(SV_ERR_SHAPE, "K must be <= 15 (got %d)", K);
     if (V > sv::kMaxSampleChunks * sv::kSampleChunk)
         return fail(SV_ERR_UNSUPPORTED, "V must be <= %d (got %d)", sv::kMaxSampleChunks * sv::kSampleChunk, V);
+    if (top_p && V >= sv::kCutMaxV)
+        return fail(SV_ERR_UNSUPPORTED, "top_p needs V < %d (got %d)", sv::kCutMaxV, V);
     if ((long long)B * (K + 1) * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL ||
         (long long)B * ((V + sv::kSampleSub - 1) / sv::kSampleSub) > 0x7FFFFFFFLL)
         return fail(SV_ERR_SHAPE, "B*(K+1)*ceil(V/%d) or B*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk,
                     sv::kSampleSub);
     if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
-        (accept_prob && !aligned(accept_prob, 4)) || (temperature && !aligned(temperature, 4)))
+        (accept_prob && !aligned(accept_prob, 4)) || (temperature && !aligned(temperature, 4)) ||
+        (top_p && !aligned(top_p, 4)))
         return fail(SV_ERR_ALIGN, "sampler arrays must be 4-byte aligned");
     const sv::SamplePlan pl = sv::plan_sample(B, K, V);
     if (!workspace)
@@ -335,6 +340,7 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.tokens = draft_tokens;
     p.uniforms = uniforms;
     p.temperature = temperature;
+    p.top_p = top_p;
     p.num_accepted = num_accepted;
     p.out_tokens = out_tokens;
     p.accept_prob = accept_prob;
@@ -342,6 +348,7 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.row_stats = ws + pl.off_stats;
     p.row_x = ws + pl.off_rowx;
     p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
+    p.row_cut = top_p ? ws + pl.off_cut : nullptr;
     p.B = B;
     p.K = K;
     p.V = V;

@@ -32,6 +32,17 @@
 // every target row is p~ = softmax(logits / T) (the draft probabilities are
 // taken as the draft's actual distribution); T <= 0 is the greedy limit,
 // all mass on the first maximal logit of the row.
+//
+// Top-p (same section): with a per-sequence top_p < 1 a fourth launch, cut,
+// runs between rowstats and decide, one 1024-thread workgroup per target
+// row.  Tokens are ranked by logit; a token is kept iff the mass ranked
+// strictly above it is below top_p (the top logit always kept), and p~ is
+// renormalised over the kept set.  The cut is a radix select over an
+// order-preserving 32-bit key of the logit, 12 + 12 + 8 bits in three passes
+// over the (cache-resident) row, histogramming the masses exp((l - M) / T) in
+// 2^-43 fixed point with LDS integer atomics, so the result does not depend
+// on the order of the additions.  Its output per row is the cut logit tau
+// (every l >= tau is kept) and 1 / kept mass.
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -58,11 +69,23 @@ struct RowX {
 struct SeqState {
     int n;         // accepted drafts
     float m;       // max logit of row n
-    double inv_z;  // 1 / sum_j exp((l_j - m) / T) of row n
+    double inv_z;  // 1 / (kept) sum_j exp((l_j - m) / T) of row n
     double inv_t;  // 1 / T
     int greedy;    // T <= 0: all mass on the first maximal logit ...
     int arg;       // ... which is this index
+    float tau;     // top-p cut of row n: entries with l < tau have p~ = 0
+    int pad;
 };
+static_assert(sizeof(SeqState) <= kSeqStateBytes, "workspace slot of SeqState");
+
+// Top-p cut of one target row: entries with l >= tau are kept; inv_p is
+// 1 / sum of exp((l - M) / T) over them, or negative when the row is not cut.
+struct RowCut {
+    float tau;
+    int pad;
+    double inv_p;
+};
+static_assert(sizeof(RowCut) == kRowCutBytes, "workspace slot of RowCut");
 
 // Temperature of sequence b: 1 without a temperature array; T <= 0 (or NaN)
 // is the greedy limit.
@@ -218,10 +241,13 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
 // formed in fp64 and split into a float hi and the remainder lo; exp(hi)
 // comes from the accurate fp32 exp and exp(lo) = 1 + lo to second order
 // (|lo| <= ulp(hi)/2); products in fp64.  Greedy rows are one-hot at `arg`.
-__device__ __forceinline__ double target_prob_fast(float l, int j, float M, double invZ, const Temp &tp, int arg)
+__device__ __forceinline__ double target_prob_fast(float l, int j, float M, double invZ, const Temp &tp, int arg,
+                                                   float tau)
 {
     if (tp.greedy)
         return j == arg ? 1.0 : 0.0;
+    if (!(l >= tau))
+        return 0.0;  // outside the top-p set
     const double a = ((double)l - (double)M) * tp.inv;
     if (!(a > -104.0))
         return 0.0;  // underflows in fp32 (and catches l = -inf)
@@ -231,23 +257,195 @@ __device__ __forceinline__ double target_prob_fast(float l, int j, float M, doub
 }
 
 // Same quantity in fp64 throughout (used for the K acceptance tests).
-__device__ __forceinline__ double target_prob(float l, int j, float M, double invZ, const Temp &tp, int arg)
+__device__ __forceinline__ double target_prob(float l, int j, float M, double invZ, const Temp &tp, int arg,
+                                              float tau)
 {
     if (tp.greedy)
         return j == arg ? 1.0 : 0.0;
+    if (!(l >= tau))
+        return 0.0;
     return exp(((double)l - (double)M) * tp.inv) * invZ;
 }
 
 // Weight of entry j of the chosen row: the residual max(0, p~ - q) after a
 // rejection, p~ itself for the bonus row or the zero-mass fallback.
 __device__ __forceinline__ double weight(float l, float q, int j, float M, double invZ, bool residual, const Temp &tp,
-                                         int arg)
+                                         int arg, float tau)
 {
-    const double pj = target_prob_fast(l, j, M, invZ, tp, arg);
+    const double pj = target_prob_fast(l, j, M, invZ, tp, arg, tau);
     if (!residual)
         return pj;
     const double r = pj - (double)q;
     return r > 0.0 ? r : 0.0;
+}
+
+// ---------------------------------------------------------------- top-p cut
+
+constexpr int kCutThreads = 1024;
+constexpr int kCutWaves = kCutThreads / kWave;
+constexpr int kCutBuckets = 4096;       // 12-bit digits (the last pass uses 8)
+constexpr double kCutScale = 8796093022208.0;  // 2^43: masses <= 1 per entry, V < 2^20
+
+// Order-preserving key of a float: larger logit, larger key; -0 takes the
+// key of +0, as the two compare equal.
+__device__ __forceinline__ uint32_t logit_key(float l)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, l);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_logit(uint32_t k)
+{
+    return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// exp((l - M) / T) to about one fp32 ulp (as target_prob_fast), in 2^-43
+// fixed point, rounded to nearest.
+__device__ __forceinline__ uint64_t cut_mass(float l, float M, double inv)
+{
+    const double a = ((double)l - (double)M) * inv;
+    if (!(a > -31.0))
+        return 0;  // rounds to 0 at 2^-43 (and -inf entries)
+    const float hi = (float)a;
+    const double lo = a - (double)hi;
+    return (uint64_t)__builtin_rint((double)expf(hi) * (1.0 + lo) * kCutScale);
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t t = __shfl_up(v, o, 64);
+        if (lane >= o)
+            v += t;
+    }
+    return v;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kCutThreads) void sv_sample_cut_kernel(SampleParams p)
+{
+    __shared__ unsigned long long s_hist[kCutBuckets];
+    __shared__ unsigned long long s_wsum[kCutWaves];
+    __shared__ int s_digit;
+    __shared__ unsigned long long s_carry, s_found;
+
+    const int row = blockIdx.x;
+    const int K1 = p.K + 1;
+    const int b = row / K1;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    RowCut* out = static_cast<RowCut *>(p.row_cut) + row;
+    const Temp tp = temp_of(p, b);
+    const float top_p = p.top_p[b];
+    if (tp.greedy || !(top_p < 1.0f)) {  // uniform across the workgroup
+        if (tid == 0)
+            *out = RowCut{-__builtin_inff(), 0, -1.0};
+        return;
+    }
+    // Row maximum from the chunk statistics.
+    if (wave == 0) {
+        const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)row * p.nchunk;
+        float m = -__builtin_inff();
+        for (int c = lane; c < p.nchunk; c += kWave)
+            m = fmaxf(m, st[c].m);
+        m = wave_max_f32(m);
+        if (lane == 0)
+            s_hist[0] = __builtin_bit_cast(uint32_t, m);
+    }
+    __syncthreads();
+    const float M = __builtin_bit_cast(float, (uint32_t)s_hist[0]);
+    __syncthreads();
+    const float *lrow = p.logits + (size_t)row * p.V;
+    const int V = p.V;
+
+    uint32_t prefix = 0;        // key bits fixed so far
+    unsigned long long carry = 0, tgt = 0;
+    // pass 0: bits 31..20; pass 1: bits 19..8; pass 2: bits 7..0
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+        const int nb = pass == 2 ? 256 : kCutBuckets;
+        const int pshift = pass == 0 ? 32 : (pass == 1 ? 20 : 8);  // bits above the digit
+        for (int i = tid; i < nb; i += kCutThreads)
+            s_hist[i] = 0;
+        __syncthreads();
+        auto visit = [&](float l) {
+            const uint32_t k = logit_key(l);
+            if (pshift < 32 && (k >> pshift) != prefix)
+                return;
+            const uint64_t w = cut_mass(l, M, tp.inv);
+            if (w)
+                atomicAdd(&s_hist[(k >> shift) & (uint32_t)(nb - 1)], (unsigned long long)w);
+        };
+        if constexpr (VEC) {
+            for (int e = tid * 4; e < V; e += kCutThreads * 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(lrow + e);
+                visit(x.x); visit(x.y); visit(x.z); visit(x.w);
+            }
+        } else {
+            for (int e = tid; e < V; e += kCutThreads)
+                visit(lrow[e]);
+        }
+        __syncthreads();
+        // Thread t owns the four buckets nb-1-4t .. nb-4-4t (descending), so
+        // an exclusive scan in thread order is the mass ranked above them.
+        unsigned long long h[4] = {0, 0, 0, 0}, own = 0;
+        if (4 * tid < nb) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                h[k] = s_hist[nb - 1 - 4 * tid - k];
+                own += h[k];
+            }
+        }
+        const unsigned long long incl = wave_incl_scan_u64(own);
+        if (lane == 63)
+            s_wsum[wave] = incl;
+        if (tid == 0)
+            s_digit = -1;
+        __syncthreads();
+        unsigned long long above = incl - own;
+        unsigned long long total = 0;
+        for (int w = 0; w < kCutWaves; ++w) {
+            const unsigned long long t = s_wsum[w];
+            if (w < wave)
+                above += t;
+            total += t;
+        }
+        if (pass == 0) {
+            // keep iff mass ranked above < top_p * total; at least one unit
+            const double x = (double)top_p * (double)total;
+            tgt = (unsigned long long)__builtin_ceil(x);
+            if (tgt < 1)
+                tgt = 1;
+        }
+        unsigned long long run = carry + above;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (run < tgt && run + h[k] >= tgt) {
+                s_digit = nb - 1 - 4 * tid - k;
+                s_carry = run;
+                s_found = h[k];
+            }
+            run += h[k];
+        }
+        __syncthreads();
+        const int d = s_digit;
+        if (d < 0) {  // unreachable for finite rows: leave the row uncut
+            if (tid == 0)
+                *out = RowCut{-__builtin_inff(), 0, -1.0};
+            return;
+        }
+        prefix = (prefix << (pass == 2 ? 8 : 12)) | (uint32_t)d;
+        carry = s_carry;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const unsigned long long kept = s_carry + s_found;
+        *out = RowCut{key_logit(prefix), 0, kCutScale / (double)kept};
+    }
 }
 
 // Loads this thread's four consecutive entries tid*4 .. tid*4+3 of a
@@ -272,8 +470,9 @@ template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
 {
     __shared__ float s_M[16];
-    __shared__ double s_Z[16];
+    __shared__ double s_Z[16];   // 1 / (kept) row mass
     __shared__ int s_A[16];
+    __shared__ float s_tau[16];
     __shared__ double s_ratio[16];
     __shared__ int s_acc[16];
     __shared__ int s_n;
@@ -319,15 +518,25 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         const double Z = wave_sum_f64(zloc);
         const int A = wave_min_i32(aloc);
         if (lane == 0) {
+            float tau = -__builtin_inff();
+            double invZ = 1.0 / Z;
+            if (p.row_cut) {
+                const RowCut rc = static_cast<const RowCut *>(p.row_cut)[(size_t)b * K1 + i];
+                if (rc.inv_p > 0.0) {
+                    tau = rc.tau;
+                    invZ = rc.inv_p;
+                }
+            }
             s_M[i] = M;
-            s_Z[i] = Z;
+            s_Z[i] = invZ;
             s_A[i] = A;
+            s_tau[i] = tau;
         }
     }
     __syncthreads();
     // 2. Acceptance tests u_i * q_i(x_i) < p~_i(x_i).
     if (tid < K) {
-        const double a = target_prob(rx.lx, x, s_M[tid], 1.0 / s_Z[tid], tp, s_A[tid]);
+        const double a = target_prob(rx.lx, x, s_M[tid], s_Z[tid], tp, s_A[tid], s_tau[tid]);
         const double c = (double)rx.qx;
         s_acc[tid] = ((double)u * c < a) ? 1 : 0;
         s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
@@ -346,8 +555,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     const int n = s_n;
     const bool residual = n < K;
     const float M = s_M[n];
-    const double invZ = 1.0 / s_Z[n];
+    const double invZ = s_Z[n];
     const int arg = s_A[n];
+    const float tau = s_tau[n];
 
     // 3. Mass of this sub-chunk: residual (or bonus) weights and plain
     //    target mass.
@@ -360,7 +570,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     double sw = 0.0, sp = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, tp, arg);
+        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, tp, arg, tau);
         sp += pj;
         if (residual) {
             const double r = pj - (double)qv[k];
@@ -393,6 +603,8 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         ss.inv_t = tp.inv;
         ss.greedy = tp.greedy ? 1 : 0;
         ss.arg = arg;
+        ss.tau = tau;
+        ss.pad = 0;
         static_cast<SeqState *>(p.seq_state)[b] = ss;
     }
     if (sub == 0 && p.accept_prob && tid < K)
@@ -507,7 +719,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     double seg = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        wv[k] = weight(lv[k], qv[k], base + e0 + k, M, invZ, use_resid, tp, ss.arg);
+        wv[k] = weight(lv[k], qv[k], base + e0 + k, M, invZ, use_resid, tp, ss.arg, ss.tau);
         seg += wv[k];
     }
     // Exclusive prefix of the run sums across the workgroup.
@@ -575,12 +787,17 @@ hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
     const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
     const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
     const dim3 g3((unsigned)p.B);
+    const dim3 gc((unsigned)(p.B * (p.K + 1)));
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
+        if (p.row_cut)
+            hipLaunchKernelGGL(sv_sample_cut_kernel<true>, gc, dim3(kCutThreads), 0, stream, p);
         hipLaunchKernelGGL(sv_sample_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
+        if (p.row_cut)
+            hipLaunchKernelGGL(sv_sample_cut_kernel<false>, gc, dim3(kCutThreads), 0, stream, p);
         hipLaunchKernelGGL(sv_sample_decide_kernel<false>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
     }

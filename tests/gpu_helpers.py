@@ -85,7 +85,7 @@ def upload_sample(s: W.SampleInputs):
     }
 
 
-def run_sample(s: W.SampleInputs, t=None, ws=None, temperature=None):
+def run_sample(s: W.SampleInputs, t=None, ws=None, temperature=None, top_p=None):
     if t is None:
         t = upload_sample(s)
     d = dev()
@@ -95,18 +95,20 @@ def run_sample(s: W.SampleInputs, t=None, ws=None, temperature=None):
     if ws is None:
         ws = sv.alloc_workspace(sv.sample_workspace_size(s.B, s.K, s.V), d)
     temp = None if temperature is None else torch.from_numpy(np.asarray(temperature, np.float32)).to(d)
+    cut = None if top_p is None else torch.from_numpy(np.asarray(top_p, np.float32)).to(d)
     sv.spec_verify_sample(t["logits"], t["probs"], t["tokens"], t["u"], n, toks, ws, accept_prob=ap,
-                          temperature=temp)
+                          temperature=temp, top_p=cut)
     torch.cuda.synchronize()
     return n.cpu().numpy(), toks.cpu().numpy(), ap.cpu().numpy()
 
 
-def compare_sampler(s: W.SampleInputs, n_gpu, toks_gpu, ref=None, temperature=None):
+def compare_sampler(s: W.SampleInputs, n_gpu, toks_gpu, ref=None, temperature=None, top_p=None):
     """Bit-exact comparison except from the first position the oracle decided
     within 1e-6 of its threshold.  Returns (mismatches, flagged)."""
     if ref is None:
         ref = oracle.sample(s.target_logits, s.draft_probs, s.draft_tokens, s.uniforms,
-                            temperature=None if temperature is None else np.asarray(temperature, np.float32))
+                            temperature=None if temperature is None else np.asarray(temperature, np.float32),
+                            top_p=None if top_p is None else np.asarray(top_p, np.float32))
     mism, flagged = 0, 0
     for b in range(s.B):
         k = int(ref["near_pos"][b])

@@ -94,9 +94,11 @@ def test_sample_argument_checks():
     assert L.spec_verify_sample(p + 2, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
     # the temperature variant: same checks, plus the temperature array's alignment
     ex = L.spec_verify_sample_ex
-    assert ex(None, p, p, p, p, p, p, None, 2, 3, 100, p, 1 << 14, None) == 1
-    assert ex(p, p, p, p, None, p, p, None, 2, 16, 100, p, 1 << 14, None) == 2
-    assert ex(p, p, p, p, p + 1, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
+    assert ex(None, p, p, p, p, None, p, p, None, 2, 3, 100, p, 1 << 14, None) == 1
+    assert ex(p, p, p, p, None, None, p, p, None, 2, 16, 100, p, 1 << 14, None) == 2
+    assert ex(p, p, p, p, p + 1, None, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
+    assert ex(p, p, p, p, None, p + 2, p, p, None, 2, 3, 100, p, 1 << 14, None) == 5
+    assert ex(p, p, p, p, None, p, p, p, None, 2, 3, 1 << 20, p, 1 << 30, None) == 3
 
 
 def test_workspace_queries():

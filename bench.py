@@ -295,10 +295,23 @@ def main():
     pages_scratch = torch.empty_like(lens_scratch)
     rollback_ms = timed_launches(lambda i: sv.spec_verify_rollback(n_acc, lens_scratch, s.K, pages_in_use=pages_scratch,
                                                                    stream=stream), args.steps)
+    n_plain = n_acc.clone()  # accepted counts of the plain sampler (for its algorithmic bytes)
+    # The sampler alone, back to back: plain, and with a target temperature
+    # and top-p cut per sequence (0.7 and 0.9, the draft rows as given).
+    samp_b2b_ms = timed_launches(lambda i: sv.spec_verify_sample(
+        sets[i % copies]["logits"], sets[i % copies]["probs"], sets[i % copies]["tokens"], sets[i % copies]["u"],
+        n_acc, toks, ws_s, stream=stream), args.steps)
+    temp_t = torch.full((s.B,), 0.7, dtype=torch.float32, device=dev)
+    cut_t = torch.full((s.B,), 0.9, dtype=torch.float32, device=dev)
+    samp_tp_ms = timed_launches(lambda i: sv.spec_verify_sample(
+        sets[i % copies]["logits"], sets[i % copies]["probs"], sets[i % copies]["tokens"], sets[i % copies]["u"],
+        n_acc, toks, ws_s, stream=stream, temperature=temp_t, top_p=cut_t), args.steps)
+    print("# sampler %.1f us, with temperature + top-p %.1f us" % (samp_b2b_ms * 1e3, samp_tp_ms * 1e3),
+          file=sys.stderr, flush=True)
     ap_bytes = 2 * k_new.numel() * (4 + {W.KV_F32: 4, W.KV_BF16: 2, W.KV_FP8_E4M3: 1}[a.kv_dtype]) + 4 * a.B * (a.T + 1)
     print("# append %.1f us, rollback %.1f us" % (append_ms * 1e3, rollback_ms * 1e3), file=sys.stderr, flush=True)
     hev.close()
-    n_rej = int((n_acc.cpu().numpy() < s.K).sum())
+    n_rej = int((n_plain.cpu().numpy() < s.K).sum())
     samp_bytes = W.sample_algorithmic_bytes(s, n_rej)
 
     attn_gbs = attn_bytes / (main_ms * 1e-3) / 1e9
@@ -336,6 +349,8 @@ def main():
         "attn_us": float(attn_ms.mean() * 1e3),
         "attn_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
         "sample_us": float(samp_ms.mean() * 1e3),
+        "sample_us_back_to_back": float(samp_b2b_ms * 1e3),
+        "sample_temp_topp_us_back_to_back": float(samp_tp_ms * 1e3),
         "kv_append_us_per_layer": float(append_ms * 1e3),
         "kv_append_bytes_per_layer": int(ap_bytes),
         "rollback_us": float(rollback_ms * 1e3),

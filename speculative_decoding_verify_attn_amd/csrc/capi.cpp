@@ -3,6 +3,7 @@
 // Nothing here reads device memory, synchronises, or allocates.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -94,6 +95,8 @@ SamplePlan plan_sample(int B, int K, int V)
     off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
     pl.off_cut = off;
     off = align256(off + (size_t)B * (K + 1) * kRowCutBytes);
+    pl.off_part = off;  // top-p: partial coarse histograms per chunk
+    off = align256(off + (size_t)B * (K + 1) * pl.nchunk * kCutCoarse * 8);
     pl.total = off;
     return pl;
 }
@@ -349,6 +352,7 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.row_x = ws + pl.off_rowx;
     p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
     p.row_cut = top_p ? ws + pl.off_cut : nullptr;
+    p.cut_part = reinterpret_cast<unsigned long long *>(ws + pl.off_part);
     p.B = B;
     p.K = K;
     p.V = V;

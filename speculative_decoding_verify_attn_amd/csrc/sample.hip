@@ -33,16 +33,16 @@
 // taken as the draft's actual distribution); T <= 0 is the greedy limit,
 // all mass on the first maximal logit of the row.
 //
-// Top-p (same section): with a per-sequence top_p < 1 a fourth launch, cut,
-// runs between rowstats and decide, one 1024-thread workgroup per target
-// row.  Tokens are ranked by logit; a token is kept iff the mass ranked
+// Top-p (same section): with a per-sequence top_p < 1 the cut runs between
+// rowstats and decide.  Tokens are ranked by logit; a token is kept iff the mass ranked
 // strictly above it is below top_p (the top logit always kept), and p~ is
-// renormalised over the kept set.  The cut is a radix select over an
-// order-preserving 32-bit key of the logit, 12 + 12 + 8 bits in three passes
-// over the (cache-resident) row, histogramming the masses exp((l - M) / T) in
-// 2^-43 fixed point with LDS integer atomics, so the result does not depend
-// on the order of the additions.  Its output per row is the cut logit tau
-// (every l >= tau is kept) and 1 / kept mass.
+// renormalised over the kept set.  The masses exp((l - M) / T) are summed in
+// 2^-43 fixed point with LDS integer atomics, so nothing depends on the order
+// of the additions: a coarse histogram over (M - l) / T finds the bucket
+// holding the cut, its entries are gathered into LDS, and a radix select on
+// an order-preserving 32-bit key of the logit finds the cut exactly.  The
+// output per row is the cut logit tau (every l >= tau is kept) and
+// 1 / kept mass.
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -281,10 +281,14 @@ __device__ __forceinline__ double weight(float l, float q, int j, float M, doubl
 
 // ---------------------------------------------------------------- top-p cut
 
-constexpr int kCutThreads = 1024;
+constexpr int kCutThreads = 1024;      // cut (select) kernel: one workgroup per row
 constexpr int kCutWaves = kCutThreads / kWave;
-constexpr int kCutBuckets = 4096;       // 12-bit digits (the last pass uses 8)
-constexpr double kCutScale = 8796093022208.0;  // 2^43: masses <= 1 per entry, V < 2^20
+constexpr int kCutDigit = 4096;        // 12-bit key digits (the last pass uses 8)
+constexpr int kCutCap = 8192;          // entries of the crossing bucket held in LDS
+constexpr int kCutBatch = 8;           // row loads in flight per thread
+constexpr float kCutSpan = 45.0f;      // 2^t * 2^43 rounds to 0 below t = -44.5
+constexpr float kCutPerUnit = kCutCoarse / kCutSpan;
+constexpr double kCutScale = 8796093022208.0;  // 2^43
 
 // Order-preserving key of a float: larger logit, larger key; -0 takes the
 // key of +0, as the two compare equal.
@@ -301,16 +305,40 @@ __device__ __forceinline__ float key_logit(uint32_t k)
     return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// exp((l - M) / T) to about one fp32 ulp (as target_prob_fast), in 2^-43
-// fixed point, rounded to nearest.
-__device__ __forceinline__ uint64_t cut_mass(float l, float M, double inv)
+// Tempered log2-mass of an entry relative to the row maximum,
+// t = (l - M) log2(e) / T <= 0, with the constant split in two floats.
+__device__ __forceinline__ float cut_t(float l, float M, const Temp &tp)
 {
-    const double a = ((double)l - (double)M) * inv;
-    if (!(a > -31.0))
-        return 0;  // rounds to 0 at 2^-43 (and -inf entries)
-    const float hi = (float)a;
-    const double lo = a - (double)hi;
-    return (uint64_t)__builtin_rint((double)expf(hi) * (1.0 + lo) * kCutScale);
+    const float dv = l - M;
+    return __builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo);
+}
+
+// Coarse bucket of t: kCutCoarse equal steps over (-45, 0], bucket 0 holding
+// the largest logits; -1 below the span (and for -inf / NaN).  Never
+// decreases as the logit decreases.
+__device__ __forceinline__ int cut_bucket(float t)
+{
+    if (!(t > -kCutSpan))
+        return -1;
+    const int bk = (int)(-t * kCutPerUnit);
+    return bk > kCutCoarse - 1 ? kCutCoarse - 1 : bk;
+}
+
+// 2^t in 2^-43 fixed point, rounded half up, from the hardware exp2: the
+// float's 24-bit significand shifted into place (exact integer steps).
+__device__ __forceinline__ uint64_t cut_mass(float t)
+{
+    const uint32_t bits = __builtin_bit_cast(uint32_t, __builtin_amdgcn_exp2f(t));
+    const int E = (int)((bits >> 23) & 0xFFu);
+    if (E == 0)
+        return 0;  // zero or subnormal: far below 2^-43
+    const uint64_t m = (bits & 0x7FFFFFu) | 0x800000u;
+    const int sh = E - 107;  // value = m * 2^(E - 150), times 2^43
+    if (sh >= 0)
+        return m << sh;
+    if (sh < -24)
+        return 0;
+    return (m + (1ull << (-sh - 1))) >> (-sh);
 }
 
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
@@ -325,127 +353,393 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
     return v;
 }
 
+// Streams entries [begin, end) of a row through f, NT threads, kCutBatch
+// loads in flight per thread; on the float4 path begin and end are multiples
+// of 4.  Entries past the end read -inf.
+template <bool VEC, int NT, typename F>
+__device__ __forceinline__ void cut_stream(const float *row, int begin, int end, F &&f)
+{
+    const int tid = threadIdx.x;
+    const float ninf = -__builtin_inff();
+    if constexpr (VEC) {
+        for (int base = begin; base < end; base += NT * 4 * kCutBatch) {
+            float4 x[kCutBatch];
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                const int e = base + (k * NT + tid) * 4;
+                x[k] = e < end ? *reinterpret_cast<const float4 *>(row + e) : make_float4(ninf, ninf, ninf, ninf);
+            }
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                f(x[k].x);
+                f(x[k].y);
+                f(x[k].z);
+                f(x[k].w);
+            }
+        }
+    } else {
+        for (int base = begin; base < end; base += NT * kCutBatch) {
+            float x[kCutBatch];
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                const int e = base + k * NT + tid;
+                x[k] = e < end ? row[e] : ninf;
+            }
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k)
+                f(x[k]);
+        }
+    }
+}
+
+// Whether row `row` is cut, and its maximum (from the chunk statistics;
+// wave 0 of the calling workgroup reduces them into *s_M).
+__device__ __forceinline__ bool cut_active(const SampleParams &p, int b, const Temp &tp)
+{
+    return !tp.greedy && p.top_p[b] < 1.0f;  // NaN or >= 1: no cut
+}
+
+__device__ __forceinline__ void cut_row_max(const SampleParams &p, int row, float *s_M)
+{
+    if (threadIdx.x < kWave) {
+        const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)row * p.nchunk;
+        float m = -__builtin_inff();
+        for (int c = threadIdx.x; c < p.nchunk; c += kWave)
+            m = fmaxf(m, st[c].m);
+        m = wave_max_f32(m);
+        if (threadIdx.x == 0)
+            *s_M = m;
+    }
+}
+
+// Coarse histogram, part 1: grid (vocabulary chunk x row), shaped as the
+// rowstats pass (its chunk loads are issued before the row maximum is
+// read); each workgroup histograms the masses of its chunk over the coarse
+// buckets in LDS and stores that partial histogram.
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_cut_hist_kernel(SampleParams p)
+{
+    __shared__ unsigned long long s_hist[kCutCoarse];
+    __shared__ float s_M;
+    const int row = blockIdx.x / p.nchunk;
+    const int chunk = blockIdx.x - row * p.nchunk;
+    const int b = row / (p.K + 1);
+    const Temp tp = temp_of(p, b);
+    if (!cut_active(p, b, tp))
+        return;  // uniform across the workgroup
+    const int base = chunk * kSampleChunk;
+    float v[kPer];
+    load_chunk<VEC>(p.logits + (size_t)row * p.V + base, min(kSampleChunk, p.V - base), -__builtin_inff(), v);
+    cut_row_max(p, row, &s_M);
+    for (int i = threadIdx.x; i < kCutCoarse; i += kSampleThreads)
+        s_hist[i] = 0;
+    __syncthreads();
+    const float M = s_M;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const float t = cut_t(v[k], M, tp);
+        const int bk = cut_bucket(t);
+        if (bk >= 0) {
+            const uint64_t w = cut_mass(t);
+            if (w)
+                atomicAdd(&s_hist[bk], (unsigned long long)w);
+        }
+    }
+    __syncthreads();
+    unsigned long long *part = p.cut_part + ((size_t)row * p.nchunk + chunk) * kCutCoarse;
+    for (int i = threadIdx.x; i < kCutCoarse; i += kSampleThreads)
+        part[i] = s_hist[i];
+}
+
+struct CutShared {
+    unsigned long long wsum[kCutWaves];
+    unsigned long long carry, found;
+    int digit, cnt;
+    float M;
+};
+
+// The crossing bucket of a mass histogram: visiting the buckets in rank
+// order (rank r is bucket r, or bucket nb-1-r when `descending`), the one
+// at which the mass ranked before it, plus `carry`, is below tgt and with it
+// reaches tgt.  Thread t owns ranks 4t .. 4t+3; one block scan.  Leaves the
+// bucket in cs.digit (-1 if none), the mass ranked before it (carry
+// included) in cs.carry and its own mass in cs.found.  With tgt = 0 the
+// target is first set to max(1, ceil(top_p * total)).  Returns the target.
+// Every thread of the workgroup calls it.
+__device__ __forceinline__ unsigned long long cut_cross(const unsigned long long *hist, int nb, bool descending,
+                                                        unsigned long long carry, unsigned long long tgt,
+                                                        float top_p, CutShared &cs)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    unsigned long long h[4] = {0, 0, 0, 0}, own = 0;
+    int bk[4] = {0, 0, 0, 0};
+    if (4 * tid < nb) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bk[k] = descending ? nb - 1 - 4 * tid - k : 4 * tid + k;
+            h[k] = hist[bk[k]];
+            own += h[k];
+        }
+    }
+    const unsigned long long incl = wave_incl_scan_u64(own);
+    if (lane == 63)
+        cs.wsum[wave] = incl;
+    if (tid == 0)
+        cs.digit = -1;
+    __syncthreads();
+    unsigned long long above = incl - own, total = 0;
+#pragma unroll
+    for (int w = 0; w < kCutWaves; ++w) {
+        const unsigned long long t = cs.wsum[w];
+        if (w < wave)
+            above += t;
+        total += t;
+    }
+    if (tgt == 0) {
+        // a token is kept iff the mass ranked above it is < top_p * total
+        tgt = (unsigned long long)__builtin_ceil((double)top_p * (double)total);
+        if (tgt < 1)
+            tgt = 1;
+    }
+    unsigned long long run = carry + above;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (run < tgt && run + h[k] >= tgt) {
+            cs.digit = bk[k];
+            cs.carry = run;
+            cs.found = h[k];
+        }
+        run += h[k];
+    }
+    __syncthreads();
+    return tgt;
+}
+
+// Streams one vocabulary chunk of a row through f with the 64 lanes of one
+// wave, kCutBatch loads in flight per lane; entries past the end read -inf.
+template <bool VEC, typename F>
+__device__ __forceinline__ void cut_stream_chunk(const float *row, int base, int n, F &&f)
+{
+    const int lane = threadIdx.x & 63;
+    const float ninf = -__builtin_inff();
+    if constexpr (VEC) {
+        for (int off = 0; off < n; off += kWave * 4 * kCutBatch) {
+            float4 x[kCutBatch];
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                const int e = off + (k * kWave + lane) * 4;
+                x[k] = e < n ? *reinterpret_cast<const float4 *>(row + base + e) : make_float4(ninf, ninf, ninf, ninf);
+            }
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                f(x[k].x);
+                f(x[k].y);
+                f(x[k].z);
+                f(x[k].w);
+            }
+        }
+    } else {
+        for (int off = 0; off < n; off += kWave * kCutBatch) {
+            float x[kCutBatch];
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k) {
+                const int e = off + k * kWave + lane;
+                x[k] = e < n ? row[base + e] : ninf;
+            }
+#pragma unroll
+            for (int k = 0; k < kCutBatch; ++k)
+                f(x[k]);
+        }
+    }
+}
+
+constexpr int kCutDirect = 512;  // up to this many candidates: rank them directly
+static_assert(2 * kCutDirect + 2 * (kCutThreads / kWave) <= kCutDigit, "direct ranking scratch fits in s_hist");
+
+// Part 2, one workgroup per row: sums the partial histograms (exact integer
+// sums), finds the coarse bucket d0 holding the cut, and gathers the entries
+// of d0 into LDS (each wave takes whole chunks; a chunk whose partial
+// histogram has no mass in d0 holds no entry that matters and is skipped).
+// The exact cut among the candidates: with at most kCutDirect of them each
+// is ranked directly (the mass of the candidates with a larger key); with
+// more, a radix select on their keys (12 + 12 + 8 bits).  Should d0 hold
+// more than kCutCap entries, the digit passes stream the row instead,
+// filtered to d0.  All masses are the fixed-point ones of part 1.
 template <bool VEC>
 __global__ __launch_bounds__(kCutThreads) void sv_sample_cut_kernel(SampleParams p)
 {
-    __shared__ unsigned long long s_hist[kCutBuckets];
-    __shared__ unsigned long long s_wsum[kCutWaves];
-    __shared__ int s_digit;
-    __shared__ unsigned long long s_carry, s_found;
+    __shared__ unsigned long long s_hist[kCutDigit];
+    __shared__ float s_cand[kCutCap];
+    __shared__ CutShared cs;
 
     const int row = blockIdx.x;
-    const int K1 = p.K + 1;
-    const int b = row / K1;
+    const int b = row / (p.K + 1);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    RowCut* out = static_cast<RowCut *>(p.row_cut) + row;
+    RowCut *out = static_cast<RowCut *>(p.row_cut) + row;
     const Temp tp = temp_of(p, b);
-    const float top_p = p.top_p[b];
-    if (tp.greedy || !(top_p < 1.0f)) {  // uniform across the workgroup
+    if (!cut_active(p, b, tp)) {  // uniform across the workgroup
         if (tid == 0)
             *out = RowCut{-__builtin_inff(), 0, -1.0};
         return;
     }
-    // Row maximum from the chunk statistics.
-    if (wave == 0) {
-        const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)row * p.nchunk;
-        float m = -__builtin_inff();
-        for (int c = lane; c < p.nchunk; c += kWave)
-            m = fmaxf(m, st[c].m);
-        m = wave_max_f32(m);
-        if (lane == 0)
-            s_hist[0] = __builtin_bit_cast(uint32_t, m);
+    const float top_p = p.top_p[b];
+    const int nchunk = p.nchunk;
+    const unsigned long long *part = p.cut_part + (size_t)row * nchunk * kCutCoarse;
+    cut_row_max(p, row, &cs.M);
+    for (int i = tid; i < kCutCoarse; i += kCutThreads)
+        s_hist[i] = 0;
+    if (tid == 0)
+        cs.cnt = 0;
+    __syncthreads();
+    {
+        // two threads per bucket, each summing every other chunk, eight
+        // loads in flight
+        constexpr int kLanesPerBucket = kCutThreads / kCutCoarse;
+        const int bk = tid % kCutCoarse, c0 = tid / kCutCoarse;
+        unsigned long long h = 0;
+        for (int c = c0; c < nchunk; c += 8 * kLanesPerBucket) {
+            unsigned long long x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int cc = c + j * kLanesPerBucket;
+                x[j] = cc < nchunk ? part[(size_t)cc * kCutCoarse + bk] : 0ull;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                h += x[j];
+        }
+        if (h)
+            atomicAdd(&s_hist[bk], h);
     }
     __syncthreads();
-    const float M = __builtin_bit_cast(float, (uint32_t)s_hist[0]);
-    __syncthreads();
+    const float M = cs.M;
     const float *lrow = p.logits + (size_t)row * p.V;
     const int V = p.V;
 
-    uint32_t prefix = 0;        // key bits fixed so far
-    unsigned long long carry = 0, tgt = 0;
-    // pass 0: bits 31..20; pass 1: bits 19..8; pass 2: bits 7..0
+    const unsigned long long tgt = cut_cross(s_hist, kCutCoarse, false, 0, 0, top_p, cs);
+    const int d0 = cs.digit;
+    const unsigned long long carry0 = cs.carry;
+    if (d0 < 0) {  // unreachable for rows with a finite maximum: leave the row uncut
+        if (tid == 0)
+            *out = RowCut{-__builtin_inff(), 0, -1.0};
+        return;
+    }
+
+    // Gather the entries of d0 (those of zero mass included: they add nothing).
+    for (int c = wave; c < nchunk; c += kCutWaves) {
+        if (part[(size_t)c * kCutCoarse + d0] == 0)
+            continue;  // uniform across the wave
+        const int base = c * kSampleChunk;
+        cut_stream_chunk<VEC>(lrow, base, min(kSampleChunk, V - base), [&](float l) {
+            if (cut_bucket(cut_t(l, M, tp)) == d0) {
+                const int slot = atomicAdd(&cs.cnt, 1);
+                if (slot < kCutCap)
+                    s_cand[slot] = l;
+            }
+        });
+    }
+    __syncthreads();
+    const int cnt = cs.cnt;
+
+    if (cnt <= kCutDirect) {
+        // Candidate i is kept iff carry0 + (mass of candidates with a larger
+        // key) < tgt; the cut is the smallest kept key.
+        uint32_t ki = 0xFFFFFFFFu;
+        unsigned long long wi = 0;
+        bool kept = false;
+        if (tid < cnt) {
+            const float l = s_cand[tid];
+            ki = logit_key(l);
+            wi = cut_mass(cut_t(l, M, tp));
+        }
+        // keys and masses side by side in s_hist: [2i] key, [2i+1] mass
+        if (tid < cnt) {
+            s_hist[2 * tid] = ki;
+            s_hist[2 * tid + 1] = wi;
+        }
+        __syncthreads();
+        if (tid < cnt) {
+            unsigned long long above = 0;
+            for (int j = 0; j < cnt; ++j) {
+                const uint32_t kj = (uint32_t)s_hist[2 * j];
+                if (kj > ki)
+                    above += s_hist[2 * j + 1];
+            }
+            kept = carry0 + above < tgt;
+        }
+        const uint32_t kmin = kept ? ki : 0xFFFFFFFFu;
+        const unsigned long long wk = kept ? wi : 0ull;
+        // block reductions: smallest kept key, kept mass
+        uint32_t m = kmin;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            m = min(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        const unsigned long long ws = wave_incl_scan_u64(wk);
+        __syncthreads();  // s_hist reads above are done
+        if (lane == 63) {
+            s_hist[2 * kCutDirect + wave] = ws;  // scratch past the candidates' slots
+            s_hist[2 * kCutDirect + kCutWaves + wave] = m;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            unsigned long long kept_mass = carry0;
+            uint32_t kcut = 0xFFFFFFFFu;
+            for (int w = 0; w < kCutWaves; ++w) {
+                kept_mass += s_hist[2 * kCutDirect + w];
+                kcut = min(kcut, (uint32_t)s_hist[2 * kCutDirect + kCutWaves + w]);
+            }
+            if (kcut == 0xFFFFFFFFu || kept_mass == 0)
+                *out = RowCut{-__builtin_inff(), 0, -1.0};  // unreachable: the top candidate is kept
+            else
+                *out = RowCut{key_logit(kcut), 0, kCutScale / (double)kept_mass};
+        }
+        return;
+    }
+
+    const bool in_lds = cnt <= kCutCap;
+    unsigned long long carry = carry0;
+    uint32_t prefix = 0;
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-        const int nb = pass == 2 ? 256 : kCutBuckets;
+        const int nb = pass == 2 ? 256 : kCutDigit;
         const int pshift = pass == 0 ? 32 : (pass == 1 ? 20 : 8);  // bits above the digit
         for (int i = tid; i < nb; i += kCutThreads)
             s_hist[i] = 0;
         __syncthreads();
-        auto visit = [&](float l) {
+        auto visit = [&](float l, float t) {
             const uint32_t k = logit_key(l);
             if (pshift < 32 && (k >> pshift) != prefix)
                 return;
-            const uint64_t w = cut_mass(l, M, tp.inv);
+            const uint64_t w = cut_mass(t);
             if (w)
                 atomicAdd(&s_hist[(k >> shift) & (uint32_t)(nb - 1)], (unsigned long long)w);
         };
-        if constexpr (VEC) {
-            for (int e = tid * 4; e < V; e += kCutThreads * 4) {
-                const float4 x = *reinterpret_cast<const float4 *>(lrow + e);
-                visit(x.x); visit(x.y); visit(x.z); visit(x.w);
+        if (in_lds) {
+            for (int i = tid; i < cnt; i += kCutThreads) {
+                const float l = s_cand[i];
+                visit(l, cut_t(l, M, tp));
             }
         } else {
-            for (int e = tid; e < V; e += kCutThreads)
-                visit(lrow[e]);
+            cut_stream<VEC, kCutThreads>(lrow, 0, V, [&](float l) {
+                const float t = cut_t(l, M, tp);
+                if (cut_bucket(t) == d0)
+                    visit(l, t);
+            });
         }
         __syncthreads();
-        // Thread t owns the four buckets nb-1-4t .. nb-4-4t (descending), so
-        // an exclusive scan in thread order is the mass ranked above them.
-        unsigned long long h[4] = {0, 0, 0, 0}, own = 0;
-        if (4 * tid < nb) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                h[k] = s_hist[nb - 1 - 4 * tid - k];
-                own += h[k];
-            }
-        }
-        const unsigned long long incl = wave_incl_scan_u64(own);
-        if (lane == 63)
-            s_wsum[wave] = incl;
-        if (tid == 0)
-            s_digit = -1;
-        __syncthreads();
-        unsigned long long above = incl - own;
-        unsigned long long total = 0;
-        for (int w = 0; w < kCutWaves; ++w) {
-            const unsigned long long t = s_wsum[w];
-            if (w < wave)
-                above += t;
-            total += t;
-        }
-        if (pass == 0) {
-            // keep iff mass ranked above < top_p * total; at least one unit
-            const double x = (double)top_p * (double)total;
-            tgt = (unsigned long long)__builtin_ceil(x);
-            if (tgt < 1)
-                tgt = 1;
-        }
-        unsigned long long run = carry + above;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (run < tgt && run + h[k] >= tgt) {
-                s_digit = nb - 1 - 4 * tid - k;
-                s_carry = run;
-                s_found = h[k];
-            }
-            run += h[k];
-        }
-        __syncthreads();
-        const int d = s_digit;
-        if (d < 0) {  // unreachable for finite rows: leave the row uncut
+        cut_cross(s_hist, nb, true, carry, tgt, top_p, cs);
+        const int d = cs.digit;
+        if (d < 0) {  // unreachable: the entries of d0 sum to its coarse mass
             if (tid == 0)
                 *out = RowCut{-__builtin_inff(), 0, -1.0};
             return;
         }
         prefix = (prefix << (pass == 2 ? 8 : 12)) | (uint32_t)d;
-        carry = s_carry;
-        __syncthreads();
+        carry = cs.carry;
     }
-    if (tid == 0) {
-        const unsigned long long kept = s_carry + s_found;
-        *out = RowCut{key_logit(prefix), 0, kCutScale / (double)kept};
-    }
+    if (tid == 0)
+        *out = RowCut{key_logit(prefix), 0, kCutScale / (double)(cs.carry + cs.found)};
 }
 
 // Loads this thread's four consecutive entries tid*4 .. tid*4+3 of a
@@ -788,16 +1082,21 @@ hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
     const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
     const dim3 g3((unsigned)p.B);
     const dim3 gc((unsigned)(p.B * (p.K + 1)));
+    const dim3 gh = g1;
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
-        if (p.row_cut)
+        if (p.row_cut) {
+            hipLaunchKernelGGL(sv_sample_cut_hist_kernel<true>, gh, block, 0, stream, p);
             hipLaunchKernelGGL(sv_sample_cut_kernel<true>, gc, dim3(kCutThreads), 0, stream, p);
+        }
         hipLaunchKernelGGL(sv_sample_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
-        if (p.row_cut)
+        if (p.row_cut) {
+            hipLaunchKernelGGL(sv_sample_cut_hist_kernel<false>, gh, block, 0, stream, p);
             hipLaunchKernelGGL(sv_sample_cut_kernel<false>, gc, dim3(kCutThreads), 0, stream, p);
+        }
         hipLaunchKernelGGL(sv_sample_decide_kernel<false>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
     }

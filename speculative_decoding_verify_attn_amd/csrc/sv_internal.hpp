@@ -65,6 +65,7 @@ struct SampleParams {
     float *accept_prob;      // [B][K] or null
     void *seq_state;         // [B] {accepted count, row max, 1/row sum, 1/T, greedy, argmax, cut}
     void *row_cut;           // [B*(K+1)] {cut logit, 1/kept mass}, or null without top_p
+    unsigned long long *cut_part;  // [B*(K+1)][nchunk][kCutCoarse] partial coarse histograms
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
     void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}
@@ -74,12 +75,13 @@ struct SampleParams {
 
 struct SamplePlan {
     int nchunk;
-    size_t off_state, off_stats, off_rowx, off_mass, off_cut, total;
+    size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, total;
 };
 
 constexpr size_t kSeqStateBytes = 48;  // workspace bytes per sequence of the decide -> pick state
 constexpr size_t kRowCutBytes = 16;    // workspace bytes per target row of the top-p cut
 constexpr int kCutMaxV = 1 << 20;      // the cut's fixed-point masses need V < 2^20
+constexpr int kCutCoarse = 512;        // coarse buckets of the top-p cut
 
 SamplePlan plan_sample(int B, int K, int V);
 hipError_t launch_sample(const SampleParams &p, hipStream_t stream);

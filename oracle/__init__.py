@@ -50,6 +50,14 @@ def _bind(lib):
         [c.c_void_p] * 6 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
     lib.oracle_top_p.restype = c.c_int
     lib.oracle_top_p.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_double, c.c_void_p]
+    lib.oracle_attn_rows_tree.restype = c.c_int
+    lib.oracle_attn_rows_tree.argtypes = (
+        [c.c_void_p] * 8 + [c.c_int] * 8 + [c.c_double, c.c_void_p, c.c_int64, c.c_void_p, c.c_int])
+    lib.oracle_sample_tree.restype = c.c_int
+    lib.oracle_sample_tree.argtypes = (
+        [c.c_void_p] * 5 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
+    lib.oracle_tree_masks.restype = c.c_int
+    lib.oracle_tree_masks.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_void_p]
     lib.oracle_target_row.restype = None
     lib.oracle_target_row.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_void_p]
     lib.oracle_encode_bf16.restype = c.c_uint16
@@ -117,7 +125,7 @@ def softmax_row(logits: np.ndarray) -> np.ndarray:
 
 
 def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=None,
-         v_scale=None, sm_scale=None, rows=None, block_size=16, nthreads=None):
+         v_scale=None, sm_scale=None, rows=None, block_size=16, nthreads=None, tree_mask=None):
     """Verify attention by the plain definition, in fp64.
 
     q [B,T,Hq,d] fp32; k_cache/v_cache [num_blocks,16,Hkv,d] as stored
@@ -125,6 +133,8 @@ def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=No
     [num_blocks] fp32 for E4M3; block_table [B,max_blocks] int32;
     context_lens [B] int32 (the T new positions included).
     rows: optional flat row indices (b*T + t)*Hq + h.
+    tree_mask: optional [B,T] uint32 ancestor sets of a BFS-ordered draft
+    tree (bit j of row t: node j is visible to node t); None is the chain.
     Returns [B,T,Hq,d] fp64, or [len(rows), d] when rows is given.
     """
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -148,9 +158,11 @@ def attn(q, k_cache, v_cache, block_table, context_lens, *, kv_dtype, k_scale=No
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
         nrows = rows_arr.shape[0]
         out = np.empty((nrows, d), dtype=np.float64)
-    rc = _load().oracle_attn_rows(
+    tm = None if tree_mask is None else np.ascontiguousarray(tree_mask, dtype=np.uint32)
+    assert tm is None or tm.shape == (B, T)
+    rc = _load().oracle_attn_rows_tree(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_table), _ptr(context_lens), B, T, Hq, Hkv, d, block_size, max_blocks,
+        _ptr(block_table), _ptr(context_lens), _ptr(tm), B, T, Hq, Hkv, d, block_size, max_blocks,
         int(kv_dtype), float(sm_scale), _ptr(rows_arr), nrows, _ptr(out),
         nthreads or default_threads())
     if rc != 0:
@@ -195,6 +207,51 @@ def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6,
         _ptr(res["near_pos"]), _ptr(res["resid_mass"]), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_sample rejected its arguments")
+    return res
+
+
+def tree_masks(parents):
+    """Ancestor sets [B,N] uint32 of BFS-ordered trees given by parents [B,N]
+    (parents[:,0] < 0; 0 <= parents[:,c] < c): bit j of masks[b,c] is set iff
+    node j is on the path from the root to node c, c included."""
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    B, N = par.shape
+    out = np.empty((B, N), dtype=np.uint32)
+    if _load().oracle_tree_masks(_ptr(par), B, N, _ptr(out)) != 0:
+        raise ValueError("oracle_tree_masks rejected the parents")
+    return out
+
+
+def sample_tree(target_logits, draft_probs, tokens, parents, uniforms, *, near_eps=1e-6, nthreads=None):
+    """Tree verification sampler (recursive rejection over siblings), fp64.
+
+    target_logits, draft_probs [B,N,V] f32 (row c: the target after node c's
+    path; the draft distribution c's children were drawn from); tokens,
+    parents [B,N] int32 (BFS order, parents[:,0] = -1); uniforms [B,N] f32
+    (column c >= 1 tests node c, column 0 drives the final draw).
+    Returns a dict: num_accepted [B], out_tokens [B,N], path [B,N] (accepted
+    node ids), accept_ratio [B,N] (NaN where untested), near_pos [B].
+    """
+    tl = np.ascontiguousarray(target_logits, dtype=np.float32)
+    dp = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    tk = np.ascontiguousarray(tokens, dtype=np.int32)
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B, N, V = tl.shape
+    assert dp.shape == (B, N, V) and tk.shape == (B, N) and par.shape == (B, N) and u.shape == (B, N)
+    res = {
+        "num_accepted": np.empty(B, dtype=np.int32),
+        "out_tokens": np.empty((B, N), dtype=np.int32),
+        "path": np.empty((B, N), dtype=np.int32),
+        "accept_ratio": np.empty((B, N), dtype=np.float64),
+        "near_pos": np.empty(B, dtype=np.int32),
+    }
+    rc = _load().oracle_sample_tree(
+        _ptr(tl), _ptr(dp), _ptr(tk), _ptr(par), _ptr(u), B, N, V, float(near_eps),
+        _ptr(res["num_accepted"]), _ptr(res["out_tokens"]), _ptr(res["path"]), _ptr(res["accept_ratio"]),
+        _ptr(res["near_pos"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_sample_tree rejected its arguments")
     return res
 
 

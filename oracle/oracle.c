@@ -86,6 +86,7 @@ typedef struct {
     int64_t nrows;
     double *out;
     double *scratch; /* per thread: score[max_blocks*block_size] */
+    const uint32_t *tree_mask; /* [B][T] ancestor sets, or NULL for the chain */
 } attn_job;
 
 /*
@@ -114,6 +115,9 @@ static void attn_one_row(const attn_job *J, int64_t row, double *score, double *
     const int64_t L = J->context_lens[b];
     const int64_t n_vis = L - T + 1 + t;
     const float *qrow = J->q + row * d;
+    /* tree verification: row t sees the prefix and the tree nodes j with bit
+     * j of its ancestor set (itself included) */
+    const uint32_t anc = J->tree_mask ? J->tree_mask[b * T + t] : 0u;
 
     for (int c = 0; c < d; ++c)
         o[c] = 0.0;
@@ -125,6 +129,10 @@ static void attn_one_row(const attn_job *J, int64_t row, double *score, double *
 
     double smax = -INFINITY;
     for (int64_t p = 0; p < n_vis; ++p) {
+        if (J->tree_mask && p >= L - T && !((anc >> (p - (L - T))) & 1u)) {
+            score[p] = -INFINITY;
+            continue;
+        }
         int64_t blk = J->block_table[b * J->max_blocks + p / bs];
         int64_t slot = p % bs;
         int64_t base = ((blk * bs + slot) * Hkv + g) * d;
@@ -142,6 +150,8 @@ static void attn_one_row(const attn_job *J, int64_t row, double *score, double *
         denom += score[p];
     }
     for (int64_t p = 0; p < n_vis; ++p) {
+        if (J->tree_mask && p >= L - T && !((anc >> (p - (L - T))) & 1u))
+            continue; /* a tree node outside A(t) */
         int64_t blk = J->block_table[b * J->max_blocks + p / bs];
         int64_t slot = p % bs;
         int64_t base = ((blk * bs + slot) * Hkv + g) * d;
@@ -177,12 +187,41 @@ static void *attn_worker(void *arg)
  * in order (nrows must then be B*T*Hq).  Returns 0, or -1 on bad arguments.
  * Rows with no visible position (L_b < T - t) are NaN.
  */
+int oracle_attn_rows_tree(const float *q, const void *k_cache, const void *v_cache,
+                          const float *k_scale, const float *v_scale,
+                          const int32_t *block_table, const int32_t *context_lens,
+                          const uint32_t *tree_mask,
+                          int B, int T, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks, int kv_dtype, double sm_scale,
+                          const int64_t *rows, int64_t nrows, double *out, int nthreads);
+
 int oracle_attn_rows(const float *q, const void *k_cache, const void *v_cache,
                      const float *k_scale, const float *v_scale,
                      const int32_t *block_table, const int32_t *context_lens,
                      int B, int T, int Hq, int Hkv, int d, int block_size,
                      int max_blocks, int kv_dtype, double sm_scale,
                      const int64_t *rows, int64_t nrows, double *out, int nthreads)
+{
+    return oracle_attn_rows_tree(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, NULL, B, T,
+                                 Hq, Hkv, d, block_size, max_blocks, kv_dtype, sm_scale, rows, nrows, out,
+                                 nthreads);
+}
+
+/*
+ * Tree verification ([KV] 8.2 and Q14): the T = N tree nodes are flattened
+ * in BFS order into the last N cache positions; node t may attend to the
+ * prefix (positions 0 .. L_b - N - 1) and to the nodes of its ancestor set
+ * A(t), itself included: bit j of tree_mask[b][t] set iff node j is in A(t).
+ * Every set must hold t and no node after t (ancestors precede in BFS order),
+ * else -1.  tree_mask == NULL is the chain, A(t) = {0 .. t}.
+ */
+int oracle_attn_rows_tree(const float *q, const void *k_cache, const void *v_cache,
+                          const float *k_scale, const float *v_scale,
+                          const int32_t *block_table, const int32_t *context_lens,
+                          const uint32_t *tree_mask,
+                          int B, int T, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks, int kv_dtype, double sm_scale,
+                          const int64_t *rows, int64_t nrows, double *out, int nthreads)
 {
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return -1;
@@ -193,9 +232,19 @@ int oracle_attn_rows(const float *q, const void *k_cache, const void *v_cache,
     for (int b = 0; b < B; ++b)
         if (context_lens[b] < 0 || context_lens[b] > (int64_t)max_blocks * block_size)
             return -1;
+    if (tree_mask) {
+        if (T > 32)
+            return -1;
+        for (int b = 0; b < B; ++b)
+            for (int t = 0; t < T; ++t) {
+                uint32_t m = tree_mask[b * T + t];
+                if (!((m >> t) & 1u) || (t < 31 && (m >> (t + 1))))
+                    return -1;
+            }
+    }
     attn_job J = {q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                   B, T, Hq, Hkv, d, block_size, max_blocks, kv_dtype, sm_scale,
-                  rows, nrows, out, NULL};
+                  rows, nrows, out, NULL, tree_mask};
     if (nthreads < 1)
         nthreads = 1;
     if (nthreads > 256)
@@ -571,6 +620,242 @@ int oracle_sample_tp(const float *target_logits, const float *draft_probs,
             rc = -1;
     }
     return rc;
+}
+
+/* ------------------------------------------------------------ tree sampler
+ *
+ * Verification of a draft tree ([KV] 8.2 and Q14: the tree's nodes are
+ * flattened in BFS order and scored by one target forward; exact
+ * verification keeps the rejection rule of [SD] 3.1 and [KV] 7.1-7.3).
+ *
+ * Inputs per sequence: N nodes in BFS order, parents[0] < 0 (the root is the
+ * last committed token), 0 <= parents[c] < c otherwise; tokens[c] the token
+ * of node c (tokens[0] unused); target row c = logits after node c's path;
+ * draft row c = the distribution q_c the children of c were drawn from;
+ * uniforms[c] (c >= 1) tests node c, uniforms[0] drives the final draw.
+ *
+ * Reading for siblings (the pages name exact tree verification but give no
+ * rule for several candidates at one node): the children of the current
+ * node are tried in BFS order, each against the target as left by the
+ * siblings rejected before it, the residual step of [SD] 3.1 applied once
+ * per rejection: p_1 = p, p_{k+1} = norm(max(0, p_k - q)).  Unnormalised,
+ * p_k = max(0, p - C_{k-1} q) / Z_k with C_0 = 0, Z_1 = 1,
+ * Z_k = sum_j max(0, p_j - C_{k-1} q_j) and C_k = C_{k-1} + Z_k.  Child k with
+ * token x is accepted iff u * q(x) < p_k(x); the walk then moves to it.  When
+ * no child is accepted (or there is none) the final token is drawn from the
+ * current residual max(0, p - C q) (p itself at a leaf or with no
+ * rejection), by the same inverse CDF and fallbacks as the chain.  A chain
+ * tree is exactly the chain sampler.
+ */
+typedef struct {
+    const float *target_logits, *draft_probs, *uniforms;
+    const int32_t *tokens, *parents;
+    int B, N;
+    int64_t V;
+    double near_eps;
+    int32_t *num_accepted, *out_tokens, *path, *near_pos;
+    double *accept_ratio;
+} tree_job;
+
+static void tree_one(const tree_job *J, int b, double *p, double *w)
+{
+    const int N = J->N;
+    const int64_t V = J->V;
+    const int32_t *par = J->parents + (int64_t)b * N;
+    const int32_t *tok = J->tokens + (int64_t)b * N;
+    const float *u = J->uniforms + (int64_t)b * N;
+    int32_t *ot = J->out_tokens + (int64_t)b * N;
+    int32_t *pth = J->path + (int64_t)b * N;
+    double *ar = J->accept_ratio + (int64_t)b * N;
+    for (int i = 0; i < N; ++i) {
+        ot[i] = -1;
+        pth[i] = -1;
+        ar[i] = NAN;
+    }
+    int node = 0, depth = 0, near = -1;
+    double C = 0.0;
+    const float *qrow = NULL;
+    for (;;) {
+        oracle_softmax_row(J->target_logits + ((int64_t)b * N + node) * V, V, p);
+        qrow = J->draft_probs + ((int64_t)b * N + node) * V;
+        C = 0.0;
+        int next = -1;
+        for (int c = node + 1; c < N; ++c) {
+            if (par[c] != node)
+                continue;
+            const int x = tok[c];
+            const double qx = (double)qrow[x];
+            double a;
+            double Z = 1.0;
+            if (C == 0.0) {
+                a = p[x];
+            } else {
+                Z = 0.0;
+                for (int64_t j = 0; j < V; ++j) {
+                    double r = p[j] - C * (double)qrow[j];
+                    Z += r > 0.0 ? r : 0.0;
+                }
+                double rx = p[x] - C * qx;
+                a = (Z > 0.0 && rx > 0.0) ? rx / Z : 0.0;
+            }
+            const double ratio = qx > 0.0 ? fmin(1.0, a / qx) : (a > 0.0 ? 1.0 : 0.0);
+            ar[c] = ratio;
+            if (near < 0 && fabs((double)u[c] - ratio) < J->near_eps)
+                near = depth;
+            if ((double)u[c] * qx < a) {
+                next = c;
+                break;
+            }
+            C += Z;
+        }
+        if (next < 0)
+            break;
+        pth[depth] = next;
+        ot[depth] = tok[next];
+        ++depth;
+        node = next;
+    }
+
+    double S = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+        double r = C == 0.0 ? p[j] : p[j] - C * (double)qrow[j];
+        w[j] = r > 0.0 ? r : 0.0;
+        S += w[j];
+    }
+    if (S == 0.0) {
+        for (int64_t j = 0; j < V; ++j) {
+            w[j] = p[j];
+            S += w[j];
+        }
+    }
+    double target = (double)u[0] * S;
+    double Cum = 0.0, Cprev = 0.0;
+    int64_t pick = -1;
+    for (int64_t j = 0; j < V; ++j) {
+        Cprev = Cum;
+        Cum += w[j];
+        if (Cum > target) {
+            pick = j;
+            break;
+        }
+    }
+    if (pick < 0) {
+        for (int64_t j = V - 1; j >= 0; --j)
+            if (w[j] > 0.0) {
+                pick = j;
+                break;
+            }
+        Cprev = S;
+        Cum = S;
+    }
+    if (near < 0 && (fabs((double)u[0] - Cprev / S) < J->near_eps || fabs((double)u[0] - Cum / S) < J->near_eps))
+        near = depth;
+    ot[depth] = (int32_t)pick;
+    J->num_accepted[b] = depth;
+    J->near_pos[b] = near;
+}
+
+typedef struct {
+    const tree_job *job;
+    int begin, end;
+} tree_slice;
+
+static void *tree_worker(void *arg)
+{
+    const tree_slice *S = (const tree_slice *)arg;
+    double *p = (double *)malloc(sizeof(double) * (size_t)S->job->V);
+    double *w = (double *)malloc(sizeof(double) * (size_t)S->job->V);
+    if (!p || !w) {
+        free(p);
+        free(w);
+        return (void *)1;
+    }
+    for (int b = S->begin; b < S->end; ++b)
+        tree_one(S->job, b, p, w);
+    free(p);
+    free(w);
+    return NULL;
+}
+
+/*
+ * The tree sampler for B sequences of N nodes each.  Shapes: target_logits
+ * and draft_probs [B][N][V], tokens, parents, uniforms [B][N].  Outputs:
+ * num_accepted [B] (accepted nodes, the root not counted), out_tokens [B][N]
+ * (the accepted nodes' tokens, then the drawn token, then -1), path [B][N]
+ * (the accepted node ids in order, then -1), accept_ratio [B][N] (the
+ * min(1, p_k/q) of every tested node, NaN elsewhere), near_pos [B] (first
+ * output position decided within near_eps, else -1).  Returns 0, or -1 on
+ * bad arguments (a parent that does not precede its child, a token out of
+ * range).
+ */
+int oracle_sample_tree(const float *target_logits, const float *draft_probs, const int32_t *tokens,
+                       const int32_t *parents, const float *uniforms, int B, int N, int64_t V, double near_eps,
+                       int32_t *num_accepted, int32_t *out_tokens, int32_t *path, double *accept_ratio,
+                       int32_t *near_pos, int nthreads)
+{
+    if (!target_logits || !draft_probs || !tokens || !parents || !uniforms || !num_accepted || !out_tokens ||
+        !path || !accept_ratio || !near_pos)
+        return -1;
+    if (B < 1 || N < 1 || V < 1)
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        if (parents[(int64_t)b * N] >= 0)
+            return -1;
+        for (int c = 1; c < N; ++c) {
+            int32_t pc = parents[(int64_t)b * N + c], x = tokens[(int64_t)b * N + c];
+            if (pc < 0 || pc >= c || x < 0 || x >= V)
+                return -1;
+        }
+    }
+    tree_job J = {target_logits, draft_probs, uniforms, tokens, parents, B, N, V, near_eps,
+                  num_accepted, out_tokens, path, near_pos, accept_ratio};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > B)
+        nthreads = B;
+    pthread_t th[256];
+    tree_slice sl[256];
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &J;
+        sl[i].begin = (int)((int64_t)B * i / nthreads);
+        sl[i].end = (int)((int64_t)B * (i + 1) / nthreads);
+    }
+    if (nthreads == 1)
+        return tree_worker(&sl[0]) ? -1 : 0;
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i)
+        pthread_create(&th[i], NULL, tree_worker, &sl[i]);
+    for (int i = 0; i < nthreads; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r)
+            rc = -1;
+    }
+    return rc;
+}
+
+/* Ancestor sets of a BFS-ordered tree ([KV] 8.2, Q14): bit j of masks[c] is
+ * set iff node j lies on the path from the root to c, c included.  Returns
+ * 0, or -1 if a parent does not precede its child or N > 32. */
+int oracle_tree_masks(const int32_t *parents, int B, int N, uint32_t *masks)
+{
+    if (N < 1 || N > 32)
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * N;
+        uint32_t *m = masks + (int64_t)b * N;
+        if (par[0] >= 0)
+            return -1;
+        m[0] = 1u;
+        for (int c = 1; c < N; ++c) {
+            if (par[c] < 0 || par[c] >= c)
+                return -1;
+            m[c] = m[par[c]] | (1u << c);
+        }
+    }
+    return 0;
 }
 
 /* ------------------------------------------------------- paged append / rollback

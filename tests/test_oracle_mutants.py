@@ -15,6 +15,7 @@ from . import test_oracle_sampler as TS
 from . import test_oracle_kvcache as TK
 from . import test_oracle_temperature as TT
 from . import test_oracle_topp as TP
+from . import test_oracle_tree as TR
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -52,6 +53,12 @@ TEMP_PINS = [
 TOPP_PINS = [
     TP.test_cut_matches_the_ascending_cumsum_recipe, TP.test_cut_matches_the_threshold_form_with_ties,
     TP.test_vanishing_top_p_is_the_greedy_limit, TP.test_full_or_nan_top_p_changes_nothing,
+]
+
+TREE_PINS = [
+    TR.test_chain_masks_are_the_causal_mask, lambda: TR.test_node_sees_exactly_prefix_and_root_path("binary3"),
+    TR.test_chain_tree_is_the_chain_sampler, TR.test_third_sibling_ratio_worked_example,
+    lambda: TR.test_exact_law_of_recursive_rejection(3),
 ]
 
 # (name, original text, replacement, pins expected to catch it)
@@ -97,6 +104,15 @@ MUTANTS = [
     ("top-p may drop the top group", "const int keep = first || above < top_p;", "const int keep = above < top_p;", TOPP_PINS),
     ("top-p counts the token itself", "const int keep = first || above < top_p;",
      "const int keep = first || above + mass < top_p;", TOPP_PINS),
+    ("tree: residual coefficient not accumulated", "            C += Z;\n        }\n        if (next < 0)",
+     "            C = Z;\n        }\n        if (next < 0)", TREE_PINS),
+    ("tree: siblings tested against p", "a = (Z > 0.0 && rx > 0.0) ? rx / Z : 0.0;", "a = p[x];", TREE_PINS),
+    ("tree: final draw ignores the rejections", "double r = C == 0.0 ? p[j] : p[j] - C * (double)qrow[j];",
+     "double r = p[j];", TREE_PINS),
+    ("tree: attention ignores the ancestor sets",
+     "!((anc >> (p - (L - T))) & 1u)) {\n            score[p] = -INFINITY;",
+     "0) {\n            score[p] = -INFINITY;", TREE_PINS),
+    ("tree: ancestor sets of the chain", "m[c] = m[par[c]] | (1u << c);", "m[c] = (2u << c) - 1u;", TREE_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

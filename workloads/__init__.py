@@ -49,7 +49,7 @@ CONFIGS = {
 }
 
 _STREAMS = ("perm", "ctx", "q", "k", "v", "logits", "noise", "noise_scale", "draft_draw", "uniforms",
-            "append", "accepted")
+            "append", "accepted", "tree")
 
 
 def streams(seed: int):
@@ -297,6 +297,80 @@ def make_sample_from_params(seed, B, K, V, target_sigma, noise, chunk_rows=64):
 def make_sample(name, seed=0):
     cfg = CONFIGS[name]
     return make_sample_from_params(seed, cfg["B"], cfg["K"], cfg["V"], cfg["target_sigma"], cfg["noise"])
+
+
+# ------------------------------------------------------------------- trees
+
+# Tree shapes for tree verification: children per node at each depth, in
+# BFS order (N = 1 + b1 + b1*b2 + ... <= 16 nodes).
+TREE_SHAPES = {
+    "chain5": (1, 1, 1, 1, 1),   # the chain of K = 5 drafts
+    "binary3": (2, 2, 2),        # 15 nodes
+    "wide5x2": (5, 2),           # 16 nodes: 5 first-token candidates, 2 continuations each
+    "top3-2-1": (3, 2, 1),       # 16 nodes: a static top-k tree
+}
+
+
+def tree_parents(branching):
+    """BFS parent array of the tree with branching[d] children per node at
+    depth d; parents[0] = -1 (the root: the last committed token)."""
+    parents = [-1]
+    level = [0]
+    for bf in branching:
+        nxt = []
+        for u in level:
+            for _ in range(bf):
+                parents.append(u)
+                nxt.append(len(parents) - 1)
+        level = nxt
+    return np.array(parents, dtype=np.int32)
+
+
+@dataclass
+class TreeInputs:
+    target_logits: np.ndarray  # [B,N,V] float32: row c = target after node c's path
+    draft_probs: np.ndarray    # [B,N,V] float32: row c = the draft distribution of c's children
+    tokens: np.ndarray         # [B,N] int32 (column 0 unused)
+    parents: np.ndarray        # [B,N] int32, BFS order, parents[:,0] = -1
+    uniforms: np.ndarray       # [B,N] float32 in [0,1): column c tests node c, column 0 the final draw
+
+    @property
+    def B(self):
+        return self.target_logits.shape[0]
+
+    @property
+    def N(self):
+        return self.target_logits.shape[1]
+
+    @property
+    def V(self):
+        return self.target_logits.shape[2]
+
+
+def make_tree(seed, B, parents, V, target_sigma=3.0, noise=1.0):
+    """Tree verification inputs: target logits ~ N(0, sigma^2) per node; each
+    node's draft row q_c = softmax(target_c + noise * N(0,1)) (fp64, stored
+    fp32); every child's token drawn independently from its parent's draft
+    row; uniforms U[0,1).  parents: [N] (one shape for the batch) or [B,N]."""
+    st = streams(seed)
+    par = np.asarray(parents, dtype=np.int32)
+    if par.ndim == 1:
+        par = np.broadcast_to(par, (B, par.shape[0]))
+    par = np.ascontiguousarray(par)
+    N = par.shape[1]
+    target = st["logits"].standard_normal((B, N, V), dtype=np.float32) * np.float32(target_sigma)
+    z = st["noise"].standard_normal((B, N, V), dtype=np.float32).astype(np.float64)
+    qd = _softmax64(target.astype(np.float64) + float(noise) * z)
+    draft = qd.astype(np.float32)
+    tokens = np.zeros((B, N), dtype=np.int32)
+    cdf = np.cumsum(qd, axis=-1)
+    u = st["tree"].random((B, N))
+    for b in range(B):
+        for c in range(1, N):
+            row = cdf[b, par[b, c]]
+            tokens[b, c] = min(int(np.searchsorted(row, u[b, c] * row[-1], side="right")), V - 1)
+    uniforms = _uniform01(st["uniforms"], (B, N))
+    return TreeInputs(target_logits=target, draft_probs=draft, tokens=tokens, parents=par, uniforms=uniforms)
 
 
 # --------------------------------------------------------------- byte models

@@ -76,7 +76,8 @@ MUTANTS = [
     ("e4m3 subnormal exponent", "return sign * ldexp((double)m / 8.0, -6);",
      "return sign * ldexp((double)m / 8.0, -7);", ATTN_PINS),
     ("residual sign flipped", "double r = p[j] - (double)qrow[j];", "double r = (double)qrow[j] - p[j];", SAMPLE_PINS),
-    ("residual is p itself", "w[j] = r > 0.0 ? r : 0.0;", "w[j] = p[j];", SAMPLE_PINS),
+    ("residual is p itself", "double r = p[j] - (double)qrow[j];\n            w[j] = r > 0.0 ? r : 0.0;",
+     "double r = p[j] - (double)qrow[j];\n            w[j] = p[j];", SAMPLE_PINS),
     ("acceptance ratio inverted", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * a < c)) {", SAMPLE_PINS),
     ("non-strict acceptance", "if (!((double)u[i] * c < a)) {", "if (!((double)u[i] * c <= a)) {", SAMPLE_PINS),
     ("inverse CDF >=", "if (C > target) {", "if (C >= target) {", SAMPLE_PINS),

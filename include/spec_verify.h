@@ -167,6 +167,27 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
  * (optional, NULL to skip) receives min(1, p_i(x_i)/q_i(x_i)) for every i.
  * 1 <= K <= 15; V >= 1.  workspace as for attention.
  * ------------------------------------------------------------------------ */
+/* Tree verification attention ("KV Cache + Speculative Decoding" 8.2 and
+ * Q14): the T nodes of a draft tree, flattened in BFS order, are the T verify
+ * rows; their K/V occupy the last T cache positions (L_b - T .. L_b - 1, in
+ * node order).  Node t attends to the prefix (positions < L_b - T) and to the
+ * nodes of its ancestor set: bit j of tree_mask[b*T + t] set iff node j lies
+ * on the path from the root (node 0) to t, t itself included.
+ *   tree_mask: [B][T] uint32, device memory, 4-byte aligned.  Every set must
+ *   hold its own node and no later node (ancestors precede in BFS order);
+ *   other sets give undefined (but memory-safe) results.  The chain's sets
+ *   {0..t} make this spec_verify_attn_ex exactly.
+ * Every other argument, the workspace and the errors as spec_verify_attn_ex
+ * (T <= 16, T*Hq/Hkv <= 64). */
+int spec_verify_attn_tree(const float *q, const void *k_cache, const void *v_cache,
+                          const float *k_scale, const float *v_scale,
+                          const int32_t *block_table, const int32_t *context_lens,
+                          const uint32_t *tree_mask, float *out,
+                          int B, int T, int Hq, int Hkv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int kv_dtype,
+                          float sm_scale, void *workspace, size_t workspace_bytes,
+                          void *stream, int algo, int blocks_per_split);
+
 size_t spec_verify_sample_workspace_size(int B, int K, int V);
 
 int spec_verify_sample(const float *target_logits, const float *draft_probs,

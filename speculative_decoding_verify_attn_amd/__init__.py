@@ -61,6 +61,8 @@ def lib():
         L.spec_verify_attn.argtypes = attn_args
         L.spec_verify_attn_ex.restype = I
         L.spec_verify_attn_ex.argtypes = attn_args + [I, I, P]
+        L.spec_verify_attn_tree.restype = I
+        L.spec_verify_attn_tree.argtypes = [P] * 9 + [I] * 9 + [F, P, S, P, I, I]
         L.spec_verify_sample_workspace_size.restype = S
         L.spec_verify_sample_workspace_size.argtypes = [I] * 3
         L.spec_verify_sample.restype = I
@@ -151,6 +153,26 @@ def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, worksp
         _ptr(context_lens), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
         kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, q.device), int(algo), int(blocks_per_split), main_done_event))
+    return out
+
+
+def spec_verify_attn_tree(q, k_cache, v_cache, block_table, context_lens, tree_mask, out, workspace, *,
+                          k_scale=None, v_scale=None, sm_scale=None, kv_dtype=None, stream=None,
+                          algo=SV_ATTN_AUTO, blocks_per_split=0):
+    """Tree verification attention (see include/spec_verify.h): as
+    spec_verify_attn with T = the tree's BFS-ordered nodes and tree_mask
+    [B,T] int32/uint32 ancestor sets (bit j of row t: node j visible to t)."""
+    B, T, Hq, d = q.shape
+    num_blocks, bs, Hkv, d2 = k_cache.shape
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    if sm_scale is None:
+        sm_scale = 1.0 / (d ** 0.5)
+    _check("spec_verify_attn_tree", lib().spec_verify_attn_tree(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(tree_mask), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
+        kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, q.device), int(algo), int(blocks_per_split)))
     return out
 
 

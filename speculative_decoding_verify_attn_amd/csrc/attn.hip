@@ -283,6 +283,21 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(%0)" 
 // All-ones if V slot `key` (absolute position) is part of the context,
 // else zero: slots past the context may hold anything, NaN included, and
 // are cleared with a mask (no branch) before they reach the PV product.
+// Visibility of cache position pos to a verify row whose ancestor set is
+// `anc`: the prefix (pos < L - T) always; verify position L - T + j (tree
+// node j in BFS order) iff bit j of the set is set.  The chain's row t has
+// the set {0 .. t}, i.e. the causal mask.
+__device__ __forceinline__ bool key_visible(int pos, int L, int T, uint32_t anc)
+{
+    const int rel = pos - (L - T);
+    return rel < 0 || (rel < T && ((anc >> rel) & 1u));
+}
+
+__device__ __forceinline__ uint32_t row_ancestors(const AttnParams &p, int b, int t)
+{
+    return p.tree_mask ? p.tree_mask[(size_t)b * p.T + t] : ((2u << t) - 1u);
+}
+
 __device__ __forceinline__ uint32_t slot_keep(bool tail, int key, int L)
 {
     return (tail && key >= L) ? 0u : 0xFFFFFFFFu;
@@ -459,11 +474,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
     for (int i = tid; i < avail; i += NT)
         s_pages[i] = clamp_block(trow[i], p.num_blocks);
     float4 qraw[RG][NDC][2];
+    uint32_t anc[RG];  // ancestor set of the lane's verify row (padding rows see everything)
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
         const int row = rt * 16 + l16;
         const bool valid = row < TG;
         const int t = valid ? row / G : 0;
+        anc[rt] = valid ? row_ancestors(p, b, t) : 0xFFFFFFFFu;
         const int hh = valid ? row - t * G : 0;
         const float *src = p.q + (((size_t)b * T + t) * p.Hq + (size_t)g * G + hh) * D;
 #pragma unroll
@@ -486,11 +503,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
     // Q tile as the B operand of S^T = K Q^T (row = l16, eight dims), bf16,
     // pre-scaled into base-2 units.
     bf16x8 qf[RG][NDC];
-    int lim[RG];
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
-        const int row = rt * 16 + l16;
-        lim[rt] = L - T + (row < TG ? row / G : T - 1);
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
             const float sc = p.qscale;
@@ -665,13 +679,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
             ksc = *reinterpret_cast<const float *>(st + 2 * PG::PT + lane * 4);
             vsc = *reinterpret_cast<const float *>(st + 2 * PG::PT + 256 + lane * 4);
         }
-        // 4. Causal / length mask (only the last pages of a sequence need it).
+        // 4. Causal (or tree) / length mask (only the last pages of a
+        //    sequence need it).
         if (key0 + kBlock - 1 > L - T) {
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (key0 + q4 * 4 + i > lim[rt])
+                    if (!key_visible(key0 + q4 * 4 + i, L, T, anc[rt]))
                         s[rt][i] = ninf;
         }
         // 5. Online softmax.  The common path only checks that no score of
@@ -781,6 +796,7 @@ __global__ __launch_bounds__(kAttnThreads) void sv_attn_valu_kernel(AttnParams p
     __shared__ __attribute__((aligned(16))) float s_q[kMaxRows * OP];  // later: obuf
     __shared__ float s_k[kBlock * KP], s_v[kBlock * D], s_p[kMaxRows * (kBlock + 1)];
     __shared__ float s_alpha[kMaxRows], s_mrow[64], s_lrow[64];
+    __shared__ uint32_t s_anc[kMaxRows];
 
     UnitWork w;
     if (!decode_work(p, w))
@@ -795,6 +811,8 @@ __global__ __launch_bounds__(kAttnThreads) void sv_attn_valu_kernel(AttnParams p
         const int t = row / G, hh = row - t * G;
         s_q[row * OP + col] = p.q[(((size_t)w.b * T + t) * p.Hq + (size_t)w.g * G + hh) * D + col] * p.qscale;
     }
+    for (int row = tid; row < TG; row += kAttnThreads)
+        s_anc[row] = row_ancestors(p, w.b, row / G);
     float o[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k)
@@ -825,7 +843,7 @@ __global__ __launch_bounds__(kAttnThreads) void sv_attn_valu_kernel(AttnParams p
             for (int col = 0; col < D; ++col)
                 dot += s_q[row * OP + col] * s_k[key * KP + col];
             const int pos = lb * kBlock + key;
-            s_p[row * (kBlock + 1) + key] = (pos <= L - T + row / G) ? dot : ninf;
+            s_p[row * (kBlock + 1) + key] = key_visible(pos, L, T, s_anc[row]) ? dot : ninf;
         }
         __syncthreads();
         if (tid < TG) {

@@ -176,12 +176,13 @@ size_t spec_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int d, int
     return spec_verify_attn_workspace_size_ex(B, T, Hq, Hkv, d, max_blocks_per_seq, 0);
 }
 
-int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
-                        const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
-                        float *out, int B, int T, int Hq, int Hkv, int d, int block_size,
-                        int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale, void *workspace,
-                        size_t workspace_bytes, void *stream, int algo, int blocks_per_split,
-                        void *main_done_event)
+namespace {
+
+int attn_impl(const float *q, const void *k_cache, const void *v_cache, const float *k_scale, const float *v_scale,
+              const int32_t *block_table, const int32_t *context_lens, const uint32_t *tree_mask, float *out, int B,
+              int T, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq, int num_blocks, int kv_dtype,
+              float sm_scale, void *workspace, size_t workspace_bytes, void *stream, int algo, int blocks_per_split,
+              void *main_done_event)
 {
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(SV_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and out must be non-NULL");
@@ -220,8 +221,8 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
         return fail(SV_ERR_ALIGN, "q and out must be 16-byte aligned");
     if (!aligned(k_cache, fp8 ? 8 : 16) || !aligned(v_cache, fp8 ? 8 : 16))
         return fail(SV_ERR_ALIGN, "k_cache and v_cache must be %d-byte aligned", fp8 ? 8 : 16);
-    if (!aligned(block_table, 4) || !aligned(context_lens, 4))
-        return fail(SV_ERR_ALIGN, "block_table and context_lens must be 4-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (tree_mask && !aligned(tree_mask, 4)))
+        return fail(SV_ERR_ALIGN, "block_table, context_lens and tree_mask must be 4-byte aligned");
 
     const sv::AttnPlan pl = sv::plan_attention(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split);
     if (!workspace)
@@ -240,6 +241,7 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
     p.v_scale = v_scale;
     p.block_table = block_table;
     p.context_lens = context_lens;
+    p.tree_mask = tree_mask;
     p.out = out;
     p.part_o = reinterpret_cast<float *>(ws + pl.off_part_o);
     p.part_ml = reinterpret_cast<float *>(ws + pl.off_part_ml);
@@ -277,6 +279,33 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
     if (e != hipSuccess)
         return fail(SV_ERR_HIP, "split-merge launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                        const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
+                        float *out, int B, int T, int Hq, int Hkv, int d, int block_size,
+                        int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale, void *workspace,
+                        size_t workspace_bytes, void *stream, int algo, int blocks_per_split,
+                        void *main_done_event)
+{
+    return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, nullptr, out, B, T, Hq, Hkv,
+                     d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace, workspace_bytes,
+                     stream, algo, blocks_per_split, main_done_event);
+}
+
+int spec_verify_attn_tree(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                          const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
+                          const uint32_t *tree_mask, float *out, int B, int T, int Hq, int Hkv, int d,
+                          int block_size, int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale,
+                          void *workspace, size_t workspace_bytes, void *stream, int algo, int blocks_per_split)
+{
+    if (!tree_mask)
+        return fail(SV_ERR_NULL, "tree_mask must be non-NULL (spec_verify_attn is the chain)");
+    return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, tree_mask, out, B, T, Hq,
+                     Hkv, d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace,
+                     workspace_bytes, stream, algo, blocks_per_split, nullptr);
 }
 
 int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,

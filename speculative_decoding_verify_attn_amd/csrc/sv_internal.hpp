@@ -32,6 +32,7 @@ struct AttnParams {
     int max_splits;        // ceil(max_blocks / bps)
     int grid;              // workgroups launched (multiple of 8)
     float qscale;          // sm_scale * log2(e): scores are kept in base-2 units
+    const uint32_t *tree_mask;  // [B][T] ancestor sets of the verify rows, or null (the chain)
 };
 
 struct AttnPlan {

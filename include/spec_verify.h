@@ -225,6 +225,44 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs,
                           int B, int K, int V,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Tree verification sampler ("KV Cache + Speculative Decoding" 8.2: the draft
+ * tree's N nodes, flattened in BFS order, are scored by one target forward;
+ * exact verification keeps the rejection rule of "50 | Speculative
+ * Decoding" 3.1 and "KV Cache + Speculative Decoding" 7.1-7.3).
+ *   target_logits [B][N][V] f32: row c = target logits after node c's path
+ *     (node 0, the root, is the last committed token);
+ *   draft_probs   [B][N][V] f32: row c = the draft distribution the children
+ *     of node c were drawn from (rows of leaves are not read);
+ *   tokens  [B][N] i32: token of node c (column 0 unused), in [0, V);
+ *   parents [B][N] i32: BFS parents, parents[b][0] = -1, 0 <= parents[b][c] < c;
+ *   uniforms [B][N] f32 in [0,1): column c >= 1 tests node c, column 0 drives
+ *     the final draw.
+ * Rule: from the root, the children of the current node are tried in BFS
+ * order, each against the target as left by the siblings rejected before it
+ * (after k rejections p_{k+1} = norm(max(0, p_k - q)), the chain's residual
+ * step applied per rejected sibling; for the first child this is the chain's
+ * test u * q(x) < p(x)).  An accepted child becomes the current node; when
+ * no child is accepted, or the node is a leaf, the final token is drawn from
+ * the current residual (p itself if nothing was rejected) by the chain's
+ * inverse CDF.  With siblings drawn independently from their parent's draft
+ * row every emitted token follows the target.  A chain tree is
+ * spec_verify_sample exactly (uniforms remapped: column i+1 tests draft i,
+ * column 0 is the chain's last uniform).
+ * Outputs: num_accepted [B] (accepted nodes, the root not counted);
+ *   out_tokens [B][N] (the accepted nodes' tokens, the drawn token, then -1);
+ *   path [B][N] (the accepted node ids in order, then -1) -- the K/V of
+ *   these nodes are the ones the cache keeps; accept_prob [B][N] optional
+ *   (NULL ok): min(1, p_k(x)/q(x)) of every tested node, NaN elsewhere.
+ * Parents that break the BFS order are clamped into [0, c-1] (results
+ * undefined, memory-safe).  N <= 16.  Workspace:
+ * spec_verify_sample_tree_workspace_size(B, N, V) bytes, 256-byte aligned. */
+size_t spec_verify_sample_tree_workspace_size(int B, int N, int V);
+int spec_verify_sample_tree(const float *target_logits, const float *draft_probs,
+                            const int32_t *tokens, const int32_t *parents, const float *uniforms,
+                            int32_t *num_accepted, int32_t *out_tokens, int32_t *path,
+                            float *accept_prob, int B, int N, int V,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * spec_verify_kv_append: write the K/V of the T verify positions into the
  * paged cache, before spec_verify_attn.

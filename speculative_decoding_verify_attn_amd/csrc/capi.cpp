@@ -80,6 +80,23 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
     return pl;
 }
 
+TreePlan plan_sample_tree(int B, int N, int V)
+{
+    TreePlan pl{};
+    pl.nchunk = ceil_div(V, kSampleChunk);
+    size_t off = 0;
+    pl.off_state = off;
+    off = align256(off + (size_t)B * kSeqStateBytes);
+    pl.off_stats = off;
+    off = align256(off + (size_t)B * N * pl.nchunk * 16);
+    pl.off_mass = off;
+    off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
+    pl.off_coefs = off;
+    off = align256(off + (size_t)B * N * N * 16);
+    pl.total = off;
+    return pl;
+}
+
 SamplePlan plan_sample(int B, int K, int V)
 {
     SamplePlan pl{};
@@ -373,6 +390,8 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.uniforms = uniforms;
     p.temperature = temperature;
     p.top_p = top_p;
+    p.qrows = K;
+    p.tree = 0;
     p.num_accepted = num_accepted;
     p.out_tokens = out_tokens;
     p.accept_prob = accept_prob;
@@ -460,6 +479,71 @@ int spec_verify_rollback(const int32_t *num_accepted, int32_t *context_lens, int
                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SV_ERR_HIP, "rollback launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+
+size_t spec_verify_sample_tree_workspace_size(int B, int N, int V)
+{
+    if (B < 1 || N < 1 || N > 16 || V < 1 || V > sv::kMaxSampleChunks * sv::kSampleChunk)
+        return 0;
+    return sv::plan_sample_tree(B, N, V).total;
+}
+
+int spec_verify_sample_tree(const float *target_logits, const float *draft_probs, const int32_t *tokens,
+                            const int32_t *parents, const float *uniforms, int32_t *num_accepted,
+                            int32_t *out_tokens, int32_t *path, float *accept_prob, int B, int N, int V,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!target_logits || !draft_probs || !tokens || !parents || !uniforms || !num_accepted || !out_tokens || !path)
+        return fail(SV_ERR_NULL, "target_logits, draft_probs, tokens, parents, uniforms, num_accepted, out_tokens "
+                                 "and path must be non-NULL");
+    if (B < 1 || N < 1 || V < 1)
+        return fail(SV_ERR_SHAPE, "B, N and V must be >= 1 (got %d, %d, %d)", B, N, V);
+    if (N > 16)
+        return fail(SV_ERR_SHAPE, "N must be <= 16 (got %d)", N);
+    if (V > sv::kMaxSampleChunks * sv::kSampleChunk)
+        return fail(SV_ERR_UNSUPPORTED, "V must be <= %d (got %d)", sv::kMaxSampleChunks * sv::kSampleChunk, V);
+    if ((long long)B * N * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL ||
+        (long long)B * ((V + sv::kSampleSub - 1) / sv::kSampleSub) > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "B*N*ceil(V/%d) or B*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk,
+                    sv::kSampleSub);
+    if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(tokens, 4) || !aligned(parents, 4) ||
+        !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) || !aligned(path, 4) ||
+        (accept_prob && !aligned(accept_prob, 4)))
+        return fail(SV_ERR_ALIGN, "tree sampler arrays must be 4-byte aligned");
+    const sv::TreePlan pl = sv::plan_sample_tree(B, N, V);
+    if (!workspace)
+        return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.total);
+    if (!aligned(workspace, 256))
+        return fail(SV_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pl.total)
+        return fail(SV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.total);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    sv::SampleParams p{};
+    p.logits = target_logits;
+    p.probs = draft_probs;
+    p.tokens = tokens;
+    p.uniforms = uniforms;
+    p.num_accepted = num_accepted;
+    p.out_tokens = out_tokens;
+    p.accept_prob = accept_prob;
+    p.seq_state = ws + pl.off_state;
+    p.row_stats = ws + pl.off_stats;
+    p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
+    p.coefs = reinterpret_cast<double *>(ws + pl.off_coefs);
+    p.parents = parents;
+    p.path = path;
+    p.B = B;
+    p.K = N - 1;
+    p.V = V;
+    p.nchunk = pl.nchunk;
+    p.qrows = N;
+    p.tree = 1;
+    p.vec4 = (V % 4 == 0) && aligned(target_logits, 16) && aligned(draft_probs, 16);
+    const hipError_t e = sv::launch_sample_tree(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "tree sampler launch: %s", hipGetErrorString(e));
     return ok();
 }
 

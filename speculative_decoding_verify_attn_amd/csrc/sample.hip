@@ -65,16 +65,22 @@ struct RowX {
     float qx;
 };
 
-// What the draw of one sequence needs from the decide pass.
+// What the draw of one sequence needs from the decide pass: the final
+// token is drawn from max(0, p~ - coef * q) over target row `row` and draft
+// row `qrow` (coef = 0: p~ itself).
 struct SeqState {
-    int n;         // accepted drafts
-    float m;       // max logit of row n
-    double inv_z;  // 1 / (kept) sum_j exp((l_j - m) / T) of row n
+    double inv_z;  // 1 / (kept) sum_j exp((l_j - m) / T) of the target row
     double inv_t;  // 1 / T
+    double coef;   // residual coefficient: 1 after a chain rejection, C_k in a tree, 0 for a bonus
+    int n;         // accepted drafts (tree: accepted nodes)
     int greedy;    // T <= 0: all mass on the first maximal logit ...
     int arg;       // ... which is this index
-    float tau;     // top-p cut of row n: entries with l < tau have p~ = 0
-    int pad;
+    int row;       // target row of the draw within the sequence
+    int qrow;      // draft row of the draw within the sequence
+    int tree;      // 1: the decide pass already wrote every output but the drawn token
+    int ucol;      // column of the sequence's uniforms that drives the draw
+    float m;       // max logit of the target row
+    float tau;     // top-p cut of the row: entries with l < tau have p~ = 0
 };
 static_assert(sizeof(SeqState) <= kSeqStateBytes, "workspace slot of SeqState");
 
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     float v[kPer];
     load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
     // x_i's own entries, fetched while the chunk streams in.
-    const bool rec = chunk == 0 && i < K;
+    const bool rec = !p.tree && chunk == 0 && i < K;
     RowX rx{0.0f, 0.0f};
     if (rec) {
         const int x = clamp_token(p.tokens[(size_t)b * K + i], p.V);
@@ -267,15 +273,16 @@ __device__ __forceinline__ double target_prob(float l, int j, float M, double in
     return exp(((double)l - (double)M) * tp.inv) * invZ;
 }
 
-// Weight of entry j of the chosen row: the residual max(0, p~ - q) after a
-// rejection, p~ itself for the bonus row or the zero-mass fallback.
-__device__ __forceinline__ double weight(float l, float q, int j, float M, double invZ, bool residual, const Temp &tp,
+// Weight of entry j of the chosen row: the residual max(0, p~ - coef * q)
+// after a rejection (coef = 1 in the chain), p~ itself (coef = 0) for the
+// bonus row or the zero-mass fallback.
+__device__ __forceinline__ double weight(float l, float q, int j, float M, double invZ, double coef, const Temp &tp,
                                          int arg, float tau)
 {
     const double pj = target_prob_fast(l, j, M, invZ, tp, arg, tau);
-    if (!residual)
+    if (coef == 0.0)
         return pj;
-    const double r = pj - (double)q;
+    const double r = pj - coef * (double)q;
     return r > 0.0 ? r : 0.0;
 }
 
@@ -895,10 +902,14 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         ss.m = M;
         ss.inv_z = invZ;
         ss.inv_t = tp.inv;
+        ss.coef = residual ? 1.0 : 0.0;
         ss.greedy = tp.greedy ? 1 : 0;
         ss.arg = arg;
+        ss.row = n;
+        ss.qrow = residual ? n : 0;
+        ss.tree = 0;
+        ss.ucol = K;
         ss.tau = tau;
-        ss.pad = 0;
         static_cast<SeqState *>(p.seq_state)[b] = ss;
     }
     if (sub == 0 && p.accept_prob && tid < K)
@@ -925,15 +936,15 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const int nsub = (V + kSampleSub - 1) / kSampleSub;
     const SeqState ss = static_cast<const SeqState *>(p.seq_state)[b];
     const int n = ss.n;
-    const bool residual = n < K;
+    const bool residual = ss.coef > 0.0;
     const float M = ss.m;
     const double invZ = ss.inv_z;
     Temp tp;
     tp.greedy = ss.greedy != 0;
     tp.inv = ss.inv_t;
     tp.c_hi = tp.c_lo = 0.0f;  // (row sums are not recomputed here)
-    const float *lrow = p.logits + ((size_t)b * K1 + n) * V;
-    const float *qrow = p.probs + ((size_t)b * K + (residual ? n : 0)) * V;
+    const float *lrow = p.logits + ((size_t)b * K1 + ss.row) * V;
+    const float *qrow = p.probs + ((size_t)b * p.qrows + ss.qrow) * V;
 
     if (tid < kWave) {
         const double *gmass = p.sub_mass + (size_t)b * nsub * 2;
@@ -948,7 +959,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
             mode = 1;
             S = wave_sum_f64(sp);
         }
-        const double tgt = (double)p.uniforms[(size_t)b * K1 + K] * S;
+        const double tgt = (double)p.uniforms[(size_t)b * K1 + ss.ucol] * S;
         double carry = 0.0, cum = 0.0;
         int cstar = -1, lastpos = -1;
         double cum_last = 0.0;
@@ -1013,7 +1024,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     double seg = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        wv[k] = weight(lv[k], qv[k], base + e0 + k, M, invZ, use_resid, tp, ss.arg, ss.tau);
+        wv[k] = weight(lv[k], qv[k], base + e0 + k, M, invZ, use_resid ? ss.coef : 0.0, tp, ss.arg, ss.tau);
         seg += wv[k];
     }
     // Exclusive prefix of the run sums across the workgroup.
@@ -1051,6 +1062,13 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
         last = max(last, s_i[i]);
     const int token = (!take_last && best != 0x7FFFFFFF) ? best : last;
 
+    if (ss.tree) {
+        if (tid == 0) {
+            p.out_tokens[(size_t)b * K1 + n] = token;
+            p.num_accepted[b] = n;
+        }
+        return;
+    }
     if (tid < K1) {
         int32_t v;
         if (tid < n)
@@ -1061,6 +1079,305 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     }
     if (tid == 0)
         p.num_accepted[b] = n;
+}
+
+// ------------------------------------------------------------ tree verify
+//
+// A draft tree of N BFS-ordered nodes per sequence ("KV Cache + Speculative
+// Decoding" 8.2): target row c holds the logits after node c's path, draft
+// row c the distribution q_c that c's children were drawn from.  The walk
+// starts at the root; the children of the current node u are tried in
+// order, the k-th (k = 1, 2, ..) accepted iff
+//     u_c * q_u(x) < max(0, p_u(x) - C_{k-1} q_u(x)) / Z_k,
+// C_0 = 0, Z_1 = 1, Z_k = sum_j max(0, p_u(j) - C_{k-1} q_u(j)),
+// C_k = C_{k-1} + Z_k: the rejection step of the chain applied once per
+// rejected sibling (for k = 1 this is the chain's test).  The walk moves to
+// an accepted child; when none is accepted the final token is drawn from
+// max(0, p_u - C q_u) with C the coefficient reached (0 at a leaf: p_u).
+// C_k and Z_k depend only on node u's two rows, never on the drafts or
+// uniforms, so they are computed for every node before the walk:
+//   tree_resid  one 1024-thread workgroup per node with >= 2 children: for
+//               k = 1 .. m-1 a pass over the node's rows gives
+//               Z_{k+1} = sum_j max(0, p_u(j) - C_k q_u(j)) (fp64 block sum);
+//   tree_decide grid (1024-entry sub-chunk x sequence): every workgroup
+//               loads the gathered (logit, q) of each node's token, the row
+//               statistics and the coefficients in one round trip, walks the
+//               tree (one thread), and sums the final weights over its
+//               sub-chunk; the first one writes the path and the tokens;
+//   pick        the chain's draw, from the row and coefficient the walk left.
+
+// Row maximum and 1 / sum_j exp(l_j - M) of target row `row` (T = 1), merged
+// from the chunk statistics by one wave.
+__device__ __forceinline__ void tree_row_mz(const SampleParams &p, int row, float &M, double &invZ)
+{
+    const int lane = threadIdx.x & 63;
+    const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)row * p.nchunk;
+    float mloc = -__builtin_inff();
+    for (int c = lane; c < p.nchunk; c += kWave)
+        mloc = fmaxf(mloc, st[c].m);
+    M = wave_max_f32(mloc);
+    double zloc = 0.0;
+    for (int c = lane; c < p.nchunk; c += kWave) {
+        const RowStat r = st[c];
+        if (r.z > 0.0)
+            zloc += r.z * exp((double)r.m - (double)M);
+    }
+    invZ = 1.0 / wave_sum_f64(zloc);
+}
+
+__device__ __forceinline__ int tree_parent(const SampleParams &p, int b, int c)
+{
+    const int pc = p.parents[(size_t)b * (p.K + 1) + c];
+    return pc < 0 ? 0 : (pc >= c ? c - 1 : pc);  // out-of-contract parents stay in bounds
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kCutThreads) void sv_tree_resid_kernel(SampleParams p)
+{
+    __shared__ double s_red[kCutWaves];
+    __shared__ int s_m;
+    __shared__ float s_M;
+    __shared__ double s_iZ;
+    const int N = p.K + 1;
+    const int row = blockIdx.x;
+    const int b = row / N, u = row - b * N;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid == 0)
+        s_m = 0;
+    __syncthreads();
+    if (tid > u && tid < N && tree_parent(p, b, tid) == u)
+        atomicAdd(&s_m, 1);
+    if (wave == 0) {
+        float M;
+        double iZ;
+        tree_row_mz(p, row, M, iZ);
+        if (lane == 0) {
+            s_M = M;
+            s_iZ = iZ;
+        }
+    }
+    __syncthreads();
+    const int m = s_m;
+    if (m < 2)
+        return;  // uniform: C_1 = 1 is all a node with one child needs
+    const float M = s_M;
+    const double invZ = s_iZ;
+    const float *lrow = p.logits + (size_t)row * p.V;
+    const float *qrow = p.probs + (size_t)row * p.V;
+    const int V = p.V;
+    const Temp t1{false, 1.0, 0.0f, 0.0f};
+    double2 *cz = reinterpret_cast<double2 *>(p.coefs) + (size_t)row * N;
+    double C = 1.0;
+    for (int k = 1; k < m; ++k) {
+        double acc = 0.0;
+        auto add = [&](float l, float q, int j) {
+            const double r = target_prob_fast(l, j, M, invZ, t1, 0, -__builtin_inff()) - C * (double)q;
+            acc += r > 0.0 ? r : 0.0;
+        };
+        if constexpr (VEC) {
+            for (int base = 0; base < V; base += kCutThreads * 4 * 4) {
+                float4 lx[4], qx[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = base + (i * kCutThreads + tid) * 4;
+                    lx[i] = e < V ? *reinterpret_cast<const float4 *>(lrow + e)
+                                  : make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+                    qx[i] = e < V ? *reinterpret_cast<const float4 *>(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = base + (i * kCutThreads + tid) * 4;
+                    add(lx[i].x, qx[i].x, e);
+                    add(lx[i].y, qx[i].y, e + 1);
+                    add(lx[i].z, qx[i].z, e + 2);
+                    add(lx[i].w, qx[i].w, e + 3);
+                }
+            }
+        } else {
+            for (int e = tid; e < V; e += kCutThreads)
+                add(lrow[e], qrow[e], e);
+        }
+        acc = wave_sum_f64(acc);
+        if (lane == 0)
+            s_red[wave] = acc;
+        __syncthreads();
+        double Z = 0.0;
+#pragma unroll
+        for (int w = 0; w < kCutWaves; ++w)
+            Z += s_red[w];
+        __syncthreads();
+        C += Z;
+        if (tid == 0)
+            cz[k + 1] = make_double2(C, Z);  // {C_{k+1}, Z_{k+1}}
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SampleParams p)
+{
+    constexpr int kMaxN = 16;
+    __shared__ float s_M[kMaxN], s_l[kMaxN], s_q[kMaxN], s_u[kMaxN];
+    __shared__ double s_iZ[kMaxN];
+    __shared__ int s_par[kMaxN], s_tok[kMaxN];
+    __shared__ double2 s_cz[kMaxN][kMaxN];
+    __shared__ double s_ratio[kMaxN];
+    __shared__ int s_path[kMaxN];
+    __shared__ int s_n, s_t;
+    __shared__ double s_coef;
+    __shared__ double s_part[kNWs][2];
+
+    const int N = p.K + 1, V = p.V;
+    const int nsub = (V + kSampleSub - 1) / kSampleSub;
+    const int b = blockIdx.x / nsub;
+    const int sub = blockIdx.x - b * nsub;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const Temp t1{false, 1.0, 0.0f, 0.0f};
+    const float ninf = -__builtin_inff();
+
+    // 1. Everything the walk reads, requested together.
+    if (tid < N) {
+        const int c = tid;
+        s_u[c] = p.uniforms[(size_t)b * N + c];
+        s_ratio[c] = __builtin_nan("");
+        if (c > 0) {
+            const int pc = tree_parent(p, b, c);
+            const int x = clamp_token(p.tokens[(size_t)b * N + c], V);
+            s_par[c] = pc;
+            s_tok[c] = x;
+            s_l[c] = p.logits[((size_t)b * N + pc) * V + x];
+            s_q[c] = p.probs[((size_t)b * N + pc) * V + x];
+        } else {
+            s_par[0] = -1;
+            s_tok[0] = 0;
+        }
+    }
+    for (int i = tid; i < N * N; i += kSampleThreads) {
+        const int u = i / N, k = i - u * N;
+        if (k >= 2)  // written by tree_resid for nodes with >= k children; read only then
+            s_cz[u][k] = reinterpret_cast<const double2 *>(p.coefs)[((size_t)b * N + u) * N + k];
+    }
+    for (int r = wave; r < N; r += kNWs) {
+        float M;
+        double iZ;
+        tree_row_mz(p, b * N + r, M, iZ);
+        if (lane == 0) {
+            s_M[r] = M;
+            s_iZ[r] = iZ;
+        }
+    }
+    __syncthreads();
+
+    // 2. The walk.
+    if (tid == 0) {
+        int node = 0, depth = 0;
+        double C = 0.0;
+        for (;;) {
+            int k = 0, next = -1;
+            C = 0.0;
+            for (int c = node + 1; c < N; ++c) {
+                if (s_par[c] != node)
+                    continue;
+                const double qx = (double)s_q[c];
+                const double px = target_prob(s_l[c], 0, s_M[node], s_iZ[node], t1, 0, ninf);
+                double a;
+                if (k == 0) {
+                    a = px;
+                } else {
+                    const double Zk = s_cz[node][k + 1].y;
+                    const double rx = px - C * qx;
+                    a = (Zk > 0.0 && rx > 0.0) ? rx / Zk : 0.0;
+                }
+                s_ratio[c] = qx > 0.0 ? fmin(1.0, a / qx) : (a > 0.0 ? 1.0 : 0.0);
+                if ((double)s_u[c] * qx < a) {
+                    next = c;
+                    break;
+                }
+                ++k;
+                C = (k == 1) ? 1.0 : s_cz[node][k].x;
+            }
+            if (next < 0)
+                break;
+            s_path[depth++] = next;
+            node = next;
+        }
+        s_n = depth;
+        s_t = node;
+        s_coef = C;
+    }
+    __syncthreads();
+    const int n = s_n, t = s_t;
+    const double coef = s_coef;
+    const float M = s_M[t];
+    const double invZ = s_iZ[t];
+
+    // 3. Mass of this sub-chunk: final weights and plain target mass.
+    const int base = sub * kSampleSub;
+    const int cnt = min(kSampleSub, V - base);
+    float lv[4], qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    load_sub<VEC>(p.logits + ((size_t)b * N + t) * V + base, cnt, ninf, lv);
+    if (coef > 0.0)
+        load_sub<VEC>(p.probs + ((size_t)b * N + t) * V + base, cnt, 0.0f, qv);
+    double sw = 0.0, sp = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, t1, 0, ninf);
+        sp += pj;
+        if (coef > 0.0) {
+            const double r = pj - coef * (double)qv[k];
+            sw += r > 0.0 ? r : 0.0;
+        } else {
+            sw += pj;
+        }
+    }
+    sw = wave_sum_f64(sw);
+    sp = wave_sum_f64(sp);
+    if (lane == 0) {
+        s_part[wave][0] = sw;
+        s_part[wave][1] = sp;
+    }
+    __syncthreads();
+    if (tid < 2) {
+        double acc = s_part[0][tid];
+#pragma unroll
+        for (int w = 1; w < kNWs; ++w)
+            acc += s_part[w][tid];
+        p.sub_mass[((size_t)b * nsub + sub) * 2 + tid] = acc;
+    }
+
+    // 4. The first workgroup of the sequence writes the state of the draw and
+    //    every output but the drawn token.
+    if (sub == 0) {
+        if (tid == 0) {
+            SeqState ss;
+            ss.n = n;
+            ss.m = M;
+            ss.inv_z = invZ;
+            ss.inv_t = 1.0;
+            ss.coef = coef;
+            ss.greedy = 0;
+            ss.arg = 0;
+            ss.row = t;
+            ss.qrow = t;
+            ss.tree = 1;
+            ss.ucol = 0;
+            ss.tau = ninf;
+            static_cast<SeqState *>(p.seq_state)[b] = ss;
+        }
+        if (tid < N) {
+            const size_t o = (size_t)b * N + tid;
+            if (tid < n) {
+                p.out_tokens[o] = s_tok[s_path[tid]];
+                p.path[o] = s_path[tid];
+            } else {
+                if (tid > n)
+                    p.out_tokens[o] = -1;  // position n: the drawn token, written by pick
+                p.path[o] = -1;
+            }
+            if (p.accept_prob)
+                p.accept_prob[o] = (float)s_ratio[tid];
+        }
+    }
 }
 
 __global__ void sv_fill_zero_kernel(uint4 *p, size_t n16, unsigned char *tail, size_t ntail)
@@ -1098,6 +1415,28 @@ hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
             hipLaunchKernelGGL(sv_sample_cut_kernel<false>, gc, dim3(kCutThreads), 0, stream, p);
         }
         hipLaunchKernelGGL(sv_sample_decide_kernel<false>, g2, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream)
+{
+    const dim3 block(kSampleThreads);
+    const int N = p.K + 1;
+    const dim3 g1((unsigned)(p.nchunk * p.B * N));
+    const dim3 gr((unsigned)(p.B * N));
+    const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
+    const dim3 g3((unsigned)p.B);
+    if (p.vec4) {
+        hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_tree_resid_kernel<true>, gr, dim3(kCutThreads), 0, stream, p);
+        hipLaunchKernelGGL(sv_tree_decide_kernel<true>, g2, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL(sv_tree_resid_kernel<false>, gr, dim3(kCutThreads), 0, stream, p);
+        hipLaunchKernelGGL(sv_tree_decide_kernel<false>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
     }
     return hipGetLastError();

@@ -67,6 +67,11 @@ struct SampleParams {
     void *seq_state;         // [B] {accepted count, row max, 1/row sum, 1/T, greedy, argmax, cut}
     void *row_cut;           // [B*(K+1)] {cut logit, 1/kept mass}, or null without top_p
     unsigned long long *cut_part;  // [B*(K+1)][nchunk][kCutCoarse] partial coarse histograms
+    int qrows;               // draft rows per sequence: K (chain) or N (tree)
+    int tree;                // tree verification: K + 1 = N nodes, see launch_sample_tree
+    const int32_t *parents;  // tree: [B][N] BFS parents (parents[b][0] < 0)
+    int32_t *path;           // tree: [B][N] accepted node ids, then -1
+    double *coefs;           // tree: [B][N][N][2] {C_k, Z_k} of each node's residual chain
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
     void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}
@@ -79,13 +84,21 @@ struct SamplePlan {
     size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, total;
 };
 
-constexpr size_t kSeqStateBytes = 48;  // workspace bytes per sequence of the decide -> pick state
+constexpr size_t kSeqStateBytes = 64;  // workspace bytes per sequence of the decide -> pick state
 constexpr size_t kRowCutBytes = 16;    // workspace bytes per target row of the top-p cut
 constexpr int kCutMaxV = 1 << 20;      // the cut's fixed-point masses need V < 2^20
 constexpr int kCutCoarse = 512;        // coarse buckets of the top-p cut
 
 SamplePlan plan_sample(int B, int K, int V);
 hipError_t launch_sample(const SampleParams &p, hipStream_t stream);
+
+// Tree verification: B sequences of N <= 16 BFS-ordered nodes.
+struct TreePlan {
+    int nchunk;
+    size_t off_state, off_stats, off_mass, off_coefs, total;
+};
+TreePlan plan_sample_tree(int B, int N, int V);
+hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream);
 hipError_t launch_clear(void *ptr, size_t bytes, hipStream_t stream);
 
 // Appending the T verify positions to the paged cache.

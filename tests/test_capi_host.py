@@ -101,6 +101,28 @@ def test_sample_argument_checks():
     assert ex(p, p, p, p, None, p, p, p, None, 2, 3, 1 << 20, p, 1 << 30, None) == 3
 
 
+def test_tree_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 20)
+    p = (ctypes.addressof(buf) + 255) & ~255
+    st = L.spec_verify_sample_tree
+    assert st(None, p, p, p, p, p, p, p, None, 2, 4, 100, p, 1 << 18, None) == 1
+    assert st(p, p, p, p, p, p, p, p, None, 2, 17, 100, p, 1 << 18, None) == 2     # N > 16
+    assert st(p, p, p, p, p, p, p, p, None, 0, 4, 100, p, 1 << 18, None) == 2
+    assert st(p, p, p + 2, p, p, p, p, p, None, 2, 4, 100, p, 1 << 18, None) == 5
+    assert st(p, p, p, p, p, p, p, p, None, 2, 4, 100, p, 8, None) == 4
+    assert L.spec_verify_sample_tree_workspace_size(2, 17, 100) == 0
+    assert L.spec_verify_sample_tree_workspace_size(2, 16, 100) > 0
+    at = L.spec_verify_attn_tree
+    # tree_mask NULL is rejected; shape checks as the chain's
+    args = [p, p, p, None, None, p, p, None, p, 2, 4, 8, 2, 64, 16, 4, 8, 1, ctypes.c_float(0.125), p, 1 << 18,
+            None, 0, 0]
+    assert at(*args) == 1
+    args[7] = p
+    args[10] = 17   # T > 16
+    assert at(*args) == 2
+
+
 def test_workspace_queries():
     assert sv.attn_workspace_size(8, 6, 32, 8, 128, 256) > 0
     assert sv.lib().spec_verify_attn_workspace_size(8, 6, 30, 8, 128, 256) == 0

@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--bps", type=int, default=0, help="context pages per split (0: planner)")
     ap.add_argument("--no-graph", action="store_true", help="headline from the eager pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
     ap.add_argument("--probe", choices=["none", "copy"], default="none",
                     help="copy: run only a plain device copy of known size (counter calibration)")
@@ -308,6 +309,58 @@ def main():
         n_acc, toks, ws_s, stream=stream, temperature=temp_t, top_p=cut_t), args.steps)
     print("# sampler %.1f us, with temperature + top-p %.1f us" % (samp_b2b_ms * 1e3, samp_tp_ms * 1e3),
           file=sys.stderr, flush=True)
+    # Tree verification at the same geometry: the widest tree shape whose
+    # nodes fit the row tiles (N * Hq/Hkv <= 64), attention over the same
+    # cache with N verify rows, and the tree sampler over N target rows.
+    tree = None
+    if not args.no_tree:
+        G = a.Hq // a.Hkv
+        shapes = sorted(W.TREE_SHAPES.items(), key=lambda kv: -len(W.tree_parents(kv[1])))
+        fit = [(nm, sh) for nm, sh in shapes if len(W.tree_parents(sh)) * G <= 64]
+        if fit:
+            tname, tshape = fit[0]
+            par = W.tree_parents(tshape)
+            N = par.shape[0]
+            masks = np.zeros((a.B, N), np.uint32)
+            for c in range(N):
+                m, u = 0, c
+                while u >= 0:
+                    m |= 1 << u
+                    u = par[u]
+                masks[:, c] = m
+            gq = torch.Generator(device=dev)
+            gq.manual_seed(args.seed + 1)
+            q_tree = torch.randn((a.B, N, a.Hq, a.d), generator=gq, device=dev)
+            tm = torch.from_numpy(masks.view(np.int32)).to(dev)
+            out_tree = torch.empty((a.B, N, a.Hq, a.d), dtype=torch.float32, device=dev)
+            ws_ta = sv.alloc_workspace(sv.attn_workspace_size(a.B, N, a.Hq, a.Hkv, a.d, a.max_blocks, 0), dev)
+            tree_attn_ms = timed_launches(lambda i: sv.spec_verify_attn_tree(
+                q_tree, sets[i % copies]["k"], sets[i % copies]["v"], sets[i % copies]["table"],
+                sets[i % copies]["lens"], tm, out_tree, ws_ta, k_scale=sets[i % copies].get("ks"),
+                v_scale=sets[i % copies].get("vs"), kv_dtype=a.kv_dtype, stream=stream), args.steps)
+            t_gen = time.time()
+            ti = W.make_tree(args.seed, s.B, par, s.V, cfg["target_sigma"],
+                             cfg["noise"] if not isinstance(cfg["noise"], tuple) else 1.0)
+            tl = up(ti.target_logits)
+            tsets = [{"logits": tl if j == 0 else tl.clone(), "probs": up(ti.draft_probs) if j == 0 else None}
+                     for j in range(max(2, int(np.ceil(3 * MALL_BYTES / (2 * tl.numel() * 4))) + 1))]
+            for j in range(1, len(tsets)):
+                tsets[j]["probs"] = tsets[0]["probs"].clone()
+            ttok, tpar, tu = up(ti.tokens), up(ti.parents), up(ti.uniforms)
+            tn = torch.empty(s.B, dtype=torch.int32, device=dev)
+            tot = torch.empty((s.B, N), dtype=torch.int32, device=dev)
+            tpath = torch.empty((s.B, N), dtype=torch.int32, device=dev)
+            ws_ts = sv.alloc_workspace(sv.sample_tree_workspace_size(s.B, N, s.V), dev)
+            tree_samp_ms = timed_launches(lambda i: sv.spec_verify_sample_tree(
+                tsets[i % len(tsets)]["logits"], tsets[i % len(tsets)]["probs"], ttok, tpar, tu, tn, tot, tpath,
+                ws_ts, max(tshape), stream=stream), args.steps)
+            tree_bytes = attn_bytes + 2 * a.B * (N - a.T) * a.Hq * a.d * 4
+            tree = {"shape": tname, "nodes": N, "attn_us": tree_attn_ms * 1e3,
+                    "attn_gbs": tree_bytes / (tree_attn_ms * 1e-3) / 1e9, "sample_us": tree_samp_ms * 1e3,
+                    "mean_accepted": float(tn.float().mean().item())}
+            print("# tree %s (N=%d): attention %.1f us, sampler %.1f us (inputs %.1f s)" % (
+                tname, N, tree_attn_ms * 1e3, tree_samp_ms * 1e3, time.time() - t_gen), file=sys.stderr, flush=True)
+            del tsets, tl
     ap_bytes = 2 * k_new.numel() * (4 + {W.KV_F32: 4, W.KV_BF16: 2, W.KV_FP8_E4M3: 1}[a.kv_dtype]) + 4 * a.B * (a.T + 1)
     print("# append %.1f us, rollback %.1f us" % (append_ms * 1e3, rollback_ms * 1e3), file=sys.stderr, flush=True)
     hev.close()
@@ -354,6 +407,7 @@ def main():
         "kv_append_us_per_layer": float(append_ms * 1e3),
         "kv_append_bytes_per_layer": int(ap_bytes),
         "rollback_us": float(rollback_ms * 1e3),
+        "tree_verify": tree,
         "attn_bytes": attn_bytes,
         "sample_bytes": samp_bytes,
         "step_gbs": (attn_bytes + samp_bytes) / (ms_step * 1e-3) / 1e9,

@@ -253,6 +253,11 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs,
  *   path [B][N] (the accepted node ids in order, then -1) -- the K/V of
  *   these nodes are the ones the cache keeps; accept_prob [B][N] optional
  *   (NULL ok): min(1, p_k(x)/q(x)) of every tested node, NaN elsewhere.
+ * max_children: the largest number of children of any node (0 .. N-1,
+ *   known to the caller from its tree shape).  One extra launch per sibling
+ *   rank 2 .. max_children prepares the normalisers; a node's children of
+ *   higher rank are skipped (never tested), so pass at least the true
+ *   maximum.
  * Parents that break the BFS order are clamped into [0, c-1] (results
  * undefined, memory-safe).  N <= 16.  Workspace:
  * spec_verify_sample_tree_workspace_size(B, N, V) bytes, 256-byte aligned. */
@@ -260,7 +265,7 @@ size_t spec_verify_sample_tree_workspace_size(int B, int N, int V);
 int spec_verify_sample_tree(const float *target_logits, const float *draft_probs,
                             const int32_t *tokens, const int32_t *parents, const float *uniforms,
                             int32_t *num_accepted, int32_t *out_tokens, int32_t *path,
-                            float *accept_prob, int B, int N, int V,
+                            float *accept_prob, int B, int N, int V, int max_children,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------

@@ -72,7 +72,7 @@ def lib():
         L.spec_verify_sample_tree_workspace_size.restype = S
         L.spec_verify_sample_tree_workspace_size.argtypes = [I] * 3
         L.spec_verify_sample_tree.restype = I
-        L.spec_verify_sample_tree.argtypes = [P] * 9 + [I] * 3 + [P, S, P]
+        L.spec_verify_sample_tree.argtypes = [P] * 9 + [I] * 4 + [P, S, P]
         L.spec_verify_kv_append.restype = I
         L.spec_verify_kv_append.argtypes = [P] * 8 + [I] * 8 + [P]
         L.spec_verify_rollback.restype = I
@@ -208,17 +208,18 @@ def sample_tree_workspace_size(B, N, V):
 
 
 def spec_verify_sample_tree(target_logits, draft_probs, tokens, parents, uniforms, num_accepted, out_tokens,
-                            path, workspace, *, accept_prob=None, stream=None):
+                            path, workspace, max_children, *, accept_prob=None, stream=None):
     """Tree verification sampler (see include/spec_verify.h).
 
     target_logits, draft_probs [B,N,V] f32; tokens, parents [B,N] i32 (BFS
-    order, parents[:,0] = -1); uniforms [B,N] f32; outputs num_accepted [B],
-    out_tokens [B,N], path [B,N] i32, optional accept_prob [B,N] f32.
+    order, parents[:,0] = -1); uniforms [B,N] f32; max_children: the largest
+    number of children of any node; outputs num_accepted [B], out_tokens
+    [B,N], path [B,N] i32, optional accept_prob [B,N] f32.
     """
     B, N, V = target_logits.shape
     _check("spec_verify_sample_tree", lib().spec_verify_sample_tree(
         _ptr(target_logits), _ptr(draft_probs), _ptr(tokens), _ptr(parents), _ptr(uniforms),
-        _ptr(num_accepted), _ptr(out_tokens), _ptr(path), _ptr(accept_prob), B, N, V,
+        _ptr(num_accepted), _ptr(out_tokens), _ptr(path), _ptr(accept_prob), B, N, V, int(max_children),
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, target_logits.device)))
     return num_accepted, out_tokens, path

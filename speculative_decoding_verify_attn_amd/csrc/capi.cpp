@@ -91,8 +91,8 @@ TreePlan plan_sample_tree(int B, int N, int V)
     off = align256(off + (size_t)B * N * pl.nchunk * 16);
     pl.off_mass = off;
     off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
-    pl.off_coefs = off;
-    off = align256(off + (size_t)B * N * N * 16);
+    pl.off_coefs = off;  // chunk partials of every node's test normaliser
+    off = align256(off + (size_t)B * N * pl.nchunk * 8);
     pl.total = off;
     return pl;
 }
@@ -493,7 +493,7 @@ size_t spec_verify_sample_tree_workspace_size(int B, int N, int V)
 int spec_verify_sample_tree(const float *target_logits, const float *draft_probs, const int32_t *tokens,
                             const int32_t *parents, const float *uniforms, int32_t *num_accepted,
                             int32_t *out_tokens, int32_t *path, float *accept_prob, int B, int N, int V,
-                            void *workspace, size_t workspace_bytes, void *stream)
+                            int max_children, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!target_logits || !draft_probs || !tokens || !parents || !uniforms || !num_accepted || !out_tokens || !path)
         return fail(SV_ERR_NULL, "target_logits, draft_probs, tokens, parents, uniforms, num_accepted, out_tokens "
@@ -502,6 +502,8 @@ int spec_verify_sample_tree(const float *target_logits, const float *draft_probs
         return fail(SV_ERR_SHAPE, "B, N and V must be >= 1 (got %d, %d, %d)", B, N, V);
     if (N > 16)
         return fail(SV_ERR_SHAPE, "N must be <= 16 (got %d)", N);
+    if (max_children < 0 || max_children > N - 1)
+        return fail(SV_ERR_SHAPE, "max_children must be in [0, N-1] (got %d, N = %d)", max_children, N);
     if (V > sv::kMaxSampleChunks * sv::kSampleChunk)
         return fail(SV_ERR_UNSUPPORTED, "V must be <= %d (got %d)", sv::kMaxSampleChunks * sv::kSampleChunk, V);
     if ((long long)B * N * ((V + sv::kSampleChunk - 1) / sv::kSampleChunk) > 0x7FFFFFFFLL ||
@@ -540,6 +542,7 @@ int spec_verify_sample_tree(const float *target_logits, const float *draft_probs
     p.nchunk = pl.nchunk;
     p.qrows = N;
     p.tree = 1;
+    p.tree_max_children = max_children;
     p.vec4 = (V % 4 == 0) && aligned(target_logits, 16) && aligned(draft_probs, 16);
     const hipError_t e = sv::launch_sample_tree(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)

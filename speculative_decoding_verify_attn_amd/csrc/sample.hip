@@ -1096,12 +1096,13 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
 // max(0, p_u - C q_u) with C the coefficient reached (0 at a leaf: p_u).
 // C_k and Z_k depend only on node u's two rows, never on the drafts or
 // uniforms, so they are computed for every node before the walk:
-//   tree_resid  one 1024-thread workgroup per node with >= 2 children: for
-//               k = 1 .. m-1 a pass over the node's rows gives
-//               Z_{k+1} = sum_j max(0, p_u(j) - C_k q_u(j)) (fp64 block sum);
+//   tree_level  one launch per sibling rank k = 2 .. max_children, grid
+//               (vocabulary chunk x node): the chunk partials of
+//               Z = sum_j max(0, p_u(j) - C q_u(j)) for every child of rank k
+//               (C from the complete sums of its earlier siblings);
 //   tree_decide grid (1024-entry sub-chunk x sequence): every workgroup
 //               loads the gathered (logit, q) of each node's token, the row
-//               statistics and the coefficients in one round trip, walks the
+//               statistics and the normalisers in one round trip, walks the
 //               tree (one thread), and sums the final weights over its
 //               sub-chunk; the first one writes the path and the tokens;
 //   pick        the chain's draw, from the row and coefficient the walk left.
@@ -1131,95 +1132,137 @@ __device__ __forceinline__ int tree_parent(const SampleParams &p, int b, int c)
     return pc < 0 ? 0 : (pc >= c ? c - 1 : pc);  // out-of-contract parents stay in bounds
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kCutThreads) void sv_tree_resid_kernel(SampleParams p)
+constexpr int kTreeMaxN = 16;
+
+// Parents of sequence b into LDS, clamped into [0, c-1] (the root: -1); one
+// load per thread.
+__device__ __forceinline__ void tree_load_parents(const SampleParams &p, int b, int *s_par)
 {
-    __shared__ double s_red[kCutWaves];
-    __shared__ int s_m;
+    const int N = p.K + 1, c = threadIdx.x;
+    if (c < N)
+        s_par[c] = c == 0 ? -1 : tree_parent(p, b, c);
+}
+
+// Rank of node c >= 1 among its siblings (1 for the first child).
+__device__ __forceinline__ int tree_rank(const int *s_par, int c)
+{
+    const int u = s_par[c];
+    int r = 1;
+    for (int c2 = u + 1; c2 < c; ++c2)
+        r += s_par[c2] == u ? 1 : 0;
+    return r;
+}
+
+// This lane's share of the normaliser of node c's test: chunks lane,
+// lane + 64, ... of its partials.  The normaliser is the wave sum of the
+// shares (fixed order), the same wherever it is needed.
+__device__ __forceinline__ double tree_z_share(const SampleParams &p, int b, int c)
+{
+    const double *part = p.coefs + ((size_t)b * (p.K + 1) + c) * p.nchunk;
+    double z = 0.0;
+    for (int i = threadIdx.x & 63; i < p.nchunk; i += kWave)
+        z += part[i];
+    return z;
+}
+
+constexpr int kTreeSlots = 4;  // workgroups per (sequence, chunk) of a rank's launch
+
+// One sibling rank: grid (slot x vocabulary chunk x sequence).  The children
+// of rank `rank` (>= 2) of the sequence are dealt to the slots in node
+// order; for child c with parent u the workgroup sums, over its chunk,
+// max(0, p_u(j) - C q_u(j)) with C = 1 + the normalisers of c's earlier
+// siblings of rank >= 2 (their partials are complete: they belong to earlier
+// launches); the sum over chunks is the normaliser Z of c's test.
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_tree_level_kernel(SampleParams p, int rank)
+{
+    __shared__ double s_red[kNWs];
+    __shared__ int s_par[kTreeMaxN], s_rank[kTreeMaxN];
     __shared__ float s_M;
-    __shared__ double s_iZ;
+    __shared__ double s_iZ, s_C;
     const int N = p.K + 1;
-    const int row = blockIdx.x;
-    const int b = row / N, u = row - b * N;
+    const int slot = blockIdx.x % kTreeSlots;
+    const int chunk = (blockIdx.x / kTreeSlots) % p.nchunk;
+    const int b = blockIdx.x / (kTreeSlots * p.nchunk);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (tid == 0)
-        s_m = 0;
+    tree_load_parents(p, b, s_par);
     __syncthreads();
-    if (tid > u && tid < N && tree_parent(p, b, tid) == u)
-        atomicAdd(&s_m, 1);
-    if (wave == 0) {
-        float M;
-        double iZ;
-        tree_row_mz(p, row, M, iZ);
-        if (lane == 0) {
-            s_M = M;
-            s_iZ = iZ;
-        }
-    }
+    if (tid < N)
+        s_rank[tid] = tid > 0 ? tree_rank(s_par, tid) : 0;
     __syncthreads();
-    const int m = s_m;
-    if (m < 2)
-        return;  // uniform: C_1 = 1 is all a node with one child needs
-    const float M = s_M;
-    const double invZ = s_iZ;
-    const float *lrow = p.logits + (size_t)row * p.V;
-    const float *qrow = p.probs + (size_t)row * p.V;
-    const int V = p.V;
+    const int base = chunk * kSampleChunk;
+    const int n = min(kSampleChunk, p.V - base);
     const Temp t1{false, 1.0, 0.0f, 0.0f};
-    double2 *cz = reinterpret_cast<double2 *>(p.coefs) + (size_t)row * N;
-    double C = 1.0;
-    for (int k = 1; k < m; ++k) {
-        double acc = 0.0;
-        auto add = [&](float l, float q, int j) {
-            const double r = target_prob_fast(l, j, M, invZ, t1, 0, -__builtin_inff()) - C * (double)q;
-            acc += r > 0.0 ? r : 0.0;
-        };
-        if constexpr (VEC) {
-            for (int base = 0; base < V; base += kCutThreads * 4 * 4) {
-                float4 lx[4], qx[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = base + (i * kCutThreads + tid) * 4;
-                    lx[i] = e < V ? *reinterpret_cast<const float4 *>(lrow + e)
-                                  : make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
-                    qx[i] = e < V ? *reinterpret_cast<const float4 *>(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = base + (i * kCutThreads + tid) * 4;
-                    add(lx[i].x, qx[i].x, e);
-                    add(lx[i].y, qx[i].y, e + 1);
-                    add(lx[i].z, qx[i].z, e + 2);
-                    add(lx[i].w, qx[i].w, e + 3);
-                }
+    int q = 0;  // index among the children of this rank (uniform)
+    for (int c = 1; c < N; ++c) {
+        if (s_rank[c] != rank)
+            continue;
+        if (q++ % kTreeSlots != slot)
+            continue;
+        const int u = s_par[c];
+        const int row = b * N + u;
+        float v[kPer], w[kPer];
+        load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
+        load_chunk<VEC>(p.probs + (size_t)row * p.V + base, n, 0.0f, w);
+        if (wave == 0) {
+            float M;
+            double iZ;
+            tree_row_mz(p, row, M, iZ);
+            if (lane == 0) {
+                s_M = M;
+                s_iZ = iZ;
             }
-        } else {
-            for (int e = tid; e < V; e += kCutThreads)
-                add(lrow[e], qrow[e], e);
+        } else if (wave == 1) {
+            // earlier siblings of rank >= 2, their shares requested together
+            double share[kTreeMaxN];
+            bool use[kTreeMaxN];
+#pragma unroll
+            for (int c2 = 1; c2 < kTreeMaxN; ++c2) {
+                use[c2] = c2 > u && c2 < c && s_par[c2] == u && s_rank[c2] >= 2;
+                share[c2] = use[c2] ? tree_z_share(p, b, c2) : 0.0;
+            }
+            double C = 1.0;
+#pragma unroll
+            for (int c2 = 1; c2 < kTreeMaxN; ++c2)
+                if (use[c2])
+                    C += wave_sum_f64(share[c2]);
+            if (lane == 0)
+                s_C = C;
+        }
+        __syncthreads();
+        const float M = s_M;
+        const double invZ = s_iZ, C = s_C;
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int e = VEC ? ((k >> 2) * kSampleThreads + tid) * 4 + (k & 3) : k * kSampleThreads + tid;
+            const double r = target_prob_fast(v[k], base + e, M, invZ, t1, 0, -__builtin_inff()) - C * (double)w[k];
+            acc += r > 0.0 ? r : 0.0;
         }
         acc = wave_sum_f64(acc);
         if (lane == 0)
             s_red[wave] = acc;
         __syncthreads();
-        double Z = 0.0;
+        if (tid == 0) {
+            double z = 0.0;
 #pragma unroll
-        for (int w = 0; w < kCutWaves; ++w)
-            Z += s_red[w];
-        __syncthreads();
-        C += Z;
-        if (tid == 0)
-            cz[k + 1] = make_double2(C, Z);  // {C_{k+1}, Z_{k+1}}
+            for (int i = 0; i < kNWs; ++i)
+                z += s_red[i];
+            p.coefs[((size_t)b * N + c) * p.nchunk + chunk] = z;
+        }
+        __syncthreads();  // s_M, s_C and s_red are reused by the next child
     }
 }
 
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SampleParams p)
 {
-    constexpr int kMaxN = 16;
+    constexpr int kMaxN = kTreeMaxN;
     __shared__ float s_M[kMaxN], s_l[kMaxN], s_q[kMaxN], s_u[kMaxN];
     __shared__ double s_iZ[kMaxN];
     __shared__ int s_par[kMaxN], s_tok[kMaxN];
-    __shared__ double2 s_cz[kMaxN][kMaxN];
+    __shared__ double s_z[kMaxN];     // normaliser of node c's test (rank >= 2)
+    __shared__ int s_rank[kMaxN];
     __shared__ double s_ratio[kMaxN];
     __shared__ int s_path[kMaxN];
     __shared__ int s_n, s_t;
@@ -1235,7 +1278,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
     const Temp t1{false, 1.0, 0.0f, 0.0f};
     const float ninf = -__builtin_inff();
 
-    // 1. Everything the walk reads, requested together.
+    // 1. Everything the walk reads, requested together: each node's token,
+    //    uniform and gathered (logit, q); the row statistics; the
+    //    normalisers of the tests of rank >= 2.
     if (tid < N) {
         const int c = tid;
         s_u[c] = p.uniforms[(size_t)b * N + c];
@@ -1252,20 +1297,58 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
             s_tok[0] = 0;
         }
     }
-    for (int i = tid; i < N * N; i += kSampleThreads) {
-        const int u = i / N, k = i - u * N;
-        if (k >= 2)  // written by tree_resid for nodes with >= k children; read only then
-            s_cz[u][k] = reinterpret_cast<const double2 *>(p.coefs)[((size_t)b * N + u) * N + k];
-    }
-    for (int r = wave; r < N; r += kNWs) {
-        float M;
-        double iZ;
-        tree_row_mz(p, b * N + r, M, iZ);
-        if (lane == 0) {
-            s_M[r] = M;
-            s_iZ[r] = iZ;
+    {
+        // wave w: the partial shares of nodes w, w + 4, w + 8, w + 12
+        double share[kTreeMaxN / kNWs];
+#pragma unroll
+        for (int i = 0; i < kTreeMaxN / kNWs; ++i) {
+            const int c = wave + i * kNWs;
+            share[i] = (c > 0 && c < N) ? tree_z_share(p, b, c) : 0.0;  // read only where the rank is >= 2
+        }
+#pragma unroll
+        for (int i = 0; i < kTreeMaxN / kNWs; ++i) {
+            const int c = wave + i * kNWs;
+            const double z = wave_sum_f64(share[i]);
+            if (lane == 0 && c < N)
+                s_z[c] = z;
         }
     }
+    if (p.nchunk <= kWave) {
+        // wave w: rows w, w + 4, w + 8, w + 12, their chunk statistics
+        // requested together (lane = chunk, as in tree_row_mz)
+        RowStat st[kTreeMaxN / kNWs];
+#pragma unroll
+        for (int i = 0; i < kTreeMaxN / kNWs; ++i) {
+            const int r = wave + i * kNWs;
+            st[i] = RowStat{-__builtin_inff(), 0, 0.0};
+            if (r < N && lane < p.nchunk)
+                st[i] = static_cast<const RowStat *>(p.row_stats)[((size_t)b * N + r) * p.nchunk + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < kTreeMaxN / kNWs; ++i) {
+            const int r = wave + i * kNWs;
+            const float M = wave_max_f32(st[i].m);
+            const double z = (lane < p.nchunk && st[i].z > 0.0) ? st[i].z * exp((double)st[i].m - (double)M) : 0.0;
+            const double iZ = 1.0 / wave_sum_f64(z);
+            if (lane == 0 && r < N) {
+                s_M[r] = M;
+                s_iZ[r] = iZ;
+            }
+        }
+    } else {
+        for (int r = wave; r < N; r += kNWs) {
+            float M;
+            double iZ;
+            tree_row_mz(p, b * N + r, M, iZ);
+            if (lane == 0) {
+                s_M[r] = M;
+                s_iZ[r] = iZ;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < N)
+        s_rank[tid] = tid > 0 ? tree_rank(s_par, tid) : 0;
     __syncthreads();
 
     // 2. The walk.
@@ -1273,18 +1356,18 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
         int node = 0, depth = 0;
         double C = 0.0;
         for (;;) {
-            int k = 0, next = -1;
+            int next = -1;
             C = 0.0;
             for (int c = node + 1; c < N; ++c) {
-                if (s_par[c] != node)
-                    continue;
+                if (s_par[c] != node || s_rank[c] > p.tree_max_children)
+                    continue;  // not a child, or beyond the ranks prepared
                 const double qx = (double)s_q[c];
                 const double px = target_prob(s_l[c], 0, s_M[node], s_iZ[node], t1, 0, ninf);
                 double a;
-                if (k == 0) {
+                if (s_rank[c] == 1) {
                     a = px;
                 } else {
-                    const double Zk = s_cz[node][k + 1].y;
+                    const double Zk = s_z[c];  // written by tree_level for ranks 2 .. max_children
                     const double rx = px - C * qx;
                     a = (Zk > 0.0 && rx > 0.0) ? rx / Zk : 0.0;
                 }
@@ -1293,8 +1376,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
                     next = c;
                     break;
                 }
-                ++k;
-                C = (k == 1) ? 1.0 : s_cz[node][k].x;
+                C = (s_rank[c] == 1) ? 1.0 : C + s_z[c];
             }
             if (next < 0)
                 break;
@@ -1425,17 +1507,19 @@ hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream)
     const dim3 block(kSampleThreads);
     const int N = p.K + 1;
     const dim3 g1((unsigned)(p.nchunk * p.B * N));
-    const dim3 gr((unsigned)(p.B * N));
+    const dim3 gl((unsigned)(kTreeSlots * p.nchunk * p.B));
     const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
     const dim3 g3((unsigned)p.B);
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
-        hipLaunchKernelGGL(sv_tree_resid_kernel<true>, gr, dim3(kCutThreads), 0, stream, p);
+        for (int r = 2; r <= p.tree_max_children; ++r)
+            hipLaunchKernelGGL(sv_tree_level_kernel<true>, gl, block, 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
-        hipLaunchKernelGGL(sv_tree_resid_kernel<false>, gr, dim3(kCutThreads), 0, stream, p);
+        for (int r = 2; r <= p.tree_max_children; ++r)
+            hipLaunchKernelGGL(sv_tree_level_kernel<false>, gl, block, 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<false>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
     }

@@ -71,7 +71,8 @@ struct SampleParams {
     int tree;                // tree verification: K + 1 = N nodes, see launch_sample_tree
     const int32_t *parents;  // tree: [B][N] BFS parents (parents[b][0] < 0)
     int32_t *path;           // tree: [B][N] accepted node ids, then -1
-    double *coefs;           // tree: [B][N][N][2] {C_k, Z_k} of each node's residual chain
+    double *coefs;           // tree: [B][N][nchunk] chunk partials of each node's test normaliser
+    int tree_max_children;   // tree: children tested per node (ranks beyond are skipped)
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
     void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}

@@ -106,11 +106,12 @@ def test_tree_argument_checks():
     buf = ctypes.create_string_buffer(1 << 20)
     p = (ctypes.addressof(buf) + 255) & ~255
     st = L.spec_verify_sample_tree
-    assert st(None, p, p, p, p, p, p, p, None, 2, 4, 100, p, 1 << 18, None) == 1
-    assert st(p, p, p, p, p, p, p, p, None, 2, 17, 100, p, 1 << 18, None) == 2     # N > 16
-    assert st(p, p, p, p, p, p, p, p, None, 0, 4, 100, p, 1 << 18, None) == 2
-    assert st(p, p, p + 2, p, p, p, p, p, None, 2, 4, 100, p, 1 << 18, None) == 5
-    assert st(p, p, p, p, p, p, p, p, None, 2, 4, 100, p, 8, None) == 4
+    assert st(None, p, p, p, p, p, p, p, None, 2, 4, 100, 2, p, 1 << 18, None) == 1
+    assert st(p, p, p, p, p, p, p, p, None, 2, 17, 100, 2, p, 1 << 18, None) == 2     # N > 16
+    assert st(p, p, p, p, p, p, p, p, None, 0, 4, 100, 2, p, 1 << 18, None) == 2
+    assert st(p, p, p, p, p, p, p, p, None, 2, 4, 100, 4, p, 1 << 18, None) == 2      # max_children > N-1
+    assert st(p, p, p + 2, p, p, p, p, p, None, 2, 4, 100, 2, p, 1 << 18, None) == 5
+    assert st(p, p, p, p, p, p, p, p, None, 2, 4, 100, 2, p, 8, None) == 4
     assert L.spec_verify_sample_tree_workspace_size(2, 17, 100) == 0
     assert L.spec_verify_sample_tree_workspace_size(2, 16, 100) > 0
     at = L.spec_verify_attn_tree

@@ -23,6 +23,11 @@ from .test_gpu_sampler import _chi2
 pytestmark = pytest.mark.gpu
 
 
+def max_children(parents):
+    par = np.asarray(parents)
+    return int(max([0] + [np.bincount(row[1:], minlength=par.shape[1]).max() for row in par if row.size > 1]))
+
+
 def _upload(t):
     d = dev()
     return {k: torch.from_numpy(np.ascontiguousarray(v)).to(d) for k, v in dict(
@@ -40,7 +45,7 @@ def _run(t, g=None, ws=None):
     if ws is None:
         ws = sv.alloc_workspace(sv.sample_tree_workspace_size(t.B, t.N, t.V), d)
     sv.spec_verify_sample_tree(g["logits"], g["probs"], g["tokens"], g["parents"], g["u"], n, ot, path, ws,
-                               accept_prob=ap)
+                               max_children(t.parents), accept_prob=ap)
     torch.cuda.synchronize()
     return n.cpu().numpy(), ot.cpu().numpy(), path.cpu().numpy(), ap.cpu().numpy()
 
@@ -119,6 +124,33 @@ def test_chain_tree_equals_the_chain_sampler():
     assert np.array_equal(n1, n2) and np.array_equal(ot1, ot2)
 
 
+def test_children_beyond_max_children_are_skipped():
+    """A star of 6 children with max_children = 3: the GPU must match the
+    oracle run on the tree with children 4..6 removed (their columns left
+    untested)."""
+    par = np.array([-1, 0, 0, 0, 0, 0, 0], np.int32)
+    t = W.make_tree(13, 32, par, 4000, 2.0, 1.5)
+    g = _upload(t)
+    d = dev()
+    n = torch.empty(t.B, dtype=torch.int32, device=d)
+    ot = torch.empty((t.B, t.N), dtype=torch.int32, device=d)
+    path = torch.empty((t.B, t.N), dtype=torch.int32, device=d)
+    ws = sv.alloc_workspace(sv.sample_tree_workspace_size(t.B, t.N, t.V), d)
+    sv.spec_verify_sample_tree(g["logits"], g["probs"], g["tokens"], g["parents"], g["u"], n, ot, path, ws, 3)
+    torch.cuda.synchronize()
+    keep = 4
+    sub = W.TreeInputs(np.ascontiguousarray(t.target_logits[:, :keep]), np.ascontiguousarray(t.draft_probs[:, :keep]),
+                       np.ascontiguousarray(t.tokens[:, :keep]), np.ascontiguousarray(t.parents[:, :keep]),
+                       np.ascontiguousarray(t.uniforms[:, :keep]))
+    ref = oracle.sample_tree(sub.target_logits, sub.draft_probs, sub.tokens, sub.parents, sub.uniforms)
+    n, ot = n.cpu().numpy(), ot.cpu().numpy()
+    for b in range(t.B):
+        k = int(ref["near_pos"][b])
+        if k < 0:
+            assert n[b] == ref["num_accepted"][b]
+            assert np.array_equal(ot[b, :keep], ref["out_tokens"][b]) and np.all(ot[b, keep:] == -1)
+
+
 def test_deterministic_and_workspace_reusable():
     t = W.make_tree(11, 16, W.tree_parents(W.TREE_SHAPES["wide5x2"]), 50000, 2.0, 0.5)
     g = _upload(t)
@@ -157,7 +189,7 @@ def test_gpu_output_law_follows_the_rows():
             tk[:, c] = rng.choice(V, size=R, p=qrows[depth[par[c]]])
         u = np.minimum(rng.random((R, N)).astype(np.float32), np.float32(1 - 2 ** -24))
         sv.spec_verify_sample_tree(logits, probs, torch.from_numpy(tk).to(d), parents, torch.from_numpy(u).to(d),
-                                   n_t, o_t, p_t, ws)
+                                   n_t, o_t, p_t, ws, 2)
         torch.cuda.synchronize()
         ns.append(n_t.cpu().numpy())
         toks.append(o_t.cpu().numpy())

@@ -58,6 +58,12 @@ def _bind(lib):
         [c.c_void_p] * 5 + [c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5 + [c.c_int])
     lib.oracle_tree_masks.restype = c.c_int
     lib.oracle_tree_masks.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_void_p]
+    lib.oracle_entropy.restype = c.c_double
+    lib.oracle_entropy.argtypes = [c.c_void_p, c.c_int64]
+    lib.oracle_sample_typical.restype = c.c_int
+    lib.oracle_sample_typical.argtypes = (
+        [c.c_void_p] * 4 + [c.c_double, c.c_double, c.c_int, c.c_int, c.c_int64, c.c_double] + [c.c_void_p] * 5
+        + [c.c_int])
     lib.oracle_target_row.restype = None
     lib.oracle_target_row.argtypes = [c.c_void_p, c.c_int64, c.c_double, c.c_void_p]
     lib.oracle_encode_bf16.restype = c.c_uint16
@@ -207,6 +213,41 @@ def sample(target_logits, draft_probs, draft_tokens, uniforms, *, near_eps=1e-6,
         _ptr(res["near_pos"]), _ptr(res["resid_mass"]), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_sample rejected its arguments")
+    return res
+
+
+def entropy(p):
+    """-sum p log p of a probability row, nats (fp64)."""
+    row = np.ascontiguousarray(p, dtype=np.float64)
+    return float(_load().oracle_entropy(row.ctypes.data, row.shape[0]))
+
+
+def sample_typical(target_logits, draft_tokens, uniforms, eps, delta, *, temperature=None, near_eps=1e-6,
+                   nthreads=None):
+    """Typical acceptance (not exact): draft x_i kept iff
+    p~_i(x_i) > min(eps, delta * exp(-H(p~_i))); the next token drawn from
+    p~_n.  Returns a dict: num_accepted [B], out_tokens [B,K+1], p_draft and
+    threshold [B,K] (NaN after the first rejection), near_pos [B]."""
+    tl = np.ascontiguousarray(target_logits, dtype=np.float32)
+    dt = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B, T, V = tl.shape
+    K = T - 1
+    assert dt.shape == (B, K) and u.shape == (B, K + 1)
+    temp = None if temperature is None else np.ascontiguousarray(temperature, dtype=np.float32)
+    res = {
+        "num_accepted": np.empty(B, dtype=np.int32),
+        "out_tokens": np.empty((B, K + 1), dtype=np.int32),
+        "p_draft": np.empty((B, K), dtype=np.float64),
+        "threshold": np.empty((B, K), dtype=np.float64),
+        "near_pos": np.empty(B, dtype=np.int32),
+    }
+    rc = _load().oracle_sample_typical(
+        _ptr(tl), _ptr(dt), _ptr(u), _ptr(temp), float(eps), float(delta), B, K, V, float(near_eps),
+        _ptr(res["num_accepted"]), _ptr(res["out_tokens"]), _ptr(res["p_draft"]), _ptr(res["threshold"]),
+        _ptr(res["near_pos"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_sample_typical rejected its arguments")
     return res
 
 

@@ -622,6 +622,167 @@ int oracle_sample_tp(const float *target_logits, const float *draft_probs,
     return rc;
 }
 
+/* ------------------------------------------------------- typical acceptance
+ *
+ * Typical acceptance ([SD] 9.1; [KV] 8.2 and Q18): not exact.  Draft x_i is
+ * accepted iff the target's own probability of it exceeds an entropy-based
+ * threshold, p~_i(x_i) > min(eps, delta * exp(-H(p~_i))), H the entropy of
+ * the (tempered) target row in nats; the draft probabilities take no part.
+ * Reading where the pages stop: the comparison is strict ("exceeds"); at the
+ * first rejection n (or n = K) the next token is drawn from the target row
+ * p~_n itself with the last uniform, by the chain's inverse CDF -- the
+ * target's own prediction at that position, with no residual since nothing
+ * is conditioned on the draft.
+ */
+
+/* Entropy -sum p log p of a distribution, in nats (terms with p = 0 add 0). */
+double oracle_entropy(const double *p, int64_t V)
+{
+    double h = 0.0;
+    for (int64_t j = 0; j < V; ++j)
+        if (p[j] > 0.0)
+            h -= p[j] * log(p[j]);
+    return h;
+}
+
+typedef struct {
+    const float *target_logits, *uniforms, *temperature;
+    const int32_t *draft_tokens;
+    double eps, delta;
+    int B, K;
+    int64_t V;
+    double near_eps;
+    int32_t *num_accepted, *out_tokens, *near_pos;
+    double *p_draft, *threshold;
+} typical_job;
+
+static void typical_one(const typical_job *J, int b, double *p)
+{
+    const int K = J->K;
+    const int64_t V = J->V;
+    const float *u = J->uniforms + (int64_t)b * (K + 1);
+    const double tau = J->temperature ? (double)J->temperature[b] : 1.0;
+    int n = K, near = -1;
+    for (int i = 0; i < K; ++i) {
+        oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + i) * V, V, tau, p);
+        const double th = fmin(J->eps, J->delta * exp(-oracle_entropy(p, V)));
+        const int x = J->draft_tokens[(int64_t)b * K + i];
+        J->p_draft[(int64_t)b * K + i] = p[x];
+        J->threshold[(int64_t)b * K + i] = th;
+        if (near < 0 && fabs(p[x] - th) < J->near_eps)
+            near = i;
+        if (!(p[x] > th)) {
+            n = i;
+            break;
+        }
+    }
+    for (int i = n + 1; i < K; ++i) {
+        J->p_draft[(int64_t)b * K + i] = NAN;
+        J->threshold[(int64_t)b * K + i] = NAN;
+    }
+    oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + n) * V, V, tau, p);
+    double S = 0.0;
+    for (int64_t j = 0; j < V; ++j)
+        S += p[j];
+    const double target = (double)u[K] * S;
+    double cum = 0.0, cum_prev = 0.0;
+    int64_t tok = -1;
+    for (int64_t j = 0; j < V; ++j) {
+        cum_prev = cum;
+        cum += p[j];
+        if (cum > target) {
+            tok = j;
+            break;
+        }
+    }
+    if (tok < 0) {
+        for (int64_t j = V - 1; j >= 0; --j)
+            if (p[j] > 0.0) {
+                tok = j;
+                break;
+            }
+        cum_prev = S;
+        cum = S;
+    }
+    if (near < 0 && (fabs((double)u[K] - cum_prev / S) < J->near_eps || fabs((double)u[K] - cum / S) < J->near_eps))
+        near = n;
+    int32_t *ot = J->out_tokens + (int64_t)b * (K + 1);
+    for (int i = 0; i < n; ++i)
+        ot[i] = J->draft_tokens[(int64_t)b * K + i];
+    ot[n] = (int32_t)tok;
+    for (int i = n + 1; i <= K; ++i)
+        ot[i] = -1;
+    J->num_accepted[b] = n;
+    J->near_pos[b] = near;
+}
+
+typedef struct {
+    const typical_job *job;
+    int begin, end;
+} typical_slice;
+
+static void *typical_worker(void *arg)
+{
+    const typical_slice *S = (const typical_slice *)arg;
+    double *p = (double *)malloc(sizeof(double) * (size_t)S->job->V);
+    if (!p)
+        return (void *)1;
+    for (int b = S->begin; b < S->end; ++b)
+        typical_one(S->job, b, p);
+    free(p);
+    return NULL;
+}
+
+/*
+ * Typical acceptance for B sequences.  Shapes as oracle_sample (no draft
+ * probabilities); temperature [B] or NULL.  Outputs: num_accepted [B],
+ * out_tokens [B][K+1], p_draft [B][K] (p~_i(x_i)) and threshold [B][K]
+ * (min(eps, delta exp(-H))) for every tested position, NaN after the first
+ * rejection; near_pos [B]: first position whose test lies within near_eps of
+ * its threshold, or whose draw lies within near_eps of a CDF edge.
+ */
+int oracle_sample_typical(const float *target_logits, const int32_t *draft_tokens, const float *uniforms,
+                          const float *temperature, double eps, double delta, int B, int K, int64_t V,
+                          double near_eps, int32_t *num_accepted, int32_t *out_tokens, double *p_draft,
+                          double *threshold, int32_t *near_pos, int nthreads)
+{
+    if (!target_logits || !draft_tokens || !uniforms || !num_accepted || !out_tokens || !p_draft || !threshold ||
+        !near_pos)
+        return -1;
+    if (B < 1 || K < 1 || V < 1)
+        return -1;
+    for (int64_t i = 0; i < (int64_t)B * K; ++i)
+        if (draft_tokens[i] < 0 || draft_tokens[i] >= V)
+            return -1;
+    typical_job J = {target_logits, uniforms, temperature, draft_tokens, eps, delta, B, K, V, near_eps,
+                     num_accepted, out_tokens, near_pos, p_draft, threshold};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > B)
+        nthreads = B;
+    pthread_t th[256];
+    typical_slice sl[256];
+    for (int i = 0; i < nthreads; ++i) {
+        sl[i].job = &J;
+        sl[i].begin = (int)((int64_t)B * i / nthreads);
+        sl[i].end = (int)((int64_t)B * (i + 1) / nthreads);
+    }
+    if (nthreads == 1)
+        return typical_worker(&sl[0]) ? -1 : 0;
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i)
+        pthread_create(&th[i], NULL, typical_worker, &sl[i]);
+    for (int i = 0; i < nthreads; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r)
+            rc = -1;
+    }
+    return rc;
+}
+
 /* ------------------------------------------------------------ tree sampler
  *
  * Verification of a draft tree ([KV] 8.2 and Q14: the tree's nodes are

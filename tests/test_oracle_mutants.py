@@ -16,6 +16,7 @@ from . import test_oracle_kvcache as TK
 from . import test_oracle_temperature as TT
 from . import test_oracle_topp as TP
 from . import test_oracle_tree as TR
+from . import test_oracle_typical as TY
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -61,6 +62,12 @@ TREE_PINS = [
     lambda: TR.test_exact_law_of_recursive_rejection(3),
 ]
 
+TYPICAL_PINS = [
+    TY.test_entropy_matches_library_and_closed_forms, TY.test_uniform_target_closed_form,
+    TY.test_one_hot_target_accepts_exactly_its_argmax, TY.test_zero_eps_accepts_every_positive_draft,
+    TY.test_two_token_worked_example, TY.test_token_after_the_prefix_follows_its_row,
+]
+
 # (name, original text, replacement, pins expected to catch it)
 MUTANTS = [
     ("head map h % Hkv", "const int g = h / G;", "const int g = h % Hkv;", ATTN_PINS),
@@ -97,8 +104,8 @@ MUTANTS = [
     ("temperature multiplies", "p[j] = exp(((double)logits[j] - m) / tau);", "p[j] = exp(((double)logits[j] - m) * tau);", TEMP_PINS),
     ("greedy takes the last maximum", "        if ((double)logits[j] > m) {\n            m = (double)logits[j];\n            arg = j;",
      "        if ((double)logits[j] >= m) {\n            m = (double)logits[j];\n            arg = j;", TEMP_PINS),
-    ("temperature on the draft row too", "const double tau = J->temperature ? (double)J->temperature[b] : 1.0;",
-     "const double tau = J->temperature ? (double)J->temperature[b] * 0.5 : 1.0;", TEMP_PINS),
+    ("temperature halved", "const double tau = J->temperature ? (double)J->temperature[b] : 1.0;\n    const float *lrow",
+     "const double tau = J->temperature ? (double)J->temperature[b] * 0.5 : 1.0;\n    const float *lrow", TEMP_PINS),
     ("top-p not renormalised", "        p[j] /= kept;", "        p[j] /= 1.0;", TOPP_PINS),
     ("top-p splits ties", "while (e < V && r[e].l == r[g].l)", "while (e < V && e == g)", TOPP_PINS),
     ("top-p ranks ascending", "return x->l > y->l ? -1 : 1;", "return x->l < y->l ? -1 : 1;", TOPP_PINS),
@@ -114,6 +121,15 @@ MUTANTS = [
      "!((anc >> (p - (L - T))) & 1u)) {\n            score[p] = -INFINITY;",
      "0) {\n            score[p] = -INFINITY;", TREE_PINS),
     ("tree: ancestor sets of the chain", "m[c] = m[par[c]] | (1u << c);", "m[c] = (2u << c) - 1u;", TREE_PINS),
+    ("typical: entropy sign", "h -= p[j] * log(p[j]);", "h += p[j] * log(p[j]);", TYPICAL_PINS),
+    ("typical: threshold takes the larger", "const double th = fmin(J->eps,", "const double th = fmax(J->eps,",
+     TYPICAL_PINS),
+    ("typical: exp(+H)", "J->delta * exp(-oracle_entropy(p, V))", "J->delta * exp(oracle_entropy(p, V))", TYPICAL_PINS),
+    ("typical: non-strict comparison", "if (!(p[x] > th)) {", "if (!(p[x] >= th)) {", TYPICAL_PINS),
+    ("typical: draw from the first row",
+     "oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + n) * V, V, tau, p);\n    double S = 0.0;",
+     "oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + 0) * V, V, tau, p);\n    double S = 0.0;",
+     TYPICAL_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

@@ -307,8 +307,11 @@ def main():
     samp_tp_ms = timed_launches(lambda i: sv.spec_verify_sample(
         sets[i % copies]["logits"], sets[i % copies]["probs"], sets[i % copies]["tokens"], sets[i % copies]["u"],
         n_acc, toks, ws_s, stream=stream, temperature=temp_t, top_p=cut_t), args.steps)
-    print("# sampler %.1f us, with temperature + top-p %.1f us" % (samp_b2b_ms * 1e3, samp_tp_ms * 1e3),
-          file=sys.stderr, flush=True)
+    samp_ty_ms = timed_launches(lambda i: sv.spec_verify_sample_typical(
+        sets[i % copies]["logits"], sets[i % copies]["tokens"], sets[i % copies]["u"], n_acc, toks, ws_s,
+        0.09, 0.3, stream=stream), args.steps)
+    print("# sampler %.1f us, with temperature + top-p %.1f us, typical acceptance %.1f us" % (
+        samp_b2b_ms * 1e3, samp_tp_ms * 1e3, samp_ty_ms * 1e3), file=sys.stderr, flush=True)
     # Tree verification at the same geometry: the widest tree shape whose
     # nodes fit the row tiles (N * Hq/Hkv <= 64), attention over the same
     # cache with N verify rows, and the tree sampler over N target rows.
@@ -404,6 +407,7 @@ def main():
         "sample_us": float(samp_ms.mean() * 1e3),
         "sample_us_back_to_back": float(samp_b2b_ms * 1e3),
         "sample_temp_topp_us_back_to_back": float(samp_tp_ms * 1e3),
+        "sample_typical_us_back_to_back": float(samp_ty_ms * 1e3),
         "kv_append_us_per_layer": float(append_ms * 1e3),
         "kv_append_bytes_per_layer": int(ap_bytes),
         "rollback_us": float(rollback_ms * 1e3),

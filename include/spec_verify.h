@@ -167,6 +167,27 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
  * (optional, NULL to skip) receives min(1, p_i(x_i)/q_i(x_i)) for every i.
  * 1 <= K <= 15; V >= 1.  workspace as for attention.
  * ------------------------------------------------------------------------ */
+/* Typical acceptance ("50 | Speculative Decoding" 9.1; "KV Cache +
+ * Speculative Decoding" 8.2 and Q18): NOT exact.  Draft x_i is accepted iff
+ * the target's own probability of it exceeds an entropy-based threshold,
+ *   p~_i(x_i) > min(eps, delta * exp(-H(p~_i))),
+ * with p~_i = softmax(target_logits row i / T_b) and H its entropy in nats;
+ * no draft probabilities are needed.  n = the first rejected position (or
+ * K); the next token is drawn from p~_n itself with uniforms[b][K] (inverse
+ * CDF in token order, as spec_verify_sample).  T_b <= 0 is greedy (H = 0).
+ *   temperature: [B] or NULL (1); eps, delta: finite, >= 0 (the pages give no
+ *   values: the caller's choice).
+ *   p_draft, threshold: optional [B][K] float outputs (NULL ok): p~_i(x_i)
+ *   and the threshold of every position up to the first rejection.
+ * Outputs and workspace as spec_verify_sample. */
+int spec_verify_sample_typical(const float *target_logits, const int32_t *draft_tokens,
+                               const float *uniforms, const float *temperature,
+                               double eps, double delta,
+                               int32_t *num_accepted, int32_t *out_tokens,
+                               float *p_draft, float *threshold,
+                               int B, int K, int V,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Tree verification attention ("KV Cache + Speculative Decoding" 8.2 and
  * Q14): the T nodes of a draft tree, flattened in BFS order, are the T verify
  * rows; their K/V occupy the last T cache positions (L_b - T .. L_b - 1, in

@@ -69,6 +69,8 @@ def lib():
         L.spec_verify_sample.argtypes = [P] * 7 + [I] * 3 + [P, S, P]
         L.spec_verify_sample_ex.restype = I
         L.spec_verify_sample_ex.argtypes = [P] * 9 + [I] * 3 + [P, S, P]
+        L.spec_verify_sample_typical.restype = I
+        L.spec_verify_sample_typical.argtypes = [P] * 4 + [c.c_double, c.c_double] + [P] * 4 + [I] * 3 + [P, S, P]
         L.spec_verify_sample_tree_workspace_size.restype = S
         L.spec_verify_sample_tree_workspace_size.argtypes = [I] * 3
         L.spec_verify_sample_tree.restype = I
@@ -195,6 +197,24 @@ def spec_verify_sample(target_logits, draft_probs, draft_tokens, uniforms, num_a
     _check("spec_verify_sample", lib().spec_verify_sample_ex(
         _ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature),
         _ptr(top_p), _ptr(num_accepted), _ptr(out_tokens), _ptr(accept_prob), B, K1 - 1, V,
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, target_logits.device)))
+    return num_accepted, out_tokens
+
+
+def spec_verify_sample_typical(target_logits, draft_tokens, uniforms, num_accepted, out_tokens, workspace,
+                               eps, delta, *, temperature=None, p_draft=None, threshold=None, stream=None):
+    """Typical acceptance (see include/spec_verify.h; not exact).
+
+    target_logits [B,K+1,V] f32, draft_tokens [B,K] i32, uniforms [B,K+1] f32;
+    eps, delta: the threshold min(eps, delta * exp(-H)); optional
+    temperature [B] f32; optional outputs p_draft and threshold [B,K] f32.
+    Workspace: sample_workspace_size(B, K, V).
+    """
+    B, K1, V = target_logits.shape
+    _check("spec_verify_sample_typical", lib().spec_verify_sample_typical(
+        _ptr(target_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), float(eps), float(delta),
+        _ptr(num_accepted), _ptr(out_tokens), _ptr(p_draft), _ptr(threshold), B, K1 - 1, V,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, target_logits.device)))
     return num_accepted, out_tokens

@@ -114,6 +114,8 @@ SamplePlan plan_sample(int B, int K, int V)
     off = align256(off + (size_t)B * (K + 1) * kRowCutBytes);
     pl.off_part = off;  // top-p: partial coarse histograms per chunk
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * kCutCoarse * 8);
+    pl.off_ent = off;  // typical acceptance: entropy sums per chunk
+    off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 8);
     pl.total = off;
     return pl;
 }
@@ -350,14 +352,14 @@ int spec_verify_sample(const float *target_logits, const float *draft_probs, con
                                  num_accepted, out_tokens, accept_prob, B, K, V, workspace, workspace_bytes, stream);
 }
 
-int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
-                          const float *uniforms, const float *temperature, const float *top_p,
-                          int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B, int K, int V,
-                          void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+// The chain sampler behind spec_verify_sample_ex and spec_verify_sample_typical.
+int sample_impl(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                const float *uniforms, const float *temperature, const float *top_p, bool typical, double eps,
+                double delta, int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, float *threshold,
+                int B, int K, int V, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
-        return fail(SV_ERR_NULL, "target_logits, draft_probs, draft_tokens, uniforms, num_accepted and "
-                                 "out_tokens must be non-NULL");
     if (B < 1 || K < 1 || V < 1)
         return fail(SV_ERR_SHAPE, "B, K and V must be >= 1 (got %d, %d, %d)", B, K, V);
     if (K > 15)
@@ -370,10 +372,10 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
         (long long)B * ((V + sv::kSampleSub - 1) / sv::kSampleSub) > 0x7FFFFFFFLL)
         return fail(SV_ERR_SHAPE, "B*(K+1)*ceil(V/%d) or B*ceil(V/%d) exceeds the grid limit", sv::kSampleChunk,
                     sv::kSampleSub);
-    if (!aligned(target_logits, 4) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
+    if (!aligned(target_logits, 4) || (draft_probs && !aligned(draft_probs, 4)) || !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
-        (accept_prob && !aligned(accept_prob, 4)) || (temperature && !aligned(temperature, 4)) ||
-        (top_p && !aligned(top_p, 4)))
+        (accept_prob && !aligned(accept_prob, 4)) || (threshold && !aligned(threshold, 4)) ||
+        (temperature && !aligned(temperature, 4)) || (top_p && !aligned(top_p, 4)))
         return fail(SV_ERR_ALIGN, "sampler arrays must be 4-byte aligned");
     const sv::SamplePlan pl = sv::plan_sample(B, K, V);
     if (!workspace)
@@ -392,6 +394,11 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.top_p = top_p;
     p.qrows = K;
     p.tree = 0;
+    p.typical = typical ? 1 : 0;
+    p.ty_eps = eps;
+    p.ty_delta = delta;
+    p.row_ent = reinterpret_cast<double *>(ws + pl.off_ent);
+    p.threshold_out = threshold;
     p.num_accepted = num_accepted;
     p.out_tokens = out_tokens;
     p.accept_prob = accept_prob;
@@ -405,11 +412,40 @@ int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, 
     p.K = K;
     p.V = V;
     p.nchunk = pl.nchunk;
-    p.vec4 = (V % 4 == 0) && aligned(target_logits, 16) && aligned(draft_probs, 16);
+    p.vec4 = (V % 4 == 0) && aligned(target_logits, 16) && (!draft_probs || aligned(draft_probs, 16));
     const hipError_t e = sv::launch_sample(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SV_ERR_HIP, "sampler launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+int spec_verify_sample_ex(const float *target_logits, const float *draft_probs, const int32_t *draft_tokens,
+                          const float *uniforms, const float *temperature, const float *top_p,
+                          int32_t *num_accepted, int32_t *out_tokens, float *accept_prob, int B, int K, int V,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
+        return fail(SV_ERR_NULL, "target_logits, draft_probs, draft_tokens, uniforms, num_accepted and "
+                                 "out_tokens must be non-NULL");
+    return sample_impl(target_logits, draft_probs, draft_tokens, uniforms, temperature, top_p, false, 0.0, 0.0,
+                       num_accepted, out_tokens, accept_prob, nullptr, B, K, V, workspace, workspace_bytes,
+                       stream);
+}
+
+int spec_verify_sample_typical(const float *target_logits, const int32_t *draft_tokens, const float *uniforms,
+                               const float *temperature, double eps, double delta, int32_t *num_accepted,
+                               int32_t *out_tokens, float *p_draft, float *threshold, int B, int K, int V,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!target_logits || !draft_tokens || !uniforms || !num_accepted || !out_tokens)
+        return fail(SV_ERR_NULL, "target_logits, draft_tokens, uniforms, num_accepted and out_tokens must be "
+                                 "non-NULL");
+    if (!std::isfinite(eps) || !std::isfinite(delta) || eps < 0.0 || delta < 0.0)
+        return fail(SV_ERR_SHAPE, "eps and delta must be finite and >= 0");
+    return sample_impl(target_logits, nullptr, draft_tokens, uniforms, temperature, nullptr, true, eps, delta,
+                       num_accepted, out_tokens, p_draft, threshold, B, K, V, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,

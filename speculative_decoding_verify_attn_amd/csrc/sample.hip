@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
     if (rec) {
         const int x = clamp_token(p.tokens[(size_t)b * K + i], p.V);
         rx.lx = p.logits[(size_t)row * p.V + x];
-        rx.qx = p.probs[((size_t)b * K + i) * p.V + x];
+        rx.qx = p.probs ? p.probs[((size_t)b * K + i) * p.V + x] : 0.0f;
     }
     float mx = v[0];
 #pragma unroll
@@ -220,6 +220,8 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
         for (int w = 0; w < kNWs; ++w)
             first = min(first, s_i[w]);
         st.arg = base + first;
+        if (p.typical && threadIdx.x == 0)
+            p.row_ent[(size_t)row * p.nchunk + chunk] = 0.0;
     } else {
         // exp((v - M) / T) = 2^((v - M) log2(e) / T) with the hardware exp2;
         // the constant log2(e) / T enters as two floats, so the scaled
@@ -227,13 +229,21 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
         // sends -inf entries (and a chunk that is -inf throughout, where
         // v - M is NaN) to a finite difference whose term is 0, whatever the
         // sign of the low part of the constant.
-        double z = 0.0;
+        double z = 0.0, ze = 0.0;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const float dv = fmaxf(v[k] - M, -3.0e38f);
-            z += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo));
+            const double w = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo));
+            z += w;
+            if (p.typical)  // entropy: sum of w * (l - m) / T, in nats
+                ze += w * ((double)dv * tp.inv);
         }
         st.z = block_sum(z, s_d);
+        if (p.typical) {
+            ze = block_sum(ze, s_d);
+            if (threadIdx.x == 0)
+                p.row_ent[(size_t)row * p.nchunk + chunk] = ze;
+        }
     }
     if (threadIdx.x == 0) {
         static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
@@ -775,6 +785,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     __shared__ int s_A[16];
     __shared__ float s_tau[16];
     __shared__ double s_ratio[16];
+    __shared__ double s_th[16];
     __shared__ int s_acc[16];
     __shared__ int s_n;
     __shared__ double s_part[kNWs][2];
@@ -818,7 +829,25 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         }
         const double Z = wave_sum_f64(zloc);
         const int A = wave_min_i32(aloc);
+        double H = 0.0;  // entropy of the row in nats (typical acceptance)
+        if (p.typical && !tp.greedy) {
+            // sum_j e^{a_j - A}(a_j - A) from the chunks' sums relative to
+            // their own maxima: e^{d}(s_c + d z_c), d = (m_c - M) / T
+            const double *ent = p.row_ent + (size_t)(b * K1 + i) * p.nchunk;
+            double sloc = 0.0;
+            for (int c = lane; c < p.nchunk; c += kWave) {
+                const RowStat r = st[c];
+                if (r.z > 0.0) {
+                    const double d = ((double)r.m - (double)M) * tp.inv;
+                    sloc += exp(d) * (ent[c] + d * r.z);
+                }
+            }
+            const double S = wave_sum_f64(sloc);
+            H = log(Z) - S / Z;
+        }
         if (lane == 0) {
+            if (p.typical)
+                s_th[i] = fmin(p.ty_eps, p.ty_delta * exp(-H));
             float tau = -__builtin_inff();
             double invZ = 1.0 / Z;
             if (p.row_cut) {
@@ -835,12 +864,18 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         }
     }
     __syncthreads();
-    // 2. Acceptance tests u_i * q_i(x_i) < p~_i(x_i).
+    // 2. Acceptance tests u_i * q_i(x_i) < p~_i(x_i), or for typical
+    //    acceptance p~_i(x_i) > min(eps, delta exp(-H_i)).
     if (tid < K) {
         const double a = target_prob(rx.lx, x, s_M[tid], s_Z[tid], tp, s_A[tid], s_tau[tid]);
-        const double c = (double)rx.qx;
-        s_acc[tid] = ((double)u * c < a) ? 1 : 0;
-        s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
+        if (p.typical) {
+            s_acc[tid] = (a > s_th[tid]) ? 1 : 0;
+            s_ratio[tid] = a;
+        } else {
+            const double c = (double)rx.qx;
+            s_acc[tid] = ((double)u * c < a) ? 1 : 0;
+            s_ratio[tid] = c > 0.0 ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
+        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -854,7 +889,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     }
     __syncthreads();
     const int n = s_n;
-    const bool residual = n < K;
+    const bool residual = n < K && !p.typical;  // typical: the draw is from p~_n itself
     const float M = s_M[n];
     const double invZ = s_Z[n];
     const int arg = s_A[n];
@@ -914,6 +949,8 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     }
     if (sub == 0 && p.accept_prob && tid < K)
         p.accept_prob[(size_t)b * K + tid] = (float)s_ratio[tid];
+    if (sub == 0 && p.threshold_out && tid < K)
+        p.threshold_out[(size_t)b * K + tid] = (float)s_th[tid];
 }
 
 // The draw: one workgroup per sequence.  Wave 0 prefix-scans the sub-chunk
@@ -944,7 +981,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     tp.inv = ss.inv_t;
     tp.c_hi = tp.c_lo = 0.0f;  // (row sums are not recomputed here)
     const float *lrow = p.logits + ((size_t)b * K1 + ss.row) * V;
-    const float *qrow = p.probs + ((size_t)b * p.qrows + ss.qrow) * V;
+    const float *qrow = p.probs ? p.probs + ((size_t)b * p.qrows + ss.qrow) * V : nullptr;
 
     if (tid < kWave) {
         const double *gmass = p.sub_mass + (size_t)b * nsub * 2;

@@ -73,6 +73,10 @@ struct SampleParams {
     int32_t *path;           // tree: [B][N] accepted node ids, then -1
     double *coefs;           // tree: [B][N][nchunk] chunk partials of each node's test normaliser
     int tree_max_children;   // tree: children tested per node (ranks beyond are skipped)
+    int typical;             // typical acceptance instead of the rejection rule
+    double ty_eps, ty_delta; // its threshold min(eps, delta exp(-H))
+    double *row_ent;         // typical: [B*(K+1)][nchunk] sum over the chunk of e^{a - a_max}(a - a_max)
+    float *threshold_out;    // typical: [B][K] thresholds, or null
     void *row_stats;         // [B*(K+1)][nchunk] {float max, double sum}
     void *row_x;             // [B*K] {target logit, draft probability} of draft token x_i
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}
@@ -82,7 +86,7 @@ struct SampleParams {
 
 struct SamplePlan {
     int nchunk;
-    size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, total;
+    size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, off_ent, total;
 };
 
 constexpr size_t kSeqStateBytes = 64;  // workspace bytes per sequence of the decide -> pick state

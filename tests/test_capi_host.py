@@ -101,6 +101,19 @@ def test_sample_argument_checks():
     assert ex(p, p, p, p, None, p, p, p, None, 2, 3, 1 << 20, p, 1 << 30, None) == 3
 
 
+def test_typical_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = (ctypes.addressof(buf) + 255) & ~255
+    ty = L.spec_verify_sample_typical
+    assert ty(None, p, p, None, 0.1, 0.3, p, p, None, None, 2, 3, 100, p, 1 << 14, None) == 1
+    assert ty(p, p, p, None, -0.1, 0.3, p, p, None, None, 2, 3, 100, p, 1 << 14, None) == 2
+    assert ty(p, p, p, None, 0.1, float("nan"), p, p, None, None, 2, 3, 100, p, 1 << 14, None) == 2
+    assert ty(p, p, p, None, 0.1, 0.3, p, p, None, None, 2, 16, 100, p, 1 << 14, None) == 2
+    assert ty(p, p, p, None, 0.1, 0.3, p, p, None, p + 1, 2, 3, 100, p, 1 << 14, None) == 5
+    assert ty(p, p, p, None, 0.1, 0.3, p, p, None, None, 2, 3, 100, p, 8, None) == 4
+
+
 def test_tree_argument_checks():
     L = sv.lib()
     buf = ctypes.create_string_buffer(1 << 20)

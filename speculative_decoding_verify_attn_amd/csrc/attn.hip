@@ -352,40 +352,45 @@ struct PageGeom {
     }
 };
 
-// Stores a wave's unnormalised O tile (lane: rows rt*16 + l16, head dims
-// NDT*(4*q4 + i) + t) into an LDS tile [RG*16][D+4].
-template <int D, int RG>
-__device__ __forceinline__ void tile_store(float *tile, const floatx4 (&acc)[D / 16][RG], int l16, int q4)
+// Stores row tiles rt0 .. rt0+TPH-1 of a wave's unnormalised O tile (lane:
+// rows rt*16 + l16, head dims NDT*(4*q4 + i) + t) into an LDS tile
+// [TPH*16][D+4].
+template <int D, int RG, int TPH>
+__device__ __forceinline__ void tile_store(float *tile, const floatx4 (&acc)[D / 16][RG], int l16, int q4, int rt0)
 {
     constexpr int OP = D + 4;
     constexpr int NDT = D / 16;
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt)
+    for (int rt = 0; rt < RG; ++rt) {
+        if (rt < rt0 || rt >= rt0 + TPH)
+            continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int t0 = 0; t0 < NDT; t0 += 4)
-                *reinterpret_cast<float4 *>(tile + (rt * 16 + l16) * OP + NDT * (4 * q4 + i) + t0) =
+                *reinterpret_cast<float4 *>(tile + ((rt - rt0) * 16 + l16) * OP + NDT * (4 * q4 + i) + t0) =
                     make_float4(acc[t0][rt][i], acc[t0 + 1][rt][i], acc[t0 + 2][rt][i], acc[t0 + 3][rt][i]);
+    }
 }
 
-// Merges the NT wave tiles of one workgroup and stores the result:
-// normalised output when the unit has a single split, else the unnormalised
-// partial (o, max, sum) for the merge kernel.  tiles: NT tiles [RG*16][D+4]
-// floats, `pitch` floats apart; sm/sl: per-tile row max (base-2 units) and
-// row sum.
+// Merges the NT wave tiles of rows r0 .. r1-1 of one workgroup and stores
+// the result: normalised output when the unit has a single split, else the
+// unnormalised partial (o, max, sum) for the merge kernel.  tiles: NT tiles
+// holding rows r0.. as [rows][D+4] floats, `pitch` floats apart; sm/sl:
+// per-wave row max (base-2 units) and row sum.
 template <int D, int RG, int NT>
 __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles, int pitch,
                                                       const float (*sm)[64], const float (*sl)[64],
-                                                      int unit, int split, int b, int g, int nsplit)
+                                                      int unit, int split, int b, int g, int nsplit, int r0, int r1)
 {
     constexpr int OP = D + 4;
     constexpr int C4 = D / 4;
     const float ninf = -__builtin_inff();
-    const int TG = p.TG, G = p.G;
-    const size_t pbase = ((size_t)unit * p.max_splits + split) * TG;
-    for (int idx = threadIdx.x; idx < TG * C4; idx += blockDim.x) {
-        const int row = idx / C4, c4 = idx - row * C4;
+    const int G = p.G;
+    const size_t pbase = ((size_t)unit * p.max_splits + split) * p.TG;
+    for (int idx = threadIdx.x; idx < (r1 - r0) * C4; idx += blockDim.x) {
+        const int lr = idx / C4, c4 = idx - lr * C4;
+        const int row = r0 + lr;
         float M = sm[0][row];
 #pragma unroll
         for (int v = 1; v < NT; ++v)
@@ -396,7 +401,7 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
         for (int v = 0; v < NT; ++v) {
             const float mv = sm[v][row];
             const float f = (mv == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * pitch + row * OP + c4 * 4);
+            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * pitch + lr * OP + c4 * 4);
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
             Ls += f * sl[v][row];
         }
@@ -413,15 +418,20 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
     }
 }
 
-// Waves per workgroup of the matrix-core kernel.  (Eight waves with
-// two-stage rings streamed no faster and cost a second merge round.)
+// Waves per workgroup of the matrix-core kernel, and row tiles merged per
+// epilogue phase (two phases for three or four row tiles keep the parked
+// output rows within a ring's size).  Measured: 8 waves streamed no faster
+// for bf16 (c2: 29.8 vs 28.9 us) and slower for E4M3 (c5b: 102 vs 82 us with
+// 8 waves, 121 with 6).
+template <int RG, bool FP8>
 constexpr int kMfmaWaves = 4;
+constexpr int kTilesPerPhase = 2;
 
 template <int D, int RG, bool FP8>
-__global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_kernel(AttnParams p)
 {
     typedef PageGeom<D, FP8> PG;
-    constexpr int NW = kMfmaWaves;
+    constexpr int NW = kMfmaWaves<RG, FP8>;
     constexpr int NT = 64 * NW;          // threads
     constexpr int NDC = PG::NDC;
     constexpr int NDT = PG::NDT;
@@ -432,7 +442,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
     constexpr int NS = NS0 > 4 ? 4 : NS0;
     constexpr int EB = PG::EB;
     constexpr int OP = D + 4;
-    constexpr int WT = RG * 16 * OP;     // floats of one wave's O tile
+    constexpr int TPH = RG < kTilesPerPhase ? RG : kTilesPerPhase;  // row tiles per epilogue phase
+    constexpr int WT = TPH * 16 * OP;    // floats of one wave's parked O rows
     // Each wave's LDS region holds its page ring, and at the end its O tile.
     constexpr int RW0 = NS * PG::STAGE > WT * 4 ? NS * PG::STAGE : WT * 4;
     constexpr int RW = (RW0 + 15) & ~15;
@@ -766,10 +777,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void sv_attn_mfma_kernel(AttnPa
             s_l[wave][rt * 16 + l16] = ls;
         }
     }
-    tile_store<D, RG>(reinterpret_cast<float *>(ring), acc, l16, q4);
-    __syncthreads();
-    merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, unit, split, b,
-                                     g, nsplit);
+#pragma unroll
+    for (int rt0 = 0; rt0 < RG; rt0 += TPH) {
+        if (rt0 > 0)
+            __syncthreads();  // the previous phase's tiles are consumed
+        tile_store<D, RG, TPH>(reinterpret_cast<float *>(ring), acc, l16, q4, rt0);
+        __syncthreads();
+        merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, unit, split,
+                                         b, g, nsplit, rt0 * 16, min(p.TG, (rt0 + TPH) * 16));
+    }
 }
 
 // ---------------------------------------------------------------- VALU kernel
@@ -906,7 +922,7 @@ template <int D, int RG, bool FP8>
 hipError_t launch_mfma_rg(const AttnParams &p, hipStream_t s)
 {
     auto kern = sv_attn_mfma_kernel<D, RG, FP8>;
-    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * kMfmaWaves), 0, s, p);
+    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * kMfmaWaves<RG, FP8>), 0, s, p);
     return hipGetLastError();
 }
 

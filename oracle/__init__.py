@@ -72,6 +72,8 @@ def _bind(lib):
     lib.oracle_encode_e4m3.argtypes = [c.c_float, c.c_float]
     lib.oracle_kv_append.restype = c.c_int
     lib.oracle_kv_append.argtypes = [c.c_void_p] * 8 + [c.c_int] * 7
+    lib.oracle_tree_commit.restype = c.c_int
+    lib.oracle_tree_commit.argtypes = [c.c_void_p] * 9 + [c.c_int] * 7
     lib.oracle_rollback.restype = None
     lib.oracle_rollback.argtypes = [c.c_void_p] * 3 + [c.c_int] * 2
     return lib
@@ -311,6 +313,30 @@ def target_row(logits, temperature=1.0, top_p=None, near_eps=1e-6, return_ambigu
         if amb < 0:
             raise MemoryError("oracle_top_p")
     return (out, bool(amb)) if return_ambiguous else out
+
+
+def tree_commit(path, num_accepted, k_cache, v_cache, block_table, context_lens, kv_dtype, k_scale=None,
+                v_scale=None):
+    """Keeps the root and the accepted path of each sequence's tree at
+    consecutive positions (see oracle_tree_commit).  path [B,N] (accepted
+    node ids, then anything), num_accepted [B]; the caches as stored.
+    Returns (k_cache, v_cache, context_lens, pages_in_use), all new arrays."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    lens = np.array(context_lens, dtype=np.int32, copy=True)
+    pages = np.empty_like(lens)
+    pa = np.ascontiguousarray(path, dtype=np.int32)
+    n = np.ascontiguousarray(num_accepted, dtype=np.int32)
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    B, N = pa.shape
+    Hkv, d = kc.shape[2], kc.shape[3]
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = None if v_scale is None else np.ascontiguousarray(v_scale, dtype=np.float32)
+    rc = _load().oracle_tree_commit(_ptr(pa), _ptr(n), _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(table),
+                                    _ptr(lens), _ptr(pages), B, N, Hkv, d, table.shape[1], kc.shape[0], int(kv_dtype))
+    if rc != 0:
+        raise ValueError("oracle_tree_commit rejected its arguments")
+    return kc, vc, lens, pages
 
 
 def kv_cache_bytes(ctx_len, n_layers, n_kv_heads, head_dim, bytes_per_elem, batch=1):

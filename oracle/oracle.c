@@ -1122,3 +1122,82 @@ void oracle_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t
         pages_in_use[b] = (L + 15) / 16;
     }
 }
+
+/* ------------------------------------------------------------- tree commit
+ *
+ * After tree verification ([KV] 8.2; the note of [KV] 7.6 that a paged cache
+ * rolls back by editing its bookkeeping): the sequence keeps the root (the
+ * last committed token) and the n accepted nodes of the path, in path order,
+ * at consecutive positions.  With L the length including the N nodes and
+ * base = L - N (the root's position), accepted node path[i] moves from
+ * position base + path[i] to base + 1 + i (all sources are read before any
+ * destination is written), and L becomes base + 1 + n; pages_in_use =
+ * ceil(L / 16).  Values are copied; for E4M3 storage a value that changes
+ * page is re-encoded for the destination page: decode(code) * scale_src
+ * rounded to float, then encoded as the append encodes (x / scale_dst in
+ * float, nearest even, saturating).  A chain path (path[i] = i + 1) moves
+ * nothing and is the chain's rollback with K = N - 1.
+ */
+int oracle_tree_commit(const int32_t *path, const int32_t *num_accepted, void *k_cache, void *v_cache,
+                       const float *k_scale, const float *v_scale, const int32_t *block_table,
+                       int32_t *context_lens, int32_t *pages_in_use, int B, int N, int Hkv, int d,
+                       int max_blocks, int num_blocks, int kv_dtype)
+{
+    const size_t esz = kv_dtype == OR_KV_F32 ? 4 : (kv_dtype == OR_KV_BF16 ? 2 : 1);
+    for (int b = 0; b < B; ++b) {
+        const int L = context_lens[b], n = num_accepted[b];
+        if (L < N || L > max_blocks * 16 || n < 0 || n > N - 1)
+            return -1;
+        for (int i = 0; i < n; ++i) {
+            const int c = path[(int64_t)b * N + i];
+            if (c < 1 || c > N - 1 || (i > 0 && c <= path[(int64_t)b * N + i - 1]))
+                return -1;
+        }
+        for (int p = L - N; p < L; ++p) {
+            const int page = block_table[(int64_t)b * max_blocks + p / 16];
+            if (page < 0 || page >= num_blocks)
+                return -1;
+        }
+    }
+    const size_t row = (size_t)Hkv * d;
+    unsigned char *tmp = (unsigned char *)malloc(2 * (size_t)N * row * esz + 1);
+    if (!tmp)
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        const int L = context_lens[b], n = num_accepted[b], base = L - N;
+        /* read every source row first */
+        for (int i = 0; i < n; ++i) {
+            const int p = base + path[(int64_t)b * N + i];
+            const int64_t page = block_table[(int64_t)b * max_blocks + p / 16];
+            const size_t off = ((size_t)page * 16 + p % 16) * row * esz;
+            memcpy(tmp + (2 * (size_t)i) * row * esz, (unsigned char *)k_cache + off, row * esz);
+            memcpy(tmp + (2 * (size_t)i + 1) * row * esz, (unsigned char *)v_cache + off, row * esz);
+        }
+        for (int i = 0; i < n; ++i) {
+            const int ps = base + path[(int64_t)b * N + i], pd = base + 1 + i;
+            const int64_t pgs = block_table[(int64_t)b * max_blocks + ps / 16];
+            const int64_t pgd = block_table[(int64_t)b * max_blocks + pd / 16];
+            const size_t off = ((size_t)pgd * 16 + pd % 16) * row * esz;
+            for (int which = 0; which < 2; ++which) {
+                const unsigned char *src = tmp + (2 * (size_t)i + which) * row * esz;
+                unsigned char *dst = (unsigned char *)(which ? v_cache : k_cache) + off;
+                if (kv_dtype != OR_KV_FP8_E4M3 || pgs == pgd) {
+                    memcpy(dst, src, row * esz);
+                } else {
+                    const float ss = which ? v_scale[pgs] : k_scale[pgs];
+                    const float sd = which ? v_scale[pgd] : k_scale[pgd];
+                    for (size_t e = 0; e < row; ++e) {
+                        const float x = (float)oracle_decode_e4m3(src[e]) * ss;
+                        dst[e] = oracle_encode_e4m3(x, sd);
+                    }
+                }
+            }
+        }
+        context_lens[b] = base + 1 + n;
+        if (pages_in_use)
+            pages_in_use[b] = (base + 1 + n + 15) / 16;
+    }
+    free(tmp);
+    return 0;
+}
+

@@ -17,6 +17,7 @@ from . import test_oracle_temperature as TT
 from . import test_oracle_topp as TP
 from . import test_oracle_tree as TR
 from . import test_oracle_typical as TY
+from . import test_oracle_tree_commit as TC
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -66,6 +67,13 @@ TYPICAL_PINS = [
     TY.test_entropy_matches_library_and_closed_forms, TY.test_uniform_target_closed_form,
     TY.test_one_hot_target_accepts_exactly_its_argmax, TY.test_zero_eps_accepts_every_positive_draft,
     TY.test_two_token_worked_example, TY.test_token_after_the_prefix_follows_its_row,
+]
+
+COMMIT_PINS = [
+    TC.test_chain_path_moves_nothing_and_is_the_rollback,
+    lambda: TC.test_committed_cache_is_prefix_root_and_path("bf16"),
+    lambda: TC.test_committed_cache_is_prefix_root_and_path("fp8"),
+    TC.test_attention_after_commit_sees_the_linear_sequence,
 ]
 
 # (name, original text, replacement, pins expected to catch it)
@@ -130,6 +138,12 @@ MUTANTS = [
      "oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + n) * V, V, tau, p);\n    double S = 0.0;",
      "oracle_target_row(J->target_logits + ((int64_t)b * (K + 1) + 0) * V, V, tau, p);\n    double S = 0.0;",
      TYPICAL_PINS),
+    ("tree commit: destinations one early", "const int ps = base + path[(int64_t)b * N + i], pd = base + 1 + i;",
+     "const int ps = base + path[(int64_t)b * N + i], pd = base + i;", COMMIT_PINS),
+    ("tree commit: length without the root", "context_lens[b] = base + 1 + n;", "context_lens[b] = base + n;",
+     COMMIT_PINS),
+    ("tree commit: E4M3 codes copied across pages", "if (kv_dtype != OR_KV_FP8_E4M3 || pgs == pgd) {",
+     "if (1) {", COMMIT_PINS),
     ("max not subtracted properly", "p[j] = exp((double)logits[j] - m);", "p[j] = exp((double)logits[j] - m) + 1e-3;", SAMPLE_PINS),
 ]
 

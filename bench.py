@@ -357,12 +357,26 @@ def main():
             tree_samp_ms = timed_launches(lambda i: sv.spec_verify_sample_tree(
                 tsets[i % len(tsets)]["logits"], tsets[i % len(tsets)]["probs"], ttok, tpar, tu, tn, tot, tpath,
                 ws_ts, max(tshape), stream=stream), args.steps)
+            # committing the accepted paths (moves K/V within the cache of copy 0;
+            # the lengths shrink from call to call and are clamped at N, which
+            # only moves the work to other pages)
+            path_np = tpath.cpu().numpy()
+            tn_np = tn.cpu().numpy()
+            cpath = torch.from_numpy(np.ascontiguousarray(path_np[:a.B] if path_np.shape[0] >= a.B else
+                                                          np.resize(path_np, (a.B, N)))).to(dev)
+            cn = torch.from_numpy(np.ascontiguousarray(np.resize(tn_np, a.B).astype(np.int32))).to(dev)
+            clens = sets[0]["lens"].clone()
+            tree_commit_ms = timed_launches(lambda i: sv.spec_verify_tree_commit(
+                cpath, cn, sets[0]["k"], sets[0]["v"], sets[0]["table"], clens,
+                k_scale=sets[0].get("ks"), v_scale=sets[0].get("vs"), kv_dtype=a.kv_dtype, stream=stream), args.steps)
             tree_bytes = attn_bytes + 2 * a.B * (N - a.T) * a.Hq * a.d * 4
             tree = {"shape": tname, "nodes": N, "attn_us": tree_attn_ms * 1e3,
                     "attn_gbs": tree_bytes / (tree_attn_ms * 1e-3) / 1e9, "sample_us": tree_samp_ms * 1e3,
+                    "commit_us": tree_commit_ms * 1e3,
                     "mean_accepted": float(tn.float().mean().item())}
-            print("# tree %s (N=%d): attention %.1f us, sampler %.1f us (inputs %.1f s)" % (
-                tname, N, tree_attn_ms * 1e3, tree_samp_ms * 1e3, time.time() - t_gen), file=sys.stderr, flush=True)
+            print("# tree %s (N=%d): attention %.1f us, sampler %.1f us, commit %.1f us (inputs %.1f s)" % (
+                tname, N, tree_attn_ms * 1e3, tree_samp_ms * 1e3, tree_commit_ms * 1e3, time.time() - t_gen),
+                file=sys.stderr, flush=True)
             del tsets, tl
     ap_bytes = 2 * k_new.numel() * (4 + {W.KV_F32: 4, W.KV_BF16: 2, W.KV_FP8_E4M3: 1}[a.kv_dtype]) + 4 * a.B * (a.T + 1)
     print("# append %.1f us, rollback %.1f us" % (append_ms * 1e3, rollback_ms * 1e3), file=sys.stderr, flush=True)

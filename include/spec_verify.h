@@ -337,6 +337,31 @@ int spec_verify_kv_append(const float *k_new, const float *v_new, void *k_cache,
 int spec_verify_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
                          void *stream);
 
+/* Tree commit ("KV Cache + Speculative Decoding" 8.2, with 7.6's note that a
+ * paged cache rolls back by editing its bookkeeping): after
+ * spec_verify_sample_tree, each sequence keeps the root (the last committed
+ * token, at base = L_b - N) and the n_b accepted nodes of the path, in path
+ * order, at the consecutive positions base+1 .. base+n_b: node path[b][i]
+ * moves from base + path[b][i] to base + 1 + i (all K and V heads), then
+ * context_lens[b] = base + 1 + n_b and, if pages_in_use is non-NULL,
+ * pages_in_use[b] = ceil(that / 16).  The drawn token is appended next
+ * round, as after spec_verify_rollback; a chain path (path[i] = i + 1) moves
+ * nothing and equals spec_verify_rollback with K = N - 1.
+ * E4M3: a value that changes page is re-encoded for the destination page
+ * (decode * scale_src in float, then x / scale_dst encoded as
+ * spec_verify_kv_append encodes); scales are never rewritten.
+ *   path [B][N], num_accepted [B]: as written by spec_verify_sample_tree
+ *   (entries past n_b are not read).  Out-of-contract data is clamped
+ *   (results undefined, memory-safe).  Two launches; no workspace.
+ *   N <= 16, d a multiple of 4 up to 256, block_size 16. */
+int spec_verify_tree_commit(const int32_t *path, const int32_t *num_accepted,
+                            void *k_cache, void *v_cache,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *block_table, int32_t *context_lens,
+                            int32_t *pages_in_use, int B, int N, int Hkv, int d,
+                            int block_size, int max_blocks_per_seq, int num_blocks,
+                            int kv_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,6 +77,8 @@ def lib():
         L.spec_verify_sample_tree.argtypes = [P] * 9 + [I] * 4 + [P, S, P]
         L.spec_verify_kv_append.restype = I
         L.spec_verify_kv_append.argtypes = [P] * 8 + [I] * 8 + [P]
+        L.spec_verify_tree_commit.restype = I
+        L.spec_verify_tree_commit.argtypes = [P] * 9 + [I] * 8 + [P]
         L.spec_verify_rollback.restype = I
         L.spec_verify_rollback.argtypes = [P] * 3 + [I] * 2 + [P]
         if L.sv_abi_version() != 1:
@@ -267,3 +269,19 @@ def spec_verify_rollback(num_accepted, context_lens, K, pages_in_use=None, strea
         _ptr(num_accepted), _ptr(context_lens), _ptr(pages_in_use), context_lens.shape[0], int(K),
         _stream_handle(stream, context_lens.device)))
     return context_lens, pages_in_use
+
+
+def spec_verify_tree_commit(path, num_accepted, k_cache, v_cache, block_table, context_lens, *, pages_in_use=None,
+                            k_scale=None, v_scale=None, kv_dtype=None, stream=None):
+    """Keeps the root and the accepted path of each tree at consecutive
+    positions and updates context_lens (see include/spec_verify.h)."""
+    B, N = path.shape
+    num_blocks, bs, Hkv, d = k_cache.shape
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    _check("spec_verify_tree_commit", lib().spec_verify_tree_commit(
+        _ptr(path), _ptr(num_accepted), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), _ptr(pages_in_use), B, N, Hkv, d, bs, block_table.shape[1],
+        num_blocks, int(kv_dtype), _stream_handle(stream, k_cache.device)))
+    return context_lens
+

@@ -586,4 +586,56 @@ int spec_verify_sample_tree(const float *target_logits, const float *draft_probs
     return ok();
 }
 
+int spec_verify_tree_commit(const int32_t *path, const int32_t *num_accepted, void *k_cache, void *v_cache,
+                            const float *k_scale, const float *v_scale, const int32_t *block_table,
+                            int32_t *context_lens, int32_t *pages_in_use, int B, int N, int Hkv, int d,
+                            int block_size, int max_blocks_per_seq, int num_blocks, int kv_dtype, void *stream)
+{
+    if (!path || !num_accepted || !k_cache || !v_cache || !block_table || !context_lens)
+        return fail(SV_ERR_NULL, "path, num_accepted, k_cache, v_cache, block_table and context_lens must be "
+                                 "non-NULL");
+    if (B < 1 || N < 1 || N > 16 || Hkv < 1 || d < 4 || d % 4 != 0 || d > 256 || max_blocks_per_seq < 1 ||
+        num_blocks < 1)
+        return fail(SV_ERR_SHAPE, "need B >= 1, 1 <= N <= 16, Hkv >= 1, d a multiple of 4 in [4, 256], "
+                                  "max_blocks_per_seq >= 1, num_blocks >= 1 (got %d, %d, %d, %d, %d, %d)",
+                    B, N, Hkv, d, max_blocks_per_seq, num_blocks);
+    if ((long long)B * Hkv > 0x7FFFFFFFLL || (long long)max_blocks_per_seq * sv::kBlock > 0x7FFFFFFFLL)
+        return fail(SV_ERR_SHAPE, "B*Hkv or max_blocks_per_seq too large");
+    if (block_size != sv::kBlock)
+        return fail(SV_ERR_UNSUPPORTED, "block_size must be %d (got %d)", sv::kBlock, block_size);
+    if (kv_dtype != SV_KV_F32 && kv_dtype != SV_KV_BF16 && kv_dtype != SV_KV_FP8_E4M3)
+        return fail(SV_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+    const bool fp8 = kv_dtype == SV_KV_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale))
+        return fail(SV_ERR_NULL, "k_scale and v_scale are required for E4M3 storage");
+    if (!fp8 && (k_scale || v_scale))
+        return fail(SV_ERR_SHAPE, "k_scale / v_scale must be NULL unless kv_dtype is E4M3");
+    const int align = kv_dtype == SV_KV_F32 ? 16 : (kv_dtype == SV_KV_BF16 ? 8 : 4);
+    if (!aligned(k_cache, align) || !aligned(v_cache, align) || !aligned(path, 4) || !aligned(num_accepted, 4) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4) || (pages_in_use && !aligned(pages_in_use, 4)) ||
+        (k_scale && !aligned(k_scale, 4)) || (v_scale && !aligned(v_scale, 4)))
+        return fail(SV_ERR_ALIGN, "k_cache / v_cache must be %d-byte aligned, the int and scale arrays 4-byte",
+                    align);
+    sv::TreeCommitParams p{};
+    p.path = path;
+    p.num_accepted = num_accepted;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.pages_in_use = pages_in_use;
+    p.B = B;
+    p.N = N;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    const hipError_t e = sv::launch_tree_commit(p, kv_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "tree commit launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -11,6 +11,7 @@
 // code of x / scale[page] (the quotient is an IEEE float division; nearest,
 // ties to even; saturating at +-448; NaN -> the NaN code).
 // Rollback: one thread per sequence, L_b <- L_b - K + n_b.
+// Tree commit: the accepted path's K/V moved next to the root (below).
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -112,7 +113,140 @@ __global__ __launch_bounds__(256) void sv_rollback_kernel(const int32_t *num_acc
         pages_in_use[b] = (L + kBlock - 1) / kBlock;
 }
 
+// ------------------------------------------------------------- tree commit
+//
+// After tree verification the root (position base = L - N) stays and the
+// accepted path's nodes move from base + path[i] to base + 1 + i.  One
+// workgroup per (sequence, KV head) reads every moved row (K and V, d
+// elements) into registers, then writes them after a barrier, since a
+// destination can be another move's source.  E4M3 values that change page
+// are re-encoded for the destination page: decode * scale_src in float, then
+// the append's encoder of x / scale_dst.  The lengths are updated by a second
+// launch, after every workgroup has read them.
+constexpr int kCommitThreads = 256;
+constexpr int kCommitPer = 4;  // (node, quad) pairs per thread: N-1 <= 15 nodes x d/4 <= 64 quads
+
+__device__ __forceinline__ float e4m3_value(uint32_t code)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+template <int KVT>
+__global__ __launch_bounds__(kCommitThreads) void sv_tree_commit_kernel(TreeCommitParams p)
+{
+    const int b = blockIdx.x / p.Hkv, g = blockIdx.x - (blockIdx.x / p.Hkv) * p.Hkv;
+    const int N = p.N, quads = p.d >> 2;
+    const int Lmax = p.max_blocks * kBlock;
+    int L = p.context_lens[b];
+    L = L < N ? N : (L > Lmax ? Lmax : L);
+    int n = p.num_accepted[b];
+    n = n < 0 ? 0 : (n > N - 1 ? N - 1 : n);
+    const int base = L - N;
+    auto page_of = [&](int pos) {
+        const int pg = p.block_table[(size_t)b * p.max_blocks + pos / kBlock];
+        return pg < 0 ? 0 : (pg >= p.num_blocks ? p.num_blocks - 1 : pg);
+    };
+    auto row_off = [&](int page, int pos) {
+        return (((size_t)page * kBlock + pos % kBlock) * p.Hkv + g) * p.d;
+    };
+    uint4 kx[kCommitPer], vx[kCommitPer];
+    int src_page[kCommitPer];
+#pragma unroll
+    for (int j = 0; j < kCommitPer; ++j) {
+        const int idx = threadIdx.x + j * kCommitThreads;
+        src_page[j] = 0;
+        kx[j] = vx[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (idx < n * quads) {
+            const int i = idx / quads, c4 = idx - i * quads;
+            int c = p.path[(size_t)b * N + i];
+            c = c < 1 ? 1 : (c > N - 1 ? N - 1 : c);
+            const int ps = base + c;
+            const int pg = page_of(ps);
+            src_page[j] = pg;
+            const size_t e = row_off(pg, ps) + (size_t)c4 * 4;
+            if constexpr (KVT == 0) {
+                kx[j] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.k_cache) + e);
+                vx[j] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.v_cache) + e);
+            } else if constexpr (KVT == 1) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k_cache) + e);
+                const uint2 c2 = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v_cache) + e);
+                kx[j].x = a.x; kx[j].y = a.y;
+                vx[j].x = c2.x; vx[j].y = c2.y;
+            } else {
+                kx[j].x = *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.k_cache) + e);
+                vx[j].x = *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.v_cache) + e);
+            }
+        }
+    }
+    __syncthreads();  // every source row is read before any destination is written
+#pragma unroll
+    for (int j = 0; j < kCommitPer; ++j) {
+        const int idx = threadIdx.x + j * kCommitThreads;
+        if (idx >= n * quads)
+            continue;
+        const int i = idx / quads, c4 = idx - i * quads;
+        const int pd = base + 1 + i;
+        const int pg = page_of(pd);
+        const size_t e = row_off(pg, pd) + (size_t)c4 * 4;
+        if constexpr (KVT == 0) {
+            *reinterpret_cast<uint4 *>(static_cast<float *>(p.k_cache) + e) = kx[j];
+            *reinterpret_cast<uint4 *>(static_cast<float *>(p.v_cache) + e) = vx[j];
+        } else if constexpr (KVT == 1) {
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.k_cache) + e) = make_uint2(kx[j].x, kx[j].y);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.v_cache) + e) = make_uint2(vx[j].x, vx[j].y);
+        } else {
+            uint32_t kc = kx[j].x, vc = vx[j].x;
+            if (pg != src_page[j]) {
+                const float kss = p.k_scale[src_page[j]], ksd = p.k_scale[pg];
+                const float vss = p.v_scale[src_page[j]], vsd = p.v_scale[pg];
+                uint32_t k2 = 0, v2 = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float xk = e4m3_value((kc >> (8 * t)) & 0xFFu) * kss;
+                    const float xv = e4m3_value((vc >> (8 * t)) & 0xFFu) * vss;
+                    k2 |= e4m3_code(xk / ksd) << (8 * t);
+                    v2 |= e4m3_code(xv / vsd) << (8 * t);
+                }
+                kc = k2;
+                vc = v2;
+            }
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.k_cache) + e) = kc;
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.v_cache) + e) = vc;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void sv_tree_length_kernel(const int32_t *num_accepted, int32_t *context_lens,
+                                                             int32_t *pages_in_use, int B, int N, int Lmax)
+{
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= B)
+        return;
+    int L = context_lens[b];
+    L = L < N ? N : (L > Lmax ? Lmax : L);
+    int n = num_accepted[b];
+    n = n < 0 ? 0 : (n > N - 1 ? N - 1 : n);
+    L = L - N + 1 + n;
+    context_lens[b] = L;
+    if (pages_in_use)
+        pages_in_use[b] = (L + kBlock - 1) / kBlock;
+}
+
 }  // namespace
+
+hipError_t launch_tree_commit(const TreeCommitParams &p, int kv_dtype, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.B * p.Hkv)), block(kCommitThreads);
+    if (kv_dtype == 0)
+        hipLaunchKernelGGL(sv_tree_commit_kernel<0>, grid, block, 0, stream, p);
+    else if (kv_dtype == 1)
+        hipLaunchKernelGGL(sv_tree_commit_kernel<1>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(sv_tree_commit_kernel<2>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(sv_tree_length_kernel, dim3((unsigned)((p.B + 255) / 256)), dim3(256), 0, stream,
+                       p.num_accepted, p.context_lens, p.pages_in_use, p.B, p.N, p.max_blocks * kBlock);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendParams &p, int kv_dtype, hipStream_t stream)
 {

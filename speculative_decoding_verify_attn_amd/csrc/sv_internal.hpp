@@ -119,6 +119,21 @@ struct AppendParams {
     int B, T, Hkv, d, max_blocks, num_blocks;
 };
 
+// Moving the accepted path of a tree next to its root.
+struct TreeCommitParams {
+    const int32_t *path;          // [B][N] accepted node ids
+    const int32_t *num_accepted;  // [B]
+    void *k_cache;
+    void *v_cache;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *block_table;
+    int32_t *context_lens;
+    int32_t *pages_in_use;
+    int B, N, Hkv, d, max_blocks, num_blocks;
+};
+hipError_t launch_tree_commit(const TreeCommitParams &p, int kv_dtype, hipStream_t stream);
+
 hipError_t launch_kv_append(const AppendParams &p, int kv_dtype, hipStream_t stream);
 hipError_t launch_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
                            hipStream_t stream);

@@ -137,6 +137,26 @@ def test_tree_argument_checks():
     assert at(*args) == 2
 
 
+def test_tree_commit_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = (ctypes.addressof(buf) + 255) & ~255
+    tc = L.spec_verify_tree_commit
+    args = [p, p, p, p, None, None, p, p, None, 2, 6, 2, 64, 16, 4, 8, 1, None]
+    a = list(args); a[0] = None
+    assert tc(*a) == 1
+    a = list(args); a[10] = 17           # N > 16
+    assert tc(*a) == 2
+    a = list(args); a[12] = 260          # d > 256
+    assert tc(*a) == 2
+    a = list(args); a[13] = 32           # block size
+    assert tc(*a) == 3
+    a = list(args); a[16] = 2            # E4M3 without scales
+    assert tc(*a) == 1
+    a = list(args); a[2] = p + 4         # bf16 cache needs 8-byte alignment
+    assert tc(*a) == 5
+
+
 def test_workspace_queries():
     assert sv.attn_workspace_size(8, 6, 32, 8, 128, 256) > 0
     assert sv.lib().spec_verify_attn_workspace_size(8, 6, 30, 8, 128, 256) == 0

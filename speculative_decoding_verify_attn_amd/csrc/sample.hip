@@ -809,45 +809,15 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
         u = p.uniforms[(size_t)b * K1 + tid];
         x = clamp_token(p.tokens[(size_t)b * K + tid], V);
     }
-    for (int i = wave; i < K1; i += kNWs) {
-        const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
-        float mloc = -__builtin_inff();
-        for (int c = lane; c < p.nchunk; c += kWave)
-            mloc = fmaxf(mloc, st[c].m);
-        const float M = wave_max_f32(mloc);
-        double zloc = 0.0;
-        int aloc = 0x7FFFFFFF;
-        for (int c = lane; c < p.nchunk; c += kWave) {
-            const RowStat r = st[c];
-            if (tp.greedy) {
-                if (r.m == M && r.arg < aloc)
-                    aloc = r.arg;  // chunks are in index order: the first maximal chunk
-            } else {
-                if (r.z > 0.0)  // a chunk that is -inf throughout adds nothing
-                    zloc += r.z * exp(((double)r.m - (double)M) * tp.inv);
-            }
-        }
-        const double Z = wave_sum_f64(zloc);
-        const int A = wave_min_i32(aloc);
-        double H = 0.0;  // entropy of the row in nats (typical acceptance)
-        if (p.typical && !tp.greedy) {
-            // sum_j e^{a_j - A}(a_j - A) from the chunks' sums relative to
-            // their own maxima: e^{d}(s_c + d z_c), d = (m_c - M) / T
-            const double *ent = p.row_ent + (size_t)(b * K1 + i) * p.nchunk;
-            double sloc = 0.0;
-            for (int c = lane; c < p.nchunk; c += kWave) {
-                const RowStat r = st[c];
-                if (r.z > 0.0) {
-                    const double d = ((double)r.m - (double)M) * tp.inv;
-                    sloc += exp(d) * (ent[c] + d * r.z);
-                }
-            }
-            const double S = wave_sum_f64(sloc);
-            H = log(Z) - S / Z;
-        }
+    // Per row: maximum, 1/Z (or the top-p cut's 1/kept mass), first argmax
+    // (greedy rows) and the typical-acceptance threshold, from the chunk
+    // statistics of lane c = chunk c (and further chunks c + 64k).
+    auto finish_row = [&](int i, float M, double Z, int A, double S) {
         if (lane == 0) {
-            if (p.typical)
+            if (p.typical) {
+                const double H = tp.greedy ? 0.0 : log(Z) - S / Z;  // entropy in nats
                 s_th[i] = fmin(p.ty_eps, p.ty_delta * exp(-H));
+            }
             float tau = -__builtin_inff();
             double invZ = 1.0 / Z;
             if (p.row_cut) {
@@ -861,6 +831,76 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
             s_Z[i] = invZ;
             s_A[i] = A;
             s_tau[i] = tau;
+        }
+    };
+    if (p.nchunk <= kWave) {
+        // every row of this wave (rows wave, wave + 4, ..) requested at once
+        constexpr int kRowsPerWave = 16 / kNWs;
+        RowStat rs[kRowsPerWave];
+        double re[kRowsPerWave];
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j) {
+            const int i = wave + j * kNWs;
+            rs[j] = RowStat{-__builtin_inff(), 0x7FFFFFFF, 0.0};
+            re[j] = 0.0;
+            if (i < K1 && lane < p.nchunk) {
+                rs[j] = static_cast<const RowStat *>(p.row_stats)[(size_t)(b * K1 + i) * p.nchunk + lane];
+                if (p.typical)
+                    re[j] = p.row_ent[(size_t)(b * K1 + i) * p.nchunk + lane];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j) {
+            const int i = wave + j * kNWs;
+            if (i >= K1)
+                break;  // uniform
+            const float M = wave_max_f32(rs[j].m);
+            double z = 0.0, sl = 0.0;
+            int al = 0x7FFFFFFF;
+            if (lane < p.nchunk) {
+                if (tp.greedy) {
+                    if (rs[j].m == M)
+                        al = rs[j].arg;
+                } else if (rs[j].z > 0.0) {
+                    const double d = ((double)rs[j].m - (double)M) * tp.inv;
+                    const double e = exp(d);
+                    z = rs[j].z * e;
+                    if (p.typical)
+                        sl = e * (re[j] + d * rs[j].z);  // e^{d}(s_c + d z_c), d = (m_c - M) / T
+                }
+            }
+            const double Z = wave_sum_f64(z);
+            const int A = wave_min_i32(al);
+            const double S = p.typical ? wave_sum_f64(sl) : 0.0;
+            finish_row(i, M, Z, A, S);
+        }
+    } else {
+        for (int i = wave; i < K1; i += kNWs) {
+            const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
+            float mloc = -__builtin_inff();
+            for (int c = lane; c < p.nchunk; c += kWave)
+                mloc = fmaxf(mloc, st[c].m);
+            const float M = wave_max_f32(mloc);
+            double zloc = 0.0, sloc = 0.0;
+            int aloc = 0x7FFFFFFF;
+            const double *ent = p.row_ent + (size_t)(b * K1 + i) * p.nchunk;
+            for (int c = lane; c < p.nchunk; c += kWave) {
+                const RowStat r = st[c];
+                if (tp.greedy) {
+                    if (r.m == M && r.arg < aloc)
+                        aloc = r.arg;  // chunks are in index order: the first maximal chunk
+                } else if (r.z > 0.0) {  // a chunk that is -inf throughout adds nothing
+                    const double d = ((double)r.m - (double)M) * tp.inv;
+                    const double e = exp(d);
+                    zloc += r.z * e;
+                    if (p.typical)
+                        sloc += e * (ent[c] + d * r.z);
+                }
+            }
+            const double Z = wave_sum_f64(zloc);
+            const int A = wave_min_i32(aloc);
+            const double S = p.typical ? wave_sum_f64(sloc) : 0.0;
+            finish_row(i, M, Z, A, S);
         }
     }
     __syncthreads();
@@ -983,12 +1023,32 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const float *lrow = p.logits + ((size_t)b * K1 + ss.row) * V;
     const float *qrow = p.probs ? p.probs + ((size_t)b * p.qrows + ss.qrow) * V : nullptr;
 
+    // The draw's uniform is column K (chain) or 0 (tree): both are requested
+    // with the state, before the column is known.
+    const float u_chain = p.uniforms[(size_t)b * K1 + K], u_tree = p.uniforms[(size_t)b * K1];
     if (tid < kWave) {
         const double *gmass = p.sub_mass + (size_t)b * nsub * 2;
+        constexpr int kRegSub = 4;  // sub-chunk masses held per lane (nsub <= 256)
+        double wr[kRegSub], pr[kRegSub];
+        const bool in_regs = nsub <= kRegSub * kWave;
         double sw = 0.0, sp = 0.0;
-        for (int c = lane; c < nsub; c += kWave) {
-            sw += gmass[2 * c];
-            sp += gmass[2 * c + 1];
+        if (in_regs) {
+#pragma unroll
+            for (int k = 0; k < kRegSub; ++k) {
+                const int c = lane + k * kWave;
+                wr[k] = c < nsub ? gmass[2 * c] : 0.0;
+                pr[k] = c < nsub ? gmass[2 * c + 1] : 0.0;
+            }
+#pragma unroll
+            for (int k = 0; k < kRegSub; ++k) {
+                sw += wr[k];
+                sp += pr[k];
+            }
+        } else {
+            for (int c = lane; c < nsub; c += kWave) {
+                sw += gmass[2 * c];
+                sp += gmass[2 * c + 1];
+            }
         }
         double S = wave_sum_f64(sw);
         int mode = 0;  // 0: residual/bonus weights, 1: fallback to p_n
@@ -996,13 +1056,22 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
             mode = 1;
             S = wave_sum_f64(sp);
         }
-        const double tgt = (double)p.uniforms[(size_t)b * K1 + ss.ucol] * S;
+        const float uf = ss.ucol == K ? u_chain : (ss.ucol == 0 ? u_tree : p.uniforms[(size_t)b * K1 + ss.ucol]);
+        const double tgt = (double)uf * S;
         double carry = 0.0, cum = 0.0;
         int cstar = -1, lastpos = -1;
         double cum_last = 0.0;
-        for (int c0 = 0; c0 < nsub; c0 += kWave) {
+        for (int c0 = 0, k = 0; c0 < nsub; c0 += kWave, ++k) {
             const int c = c0 + lane;
-            const double mc = c < nsub ? gmass[2 * c + mode] : 0.0;
+            double mc = 0.0;
+            if (in_regs) {
+#pragma unroll
+                for (int kk = 0; kk < kRegSub; ++kk)
+                    if (kk == k)
+                        mc = mode ? pr[kk] : wr[kk];
+            } else {
+                mc = c < nsub ? gmass[2 * c + mode] : 0.0;
+            }
             const double incl = wave_inclusive_scan_f64(mc) + carry;
             const uint64_t hit = __ballot(c < nsub && incl > tgt);
             const uint64_t pos = __ballot(c < nsub && mc > 0.0);

@@ -66,3 +66,111 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for r, x in zip(ref2, other):
             assert torch.equal(r, x)
+
+
+def _same_bits(a, b):
+    """Bitwise equality (NaN-poisoned cache slots compare equal to themselves)."""
+    if a.is_floating_point():
+        a = a.view({2: torch.int16, 4: torch.int32, 8: torch.int64}[a.element_size()])
+        b = b.view(a.dtype)
+    return torch.equal(a, b)
+
+
+def _replays_match(make_call, outputs, dev, reps=4):
+    """Captures make_call(out, stream) on a side stream; each replay must equal
+    the eager result, with an eager call on other inputs in between."""
+    ref = outputs()
+    make_call(ref, None, 0)
+    ref2 = outputs()
+    make_call(ref2, None, 1)
+    torch.cuda.synchronize()
+    got = outputs()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            make_call(got, side, 0)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    other = outputs()
+    for rep in range(reps):
+        for x in got:
+            x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for r, x in zip(ref, got):
+            assert _same_bits(r, x), "replay %d differs from eager" % rep
+        make_call(other, None, 1)
+        torch.cuda.synchronize()
+        for r, x in zip(ref2, other):
+            assert _same_bits(r, x)
+
+
+def test_graph_replay_sampler_variants():
+    """Temperature + top-p, and typical acceptance, captured and replayed."""
+    dev = torch.device("cuda", 0)
+    ss = [W.make_sample_from_params(33 + i, 4, 5, 40000, 2.0, 0.7) for i in range(2)]
+    ts = [upload_sample(s) for s in ss]
+    s = ss[0]
+    ws = sv.alloc_workspace(sv.sample_workspace_size(s.B, s.K, s.V), dev)
+    temp = torch.tensor([0.7, 1.0, 1.3, 0.0], dtype=torch.float32, device=dev)
+    cut = torch.tensor([0.9, 0.5, 1.0, 0.8], dtype=torch.float32, device=dev)
+
+    def outputs():
+        return (torch.empty(s.B, dtype=torch.int32, device=dev),
+                torch.empty((s.B, s.K + 1), dtype=torch.int32, device=dev))
+
+    def topp(o, stream, which):
+        t = ts[which]
+        sv.spec_verify_sample(t["logits"], t["probs"], t["tokens"], t["u"], o[0], o[1], ws, stream=stream,
+                              temperature=temp, top_p=cut)
+
+    def typical(o, stream, which):
+        t = ts[which]
+        sv.spec_verify_sample_typical(t["logits"], t["tokens"], t["u"], o[0], o[1], ws, 0.09, 0.3,
+                                      temperature=temp, stream=stream)
+
+    _replays_match(topp, outputs, dev)
+    _replays_match(typical, outputs, dev)
+
+
+def test_graph_replay_tree_sampler_and_commit():
+    dev = torch.device("cuda", 0)
+    par = W.tree_parents(W.TREE_SHAPES["wide5x2"])
+    N = par.shape[0]
+    trees = [W.make_tree(35 + i, 4, par, 20000, 2.0, 0.5) for i in range(2)]
+    up = lambda x: torch.from_numpy(x).to(dev)
+    tt = [{k: up(getattr(t, k)) for k in ("target_logits", "draft_probs", "tokens", "parents", "uniforms")}
+          for t in trees]
+    ws = sv.alloc_workspace(sv.sample_tree_workspace_size(4, N, 20000), dev)
+
+    def outputs():
+        return (torch.empty(4, dtype=torch.int32, device=dev), torch.empty((4, N), dtype=torch.int32, device=dev),
+                torch.empty((4, N), dtype=torch.int32, device=dev))
+
+    def tree(o, stream, which):
+        t = tt[which]
+        sv.spec_verify_sample_tree(t["target_logits"], t["draft_probs"], t["tokens"], t["parents"], t["uniforms"],
+                                   o[0], o[1], o[2], ws, 5, stream=stream)
+
+    _replays_match(tree, outputs, dev)
+
+    # the commit: each call starts from a fresh copy of the cache and lengths
+    a = W.make_attn_from_lens(37, 4, N, 16, 4, 64, [40, 77, 100, 300], kv="bf16")
+    base = upload_attn(a)
+    res = outputs()
+    tree(res, None, 0)
+    torch.cuda.synchronize()
+
+    def commit(o, stream, which):
+        k, v, lens = o
+        k.copy_(base["k"])
+        v.copy_(base["v"])
+        lens.copy_(base["lens"])
+        sv.spec_verify_tree_commit(res[2], res[0], k, v, base["table"], lens, kv_dtype=a.kv_dtype, stream=stream)
+
+    def commit_outputs():
+        return (torch.empty_like(base["k"]), torch.empty_like(base["v"]), torch.empty_like(base["lens"]))
+
+    _replays_match(commit, commit_outputs, dev)

@@ -115,3 +115,38 @@ def test_config_ragged_full_size():
     print("c4 max row rel err %.3e" % err)
     assert err <= TOL[a.kv_dtype]
     assert torch.isfinite(out).all()
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        T = int(rng.integers(1, 17))
+        if T * G > 64:
+            continue
+        B = int(rng.integers(1, 6))
+        kv = str(rng.choice(["f32", "bf16", "fp8"]))
+        lens = [int(rng.integers(T, 900)) for _ in range(B)]
+        bps = int(rng.choice([0, 4, 8, 32]))
+        out.append((len(out), B, T, Hkv * G, Hkv, d, lens, kv, bps))
+    return out
+
+
+RANDOM = _random_shapes(24, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[str(c[0]) for c in RANDOM])
+def test_random_shapes(case):
+    """Seeded random shapes: every GQA ratio and head count, 1 to 16 verify
+    rows, ragged lengths, all storage types, forced context splits, both
+    kernels (bf16/E4M3 also through the vector-ALU kernel)."""
+    i, B, T, Hq, Hkv, d, lens, kv, bps = case
+    a = W.make_attn_from_lens(500 + i, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=2)
+    algos = [sv.SV_ATTN_AUTO] + ([sv.SV_ATTN_VALU] if kv != "f32" else [])
+    for algo in algos:
+        out = run_attn(a, algo=algo, blocks_per_split=bps)
+        err = _check(a, out)
+        assert err <= TOL[a.kv_dtype], (case, algo, err)

@@ -46,6 +46,27 @@ namespace {
 
 constexpr float kSlack = 8.0f;  // base-2 headroom before the running max is moved
 
+// Clamped context length and its page count (the same everywhere a unit's pages
+// are counted).
+__device__ __forceinline__ int clamp_len(const AttnParams &p, int Lraw)
+{
+    return Lraw < 0 ? 0 : (Lraw > p.max_blocks * kBlock ? p.max_blocks * kBlock : Lraw);
+}
+
+// Pages per balanced share for `total` (unit, page) pairs.  Share j (the
+// block index) is pairs [j*S, (j+1)*S) of the batch's list (units in order
+// b * Hkv + g, pages in order within a unit); a unit cut by several shares
+// leaves partials in slots unit + j, consecutive in j.  Shares go to the
+// dies round robin with the block index.  (Giving each die the units of its
+// own KV heads measured 9% slower on a ragged batch, 3% faster on one long
+// sequence.)
+__device__ __forceinline__ int bal_share(int total)
+{
+    int s = (total + kBalTargetWgs - 1) / kBalTargetWgs;
+    s = s < 4 ? 4 : s;
+    return s > kBalMaxShare ? kBalMaxShare : s;
+}
+
 struct UnitWork {
     int b, g, unit, split;
     int L;          // clamped context length
@@ -130,10 +151,12 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 // Split merge (flash-decoding second pass): one wave per (unit, row).
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s o_s 2^(m_s - M) / L.
 // Lanes hold one split's statistics each (reduced with DPP) and slices of
-// the head dim.  The context length, the statistics and the partial rows of
-// the first eight splits are requested together (all lie inside the
-// workspace), so the common case costs one round trip to memory; entries of
-// splits past the context are discarded.
+// the head dim.  Fixed splits: the context length, the statistics and the
+// partial rows of the first eight splits are requested together (all lie
+// inside the workspace), so the common case costs one round trip to memory;
+// entries of splits past the context are discarded.  Balanced shares: the
+// unit's first slot and its number of partials come from the prefix sums the
+// attention kernel left in the workspace, then the same loads follow.
 template <int D>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
@@ -146,21 +169,36 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
         return;
     const int unit = gw / p.TG, row = gw - unit * p.TG;
     const int b = unit / p.Hkv, g = unit - b * p.Hkv;
-    const int msp = p.max_splits;
     const float ninf = -__builtin_inff();
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + (size_t)unit * msp * p.TG + row;
-    const float *po = p.part_o + ((size_t)unit * msp * p.TG + row) * D + lane * PER;
+    size_t slot0;
+    int cnt, ns = 0;  // partials that may be read; partials of the unit
+    int Lraw = 0;
+    if (p.balanced) {
+        const int nblk = (clamp_len(p, p.context_lens[b]) + kBlock - 1) / kBlock;
+        const int S = bal_share(p.Hkv * p.bal_prefix[p.B]);
+        const int start = p.Hkv * p.bal_prefix[b] + g * nblk;
+        ns = nblk > 0 ? (start + nblk - 1) / S - start / S + 1 : 0;
+        if (ns <= 1)
+            return;  // written directly by the attention kernel (or no context)
+        slot0 = (size_t)unit + start / S;
+        cnt = ns;
+    } else {
+        slot0 = (size_t)unit * p.max_splits;
+        cnt = p.max_splits;
+        Lraw = p.context_lens[b];
+    }
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + slot0 * p.TG + row;
+    const float *po = p.part_o + (slot0 * p.TG + row) * D + lane * PER;
     const size_t sstride = (size_t)p.TG * D;  // floats between splits' partial rows
 
-    const int Lraw = p.context_lens[b];
-    const float2 st0 = lane < msp ? ml[(size_t)lane * p.TG] : make_float2(ninf, 0.0f);
+    const float2 st0 = lane < cnt ? ml[(size_t)lane * p.TG] : make_float2(ninf, 0.0f);
     float o[NB][PER];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int k = 0; k < PER; ++k)
             o[j][k] = 0.0f;
-        if (j < msp) {
+        if (j < cnt) {
             if constexpr (PER == 2) {
                 const float2 v = *reinterpret_cast<const float2 *>(po + j * sstride);
                 o[j][0] = v.x;
@@ -170,11 +208,12 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
             }
         }
     }
-    const int L = Lraw < 0 ? 0 : (Lraw > p.max_blocks * kBlock ? p.max_blocks * kBlock : Lraw);
-    const int nblk = (L + kBlock - 1) / kBlock;
-    const int ns = (nblk + p.bps - 1) / p.bps;
-    if (ns <= 1)
-        return;  // written directly by the attention kernel
+    if (!p.balanced) {
+        const int nblk = (clamp_len(p, Lraw) + kBlock - 1) / kBlock;
+        ns = (nblk + p.bps - 1) / p.bps;
+        if (ns <= 1)
+            return;  // written directly by the attention kernel
+    }
 
     float mloc = lane < ns ? st0.x : ninf;
     for (int s = lane + kWave; s < ns; s += kWave)
@@ -374,20 +413,21 @@ __device__ __forceinline__ void tile_store(float *tile, const floatx4 (&acc)[D /
 }
 
 // Merges the NT wave tiles of rows r0 .. r1-1 of one workgroup and stores
-// the result: normalised output when the unit has a single split, else the
-// unnormalised partial (o, max, sum) for the merge kernel.  tiles: NT tiles
+// the result: normalised output when slot < 0 (the workgroup saw the unit's
+// whole context), else the unnormalised partial (o, max, sum) in workspace
+// slot `slot` for the merge kernel.  tiles: NT tiles
 // holding rows r0.. as [rows][D+4] floats, `pitch` floats apart; sm/sl:
 // per-wave row max (base-2 units) and row sum.
 template <int D, int RG, int NT>
 __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles, int pitch,
                                                       const float (*sm)[64], const float (*sl)[64],
-                                                      int unit, int split, int b, int g, int nsplit, int r0, int r1)
+                                                      int slot, int b, int g, int r0, int r1)
 {
     constexpr int OP = D + 4;
     constexpr int C4 = D / 4;
     const float ninf = -__builtin_inff();
     const int G = p.G;
-    const size_t pbase = ((size_t)unit * p.max_splits + split) * p.TG;
+    const size_t pbase = (size_t)(slot < 0 ? 0 : slot) * p.TG;
     for (int idx = threadIdx.x; idx < (r1 - r0) * C4; idx += blockDim.x) {
         const int lr = idx / C4, c4 = idx - lr * C4;
         const int row = r0 + lr;
@@ -405,7 +445,7 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
             Ls += f * sl[v][row];
         }
-        if (nsplit == 1) {
+        if (slot < 0) {
             const float inv = 1.0f / Ls;
             o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
             const int t = row / G, hh = row - t * G;
@@ -428,39 +468,45 @@ constexpr int kMfmaWaves = 4;
 constexpr int kTilesPerPhase = 2;
 
 template <int D, int RG, bool FP8>
-__global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_kernel(AttnParams p)
-{
+struct MfmaShape {
     typedef PageGeom<D, FP8> PG;
-    constexpr int NW = kMfmaWaves<RG, FP8>;
-    constexpr int NT = 64 * NW;          // threads
-    constexpr int NDC = PG::NDC;
-    constexpr int NDT = PG::NDT;
+    static constexpr int NW = kMfmaWaves<RG, FP8>;
     // Ring stages per wave: about 8 KB of copies in flight behind the page
     // being computed.  (Deeper rings measured slower: more requests queue at
     // the memory controllers without raising the stream rate.)
-    constexpr int NS0 = 1 + (8192 + PG::STAGE - 1) / PG::STAGE;
-    constexpr int NS = NS0 > 4 ? 4 : NS0;
-    constexpr int EB = PG::EB;
-    constexpr int OP = D + 4;
-    constexpr int TPH = RG < kTilesPerPhase ? RG : kTilesPerPhase;  // row tiles per epilogue phase
-    constexpr int WT = TPH * 16 * OP;    // floats of one wave's parked O rows
+    static constexpr int NS0 = 1 + (8192 + PG::STAGE - 1) / PG::STAGE;
+    static constexpr int NS = NS0 > 4 ? 4 : NS0;
+    static constexpr int OP = D + 4;
+    static constexpr int TPH = RG < kTilesPerPhase ? RG : kTilesPerPhase;  // row tiles per epilogue phase
+    static constexpr int WT = TPH * 16 * OP;  // floats of one wave's parked O rows
     // Each wave's LDS region holds its page ring, and at the end its O tile.
-    constexpr int RW0 = NS * PG::STAGE > WT * 4 ? NS * PG::STAGE : WT * 4;
-    constexpr int RW = (RW0 + 15) & ~15;
-    constexpr int SMEM = NW * RW;
+    static constexpr int RW0 = NS * PG::STAGE > WT * 4 ? NS * PG::STAGE : WT * 4;
+    static constexpr int RW = (RW0 + 15) & ~15;
+    static constexpr int SMEM = NW * RW;
+};
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    __shared__ float s_m[NW][64], s_l[NW][64];
-    __shared__ int s_pages[kMaxBps];
-
-    // Work item from the block index alone (see work_item), so that every
-    // load of the prologue below can be in flight at once.
-    int unit, split;
-    work_item(p, unit, split);
-    if (unit >= p.B * p.Hkv)
-        return;
-    const int b = unit / p.Hkv, g = unit - b * p.Hkv;
-    const int blk_begin = split * p.bps;
+// One run of pages of one (sequence b, KV head g) unit: pages blk_begin ..
+// blk_begin + cap - 1, clipped to the context.  slot >= 0: the result is an
+// unnormalised partial in that workspace slot; slot < 0: the run is the
+// unit's whole context and the result is normalised into `out`.  With fixed
+// splits (fixed = true) the slot given is that of (unit, split), replaced by
+// -1 when the sequence has a single split.  Called by every thread of the
+// workgroup.
+template <int D, int RG, bool FP8>
+__device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char *smem, float (*s_m)[64],
+                                             float (*s_l)[64], int *s_pages, const int b, const int g,
+                                             const int blk_begin, const int cap, const int slot, const bool fixed)
+{
+    typedef MfmaShape<D, RG, FP8> SH;
+    typedef typename SH::PG PG;
+    constexpr int NW = SH::NW;
+    constexpr int NT = 64 * NW;          // threads
+    constexpr int NDC = PG::NDC;
+    constexpr int NDT = PG::NDT;
+    constexpr int NS = SH::NS;
+    constexpr int EB = PG::EB;
+    constexpr int TPH = SH::TPH;
+    constexpr int RW = SH::RW;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -474,7 +520,7 @@ __global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_ke
     // are all requested before any of them is used.  Table entries past the
     // context are read (they are in bounds) but never used.
     const int32_t *trow = p.block_table + (size_t)b * p.max_blocks + blk_begin;
-    const int avail = min(p.bps, p.max_blocks - blk_begin);
+    const int avail = min(cap, p.max_blocks - blk_begin);
     const int Lraw = p.context_lens[b];
     int first[NS - 1];
 #pragma unroll
@@ -508,8 +554,8 @@ __global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_ke
     const int nblk = (L + kBlock - 1) / kBlock;
     if (blk_begin >= nblk)
         return;  // uniform over the workgroup: nothing of this split is visible
-    const int npg = min(blk_begin + p.bps, nblk) - blk_begin;
-    const int nsplit = (nblk + p.bps - 1) / p.bps;
+    const int npg = min(blk_begin + cap, nblk) - blk_begin;
+    const int oslot = (fixed && (nblk + p.bps - 1) / p.bps == 1) ? -1 : slot;
 
     // Q tile as the B operand of S^T = K Q^T (row = l16, eight dims), bf16,
     // pre-scaled into base-2 units.
@@ -783,8 +829,122 @@ __global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_ke
             __syncthreads();  // the previous phase's tiles are consumed
         tile_store<D, RG, TPH>(reinterpret_cast<float *>(ring), acc, l16, q4, rt0);
         __syncthreads();
-        merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, unit, split,
-                                         b, g, nsplit, rt0 * 16, min(p.TG, (rt0 + TPH) * 16));
+        merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, oslot, b, g,
+                                         rt0 * 16, min(p.TG, (rt0 + TPH) * 16));
+    }
+}
+
+// Fixed splits: the workgroup's (unit, split) comes from its block index
+// alone (see work_item), so every load of the segment's prologue can be in
+// flight at once.  Balanced shares (see bal_share): the workgroup first sums
+// the page counts of all sequences (one round trip for the context lengths,
+// a workgroup prefix sum into LDS), then runs one segment per unit its share
+// meets.  The merge kernel finds a cut unit's partials from the same prefix
+// sums, which workgroup 0 leaves in the workspace.
+template <int D, int RG, bool FP8, bool BAL>
+__global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_kernel(AttnParams p)
+{
+    typedef MfmaShape<D, RG, FP8> SH;
+    constexpr int NW = SH::NW;
+    constexpr int NT = 64 * NW;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SH::SMEM];
+    __shared__ float s_m[NW][64], s_l[NW][64];
+    __shared__ int s_pages[kMaxBps];
+    static_assert(kBalMaxShare <= kMaxBps, "a share's page ids fit the LDS list");
+
+    if constexpr (!BAL) {
+        int unit, split;
+        work_item(p, unit, split);
+        if (unit >= p.B * p.Hkv)
+            return;
+        const int b = unit / p.Hkv;
+        mfma_segment<D, RG, FP8>(p, smem, s_m, s_l, s_pages, b, unit - b * p.Hkv, split * p.bps, p.bps,
+                                 unit * p.max_splits + split, true);
+        return;
+    }
+    __shared__ int s_P[kBalMaxB + 1];  // pages of the sequences before b
+    __shared__ int s_wsum[NW];
+    int pos = 0, end = 0, sb = 0, total = 0;
+    {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        constexpr int PER = (kBalMaxB + NT - 1) / NT;  // sequences per thread
+        int nbk[PER];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int bb = tid * PER + k;
+            nbk[k] = bb < p.B ? (clamp_len(p, p.context_lens[bb]) + kBlock - 1) / kBlock : 0;
+            sum += nbk[k];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_up(incl, o, kWave);
+            if (lane >= o)
+                incl += t;
+        }
+        if (lane == kWave - 1)
+            s_wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - sum;
+        for (int w = 0; w < wave; ++w)
+            run += s_wsum[w];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int bb = tid * PER + k;
+            if (bb < p.B)
+                s_P[bb] = run;
+            run += nbk[k];
+        }
+        if (tid == NT - 1)
+            s_P[p.B] = run;  // every sequence's pages
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int i = tid; i <= p.B; i += NT)
+                p.bal_prefix[i] = s_P[i];
+        total = p.Hkv * s_P[p.B];
+        const int S = bal_share(total);
+        pos = (int)blockIdx.x * S;
+        if (pos >= total)
+            return;
+        end = min(total, pos + S);
+        // the sequence holding pair pos: the largest sb with Hkv * P[sb] <= pos
+        // (sequences without pages are skipped: their successor has the same P)
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.Hkv * s_P[mid] <= pos)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        sb = lo;
+    }
+    for (;;) {
+        int b, g, blk_begin, cap, slot;
+        {
+            const int Pb = s_P[sb], nb = s_P[sb + 1] - Pb;
+            if (nb <= 0)
+                return;  // unreachable: pair pos lies inside sequence sb
+            const int base = p.Hkv * Pb, rel = pos - base;
+            const int gg = rel / nb;
+            const int uend = base + (gg + 1) * nb;  // one past the unit's last pair
+            const int send = min(end, uend);
+            const int off = rel - gg * nb;
+            b = __builtin_amdgcn_readfirstlane(sb);
+            g = __builtin_amdgcn_readfirstlane(gg);
+            blk_begin = __builtin_amdgcn_readfirstlane(off);
+            cap = __builtin_amdgcn_readfirstlane(send - pos);
+            slot = __builtin_amdgcn_readfirstlane((off == 0 && send == uend) ? -1
+                                                                              : sb * p.Hkv + gg + (int)blockIdx.x);
+        }
+        mfma_segment<D, RG, FP8>(p, smem, s_m, s_l, s_pages, b, g, blk_begin, cap, slot, false);
+        pos += cap;
+        if (pos >= end)
+            return;
+        __syncthreads();  // the next segment reuses the LDS this one's epilogue read
+        while (sb < p.B - 1 && p.Hkv * s_P[sb + 1] <= pos)
+            ++sb;
     }
 }
 
@@ -921,7 +1081,7 @@ hipError_t launch(Kernel k, const AttnParams &p, hipStream_t stream)
 template <int D, int RG, bool FP8>
 hipError_t launch_mfma_rg(const AttnParams &p, hipStream_t s)
 {
-    auto kern = sv_attn_mfma_kernel<D, RG, FP8>;
+    auto kern = p.balanced ? sv_attn_mfma_kernel<D, RG, FP8, true> : sv_attn_mfma_kernel<D, RG, FP8, false>;
     hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * kMfmaWaves<RG, FP8>), 0, s, p);
     return hipGetLastError();
 }
@@ -952,7 +1112,7 @@ hipError_t launch_valu_d(const AttnParams &p, int kv, hipStream_t s)
 
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
 {
-    if (p.max_splits <= 1)
+    if (!p.balanced && p.max_splits <= 1)
         return hipSuccess;
     const long long waves = (long long)p.B * p.Hkv * p.TG;
     const dim3 grid((unsigned)((waves + 3) / 4));

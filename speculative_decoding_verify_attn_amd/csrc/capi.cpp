@@ -49,10 +49,15 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
 {
     AttnPlan pl{};
     const long long units = (long long)B * Hkv;
+    const long long pairs = units * max_blocks;  // (unit, page) pairs at the longest context
+    const bool bal_ok = B <= kBalMaxB && pairs <= kBalMaxPages;
+    // (one sequence cannot be ragged: the fixed split is as balanced and
+    // needs no merge when it is not split)
+    pl.balanced = bal_ok && (bps_request == kSplitBalanced || (bps_request == 0 && B > 1 && pairs >= kBalMinPages));
     int bps;
     if (bps_request > 0) {
         bps = bps_request;
-    } else {
+    } else {  // the planner's fixed split (also the vector-ALU kernel's under balanced shares)
         const long long target_wgs = 256;
         long long splits = (target_wgs + units - 1) / units;
         if (splits < 1)
@@ -76,7 +81,23 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
     } else {
         pl.off_part_ml = off;
     }
-    pl.total = off > 256 ? off : 256;
+    size_t total = off;
+    if (pl.balanced) {
+        // ceil(total / S) shares never exceed this many workgroups
+        // (S = kBalMaxShare, or S >= ceil(total / kBalTargetWgs))
+        const long long g = std::max<long long>(kBalTargetWgs, (pairs + kBalMaxShare - 1) / kBalMaxShare);
+        pl.grid_bal = (int)g;
+        const long long slots = units + g;
+        size_t o = 0;
+        pl.off_prefix = o;
+        o = align256(o + (size_t)(B + 1) * 4);
+        pl.off_bal_o = o;
+        o = align256(o + (size_t)slots * TG * d * 4);
+        pl.off_bal_ml = o;
+        o = align256(o + (size_t)slots * TG * 2 * 4);
+        total = std::max(total, o);
+    }
+    pl.total = total > 256 ? total : 256;
     return pl;
 }
 
@@ -181,6 +202,12 @@ size_t spec_verify_attn_workspace_size_ex(int B, int T, int Hq, int Hkv, int d, 
 {
     if (check_attn_shape(B, T, Hq, Hkv, d, max_blocks_per_seq) != SV_OK)
         return 0;
+    if (ceil_div(max_blocks_per_seq, sv::kMaxBps) > sv::kMaxSplits)
+        return 0;
+    if (blocks_per_split == sv::kSplitBalanced) {
+        const sv::AttnPlan pl = sv::plan_attention(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split);
+        return pl.balanced ? pl.total : 0;
+    }
     if (blocks_per_split < 0 || (blocks_per_split > 0 && blocks_per_split % 4) || blocks_per_split > sv::kMaxBps)
         return 0;
     if (blocks_per_split > 0 && ceil_div(max_blocks_per_seq, blocks_per_split) > sv::kMaxSplits)
@@ -227,8 +254,17 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
         return fail(SV_ERR_UNSUPPORTED, "unknown algo %d", algo);
     if (algo == SV_ATTN_MFMA && kv_dtype == SV_KV_F32)
         return fail(SV_ERR_UNSUPPORTED, "the matrix-core kernel needs bf16 or E4M3 storage");
-    if (blocks_per_split < 0 || (blocks_per_split > 0 && blocks_per_split % 4))
-        return fail(SV_ERR_SHAPE, "blocks_per_split must be 0 or a positive multiple of 4 (got %d)", blocks_per_split);
+    const bool use_mfma = (algo == SV_ATTN_MFMA) || (algo == SV_ATTN_AUTO && kv_dtype != SV_KV_F32);
+    if (blocks_per_split == sv::kSplitBalanced) {
+        if (!use_mfma)
+            return fail(SV_ERR_UNSUPPORTED, "balanced shares (blocks_per_split = -1) need the matrix-core kernel");
+        if (B > sv::kBalMaxB || (long long)B * Hkv * max_blocks_per_seq > sv::kBalMaxPages)
+            return fail(SV_ERR_UNSUPPORTED, "balanced shares need B <= %d and B*Hkv*max_blocks_per_seq <= 2^30",
+                        sv::kBalMaxB);
+    } else if (blocks_per_split < 0 || (blocks_per_split > 0 && blocks_per_split % 4)) {
+        return fail(SV_ERR_SHAPE, "blocks_per_split must be -1, 0 or a positive multiple of 4 (got %d)",
+                    blocks_per_split);
+    }
     if (blocks_per_split > sv::kMaxBps)
         return fail(SV_ERR_SHAPE, "blocks_per_split must be <= %d (got %d)", sv::kMaxBps, blocks_per_split);
     if (blocks_per_split > 0 && ceil_div(max_blocks_per_seq, blocks_per_split) > sv::kMaxSplits)
@@ -262,8 +298,10 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.context_lens = context_lens;
     p.tree_mask = tree_mask;
     p.out = out;
-    p.part_o = reinterpret_cast<float *>(ws + pl.off_part_o);
-    p.part_ml = reinterpret_cast<float *>(ws + pl.off_part_ml);
+    p.balanced = (pl.balanced && use_mfma) ? 1 : 0;
+    p.part_o = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_o : pl.off_part_o));
+    p.part_ml = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_ml : pl.off_part_ml));
+    p.bal_prefix = p.balanced ? reinterpret_cast<int *>(ws + pl.off_prefix) : nullptr;
     p.B = B;
     p.T = T;
     p.Hq = Hq;
@@ -275,14 +313,14 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.num_blocks = num_blocks;
     p.bps = pl.bps;
     p.max_splits = pl.max_splits;
-    // 8 * ceil(units / 8) * max_splits workgroups (see work_item in attn.hip)
-    const long long wgs = ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits;
+    // fixed splits: 8 * ceil(units / 8) * max_splits workgroups (see
+    // work_item in attn.hip); balanced shares: the plan's grid
+    const long long wgs = p.balanced ? (long long)pl.grid_bal : ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits;
     if (wgs > 0x7FFFFFF0LL)
         return fail(SV_ERR_SHAPE, "too many workgroups");
     p.grid = (int)wgs;
     p.qscale = (float)((double)sm_scale * 1.4426950408889634);
 
-    const bool use_mfma = (algo == SV_ATTN_MFMA) || (algo == SV_ATTN_AUTO && kv_dtype != SV_KV_F32);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = use_mfma ? sv::launch_attn_mfma(p, kv_dtype, s) : sv::launch_attn_valu(p, kv_dtype, s);
     if (e != hipSuccess)

@@ -24,8 +24,12 @@ struct AttnParams {
     const int32_t *block_table;
     const int32_t *context_lens;
     float *out;
-    float *part_o;         // [B*Hkv][max_splits][TG][d]  unnormalised partial outputs
-    float *part_ml;        // [B*Hkv][max_splits][TG][2]  (running max in log2 units, sum)
+    float *part_o;         // [slot][TG][d]  unnormalised partial outputs
+    float *part_ml;        // [slot][TG][2]  (running max in log2 units, sum)
+                           // fixed splits: slot = unit * max_splits + split;
+                           // balanced shares: slot = unit + workgroup
+    int *bal_prefix;       // balanced shares: [B+1] pages of the sequences before b (written by workgroup 0)
+    int balanced;          // 1: every workgroup takes an equal share of all (unit, page) pairs
     int B, T, Hq, Hkv, G, TG, d;
     int max_blocks, num_blocks;
     int bps;               // context blocks per split (multiple of 8)
@@ -38,8 +42,29 @@ struct AttnParams {
 struct AttnPlan {
     int bps;
     int max_splits;
-    size_t off_part_o, off_part_ml, total;
+    size_t off_part_o, off_part_ml;
+    // balanced shares (usable by the matrix-core kernel only): grid and
+    // workspace layout; the fixed-split fields above stay valid for the
+    // vector-ALU kernel
+    int balanced;
+    int grid_bal;
+    size_t off_prefix, off_bal_o, off_bal_ml;
+    size_t total;  // bytes covering whichever layout the call uses
 };
+
+// Balanced shares.  The (unit, page) pairs of the whole batch, units in
+// order b * Hkv + g and pages in order within a unit, are cut into equal
+// shares of S = min(kBalMaxShare, max(4, ceil(total / kBalTargetWgs))) pages,
+// one per workgroup, so ragged context lengths leave no long workgroup
+// behind.
+// Chosen by the planner for large batches of several sequences (at least
+// kBalMinPages pairs at the longest context, at most kBalMaxB sequences).
+constexpr int kSplitBalanced = -1;      // blocks_per_split value that asks for balanced shares
+constexpr int kBalMaxB = 1024;          // sequences (prefix sums held in LDS)
+constexpr int kBalTargetWgs = 256;      // shares aimed for: one per compute unit
+constexpr int kBalMaxShare = 512;      // pages per share (512 measured 16% faster than 1024 on a ragged batch)
+constexpr long long kBalMinPages = 65536;
+constexpr long long kBalMaxPages = 1LL << 30;  // (unit, page) pairs: positions stay in int
 
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, int bps_request);
 

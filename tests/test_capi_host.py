@@ -73,6 +73,10 @@ def _attn(**kw):
     (dict(algo=2, kv=0), 3),      # matrix cores need bf16/E4M3
     (dict(bps=10), 2),
     (dict(bps=516), 2),
+    (dict(bps=-2), 2),
+    (dict(bps=-1, kv=0), 3),      # balanced shares need the matrix-core kernel
+    (dict(bps=-1, algo=1), 3),
+    (dict(bps=-1, B=1025), 3),    # balanced shares: at most 1024 sequences
     (dict(ws=None), 4),
     (dict(wsb=16), 4),
     (dict(q=1 << 20 | 4), 5),     # misaligned
@@ -159,6 +163,16 @@ def test_tree_commit_argument_checks():
 
 def test_workspace_queries():
     assert sv.attn_workspace_size(8, 6, 32, 8, 128, 256) > 0
+    # balanced shares (blocks_per_split = -1): prefix sums plus one partial
+    # slot per unit and per workgroup (at least 256 workgroups)
+    L = sv.lib()
+    bal = L.spec_verify_attn_workspace_size_ex(8, 6, 32, 8, 128, 256, -1)
+    assert bal >= (8 * 8 + 256) * 24 * 128 * 4
+    assert L.spec_verify_attn_workspace_size_ex(1025, 6, 32, 8, 128, 256, -1) == 0
+    assert L.spec_verify_attn_workspace_size_ex(1024, 6, 32, 8, 128, 256, -1) > 0
+    # the planner's choice for large batches is covered by the default size
+    big = (64, 8, 32, 8, 128, 1024)
+    assert L.spec_verify_attn_workspace_size_ex(*big, 0) >= L.spec_verify_attn_workspace_size_ex(*big, -1)
     assert sv.lib().spec_verify_attn_workspace_size(8, 6, 30, 8, 128, 256) == 0
     assert sv.sample_workspace_size(8, 5, 128256) >= 8 * 6 * 16 * 16
     assert sv.lib().spec_verify_sample_workspace_size(8, 0, 10) == 0

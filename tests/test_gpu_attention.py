@@ -36,7 +36,8 @@ def _check(a, out, rows=None):
     if rows is not None:
         got = got[rows]
     err = row_rel_err(got, ref)
-    assert np.all(np.isfinite(got)), "non-finite output"
+    bad = np.nonzero(~np.all(np.isfinite(got), axis=1))[0]
+    assert bad.size == 0, "non-finite output rows %s" % bad[:8]
     return float(err.max())
 
 
@@ -150,3 +151,68 @@ def test_random_shapes(case):
         out = run_attn(a, algo=algo, blocks_per_split=bps)
         err = _check(a, out)
         assert err <= TOL[a.kv_dtype], (case, algo, err)
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[7] != "f32"], ids=lambda c: str(c[0]))
+def test_small_shapes_balanced(case):
+    """Balanced shares (blocks_per_split = -1): the batch's (unit, page)
+    pairs cut into equal runs, here of 4 pages, so units are split across
+    many workgroups and workgroups span several units."""
+    seed, B, T, Hq, Hkv, d, lens, kv = case
+    a = W.make_attn_from_lens(seed, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=2)
+    out = run_attn(a, blocks_per_split=-1)
+    err = _check(a, out)
+    assert err <= TOL[a.kv_dtype], (case, err)
+
+
+@pytest.mark.parametrize("lens", [
+    [5000, 16, 17, 5, 700, 9, 6, 33, 1200, 64, 65, 300],   # ragged: runs cross unit and sequence ends
+    [4096] * 5,                                            # uniform: shares of whole splits
+    [8, 3000, 8, 8, 8, 8, 8, 2500],                        # many one-page units inside one share
+])
+def test_balanced_shares_ragged(lens):
+    a = W.make_attn_from_lens(31, len(lens), 5, 32, 8, 128, lens, kv="bf16", extra_blocks=2)
+    out = run_attn(a, blocks_per_split=-1)
+    err = _check(a, out)
+    print("balanced lens %s: max row rel err %.3e" % (lens[:4], err))
+    assert err <= TOL[a.kv_dtype]
+    out_f = run_attn(a, blocks_per_split=16)
+    assert _check(a, out_f) <= TOL[a.kv_dtype]
+
+
+def test_balanced_shares_skip_empty_sequences():
+    """A sequence without context holds no pairs: the shares skip it and the
+    other sequences' rows are unaffected (its own rows are not written)."""
+    lens = [300, 0, 900, 0, 0, 45]
+    a = W.make_attn_from_lens(32, len(lens), 5, 32, 8, 128, [max(L, 5) for L in lens], kv="bf16", extra_blocks=2)
+    keep = np.array([L > 0 for L in lens])
+    ref_rows = np.arange(a.B * a.T * a.Hq).reshape(a.B, -1)[keep].ravel()
+    t = upload_attn(a)
+    t["lens"].copy_(torch.tensor(lens, dtype=torch.int32))
+    out = run_attn(a, t, blocks_per_split=-1)
+    err = _check(a, out, rows=ref_rows)
+    assert err <= TOL[a.kv_dtype]
+
+
+def test_balanced_shares_deterministic_with_garbage_workspace():
+    a = W.make_attn_from_lens(33, 6, 6, 32, 8, 128, [2000, 33, 700, 1024, 6, 4000], kv="bf16")
+    t = upload_attn(a)
+    ws = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, -1), t["q"].device)
+    ws.fill_(0xAB)
+    o1 = run_attn(a, t, blocks_per_split=-1, ws=ws).clone()
+    assert _check(a, o1) <= TOL[a.kv_dtype]
+    for _ in range(3):
+        o2 = run_attn(a, t, blocks_per_split=-1, ws=ws)
+        assert torch.equal(o1, o2)
+
+
+RANDOM_BAL = [c for c in _random_shapes(40, 2025) if c[7] != "f32"][:12]
+
+
+@pytest.mark.parametrize("case", RANDOM_BAL, ids=[str(c[0]) for c in RANDOM_BAL])
+def test_random_shapes_balanced(case):
+    i, B, T, Hq, Hkv, d, lens, kv, _ = case
+    a = W.make_attn_from_lens(700 + i, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=2)
+    out = run_attn(a, blocks_per_split=-1)
+    err = _check(a, out)
+    assert err <= TOL[a.kv_dtype], (case, err)

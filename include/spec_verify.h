@@ -125,9 +125,22 @@ int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache,
 
 /* As spec_verify_attn, with the implementation and the context split chosen
  * by the caller (for measurement).  blocks_per_split = 0 lets the planner
- * choose; otherwise it must be a positive multiple of 4, at most 512, with
- * ceil(max_blocks_per_seq / blocks_per_split) <= 128.  The workspace must
- * then hold spec_verify_attn_workspace_size_ex(..., blocks_per_split) bytes.
+ * choose; -1 asks for balanced shares (below); otherwise it must be a
+ * positive multiple of 4, at most 512, with
+ * ceil(max_blocks_per_seq / blocks_per_split) <= 128, and every sequence's
+ * context is cut into splits of that many pages.  The workspace must then
+ * hold spec_verify_attn_workspace_size_ex(..., blocks_per_split) bytes.
+ *
+ * Balanced shares (matrix-core kernel only; B <= 1024 and
+ * B*Hkv*max_blocks_per_seq <= 2^30, else SV_ERR_UNSUPPORTED): the
+ * (sequence, KV head, page) triples of the whole batch, in that order, are
+ * cut on the device, from context_lens, into equal runs of
+ * S = min(512, max(4, ceil(total / 256))) pages, one per workgroup, so a
+ * ragged batch leaves no long workgroup behind.  The planner uses them for
+ * batches of two or more sequences with B*Hkv*max_blocks_per_seq >= 65536
+ * when the matrix-core kernel runs.  Results agree with the fixed split up
+ * to the order of floating-point additions.
+ *
  * main_done_event: optional hipEvent_t (NULL to skip), recorded on `stream`
  * after the main attention kernel and before the split merge, so a caller
  * can time the main kernel on its own. */

@@ -206,6 +206,20 @@ def test_balanced_shares_deterministic_with_garbage_workspace():
         assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("B", [1000, 1024])
+def test_balanced_shares_many_sequences(B):
+    """Up to the 1024 sequences the balanced prefix sums hold: every thread
+    of the workgroup carries four sequences' page counts."""
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(5, 200, size=B)]
+    a = W.make_attn_from_lens(34, B, 5, 16, 8, 64, lens, kv="bf16", extra_blocks=2)
+    out = run_attn(a, blocks_per_split=-1)
+    rows = sample_rows(a, 2048, seed=3)
+    err = _check(a, out, rows)
+    assert err <= TOL[a.kv_dtype]
+    assert torch.isfinite(out).all()
+
+
 RANDOM_BAL = [c for c in _random_shapes(40, 2025) if c[7] != "f32"][:12]
 
 

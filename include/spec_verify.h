@@ -375,6 +375,32 @@ int spec_verify_tree_commit(const int32_t *path, const int32_t *num_accepted,
                             int block_size, int max_blocks_per_seq, int num_blocks,
                             int kv_dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * spec_verify_check_inputs: a debug aid that counts the device-data
+ * preconditions the calls above document but do not check (they stay
+ * memory-safe on such data by clamping; their results are then undefined).
+ *
+ * Checks ("KV Cache + Speculative Decoding" 5.2-5.3 paged cache and 6.1
+ * cached attention; "50 | Speculative Decoding" 3.1 acceptance test), per
+ * sequence b < B, each into one counter of counts[SV_CHECK_COUNTS]:
+ *   [0] context_lens[b] outside [T, 16 * max_blocks_per_seq];
+ *   [1] block_table[b][i] outside [0, num_blocks) for the pages holding
+ *       visible positions, i < ceil(min(max(L_b, 0), 16*max_blocks)/16);
+ *   [2] tokens[b][i], i < n_tokens, outside [0, V);
+ *   [3] uniforms[b][i], i < n_uniforms, outside [0, 1) or not finite.
+ * context_lens NULL skips [0] and [1]; block_table NULL skips [1]; tokens
+ * NULL skips [2]; uniforms NULL skips [3] (the sizes of a skipped check
+ * are ignored).  counts: int32[SV_CHECK_COUNTS] device memory, cleared and
+ * then written on `stream` (read it after synchronising).  Allocates
+ * nothing; two launches.
+ * ------------------------------------------------------------------------ */
+#define SV_CHECK_COUNTS 4
+int spec_verify_check_inputs(const int32_t *block_table, const int32_t *context_lens, int T,
+                             int max_blocks_per_seq, int num_blocks,
+                             const int32_t *tokens, int n_tokens, int V,
+                             const float *uniforms, int n_uniforms,
+                             int B, int32_t *counts, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

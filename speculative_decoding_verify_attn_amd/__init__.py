@@ -81,6 +81,8 @@ def lib():
         L.spec_verify_tree_commit.argtypes = [P] * 9 + [I] * 8 + [P]
         L.spec_verify_rollback.restype = I
         L.spec_verify_rollback.argtypes = [P] * 3 + [I] * 2 + [P]
+        L.spec_verify_check_inputs.restype = I
+        L.spec_verify_check_inputs.argtypes = [P, P] + [I] * 3 + [P, I, I, P, I, I, P, P]
         if L.sv_abi_version() != 1:
             raise ImportError("libspecverify ABI version mismatch")
         _lib = L
@@ -269,6 +271,32 @@ def spec_verify_rollback(num_accepted, context_lens, K, pages_in_use=None, strea
         _ptr(num_accepted), _ptr(context_lens), _ptr(pages_in_use), context_lens.shape[0], int(K),
         _stream_handle(stream, context_lens.device)))
     return context_lens, pages_in_use
+
+
+SV_CHECK_COUNTS = 4
+
+
+def spec_verify_check_inputs(B, *, block_table=None, context_lens=None, T=1, max_blocks_per_seq=None, num_blocks=0,
+                             tokens=None, V=0, uniforms=None, counts=None, stream=None):
+    """Counts violations of the documented device-data preconditions (see
+    include/spec_verify.h): [0] context lengths outside [T, 16*max_blocks],
+    [1] out-of-range table entries of visible pages, [2] tokens outside
+    [0, V), [3] uniforms outside [0, 1).  Returns the int32[4] device tensor
+    (allocated here unless `counts` is given); read it after synchronising."""
+    ref = next(x for x in (block_table, context_lens, tokens, uniforms, counts) if x is not None)
+    if counts is None:
+        counts = torch.empty(SV_CHECK_COUNTS, dtype=torch.int32, device=ref.device)
+    max_blocks = max_blocks_per_seq
+    if max_blocks is None:
+        if block_table is None and context_lens is not None:
+            raise ValueError("checking context_lens without block_table needs max_blocks_per_seq")
+        max_blocks = block_table.shape[1] if block_table is not None else 1
+    n_tokens = tokens.shape[1] if tokens is not None else 0
+    n_uniforms = uniforms.shape[1] if uniforms is not None else 0
+    _check("spec_verify_check_inputs", lib().spec_verify_check_inputs(
+        _ptr(block_table), _ptr(context_lens), int(T), int(max_blocks), int(num_blocks), _ptr(tokens), int(n_tokens),
+        int(V), _ptr(uniforms), int(n_uniforms), int(B), _ptr(counts), _stream_handle(stream, ref.device)))
+    return counts
 
 
 def spec_verify_tree_commit(path, num_accepted, k_cache, v_cache, block_table, context_lens, *, pages_in_use=None,

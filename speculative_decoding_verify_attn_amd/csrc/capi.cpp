@@ -540,6 +540,47 @@ int spec_verify_kv_append(const float *k_new, const float *v_new, void *k_cache,
     return ok();
 }
 
+int spec_verify_check_inputs(const int32_t *block_table, const int32_t *context_lens, int T, int max_blocks_per_seq,
+                             int num_blocks, const int32_t *tokens, int n_tokens, int V, const float *uniforms,
+                             int n_uniforms, int B, int32_t *counts, void *stream)
+{
+    static_assert(SV_CHECK_COUNTS == sv::kCheckCounts, "counter count of the header");
+    if (!counts)
+        return fail(SV_ERR_NULL, "counts must be non-NULL");
+    if (B < 1)
+        return fail(SV_ERR_SHAPE, "B must be >= 1 (got %d)", B);
+    if (block_table && !context_lens)
+        return fail(SV_ERR_NULL, "checking block_table needs context_lens (the visible pages)");
+    if (context_lens && (T < 1 || max_blocks_per_seq < 1))
+        return fail(SV_ERR_SHAPE, "need T >= 1 and max_blocks_per_seq >= 1 (got %d, %d)", T, max_blocks_per_seq);
+    if (block_table && num_blocks < 1)
+        return fail(SV_ERR_SHAPE, "num_blocks must be >= 1 (got %d)", num_blocks);
+    if (tokens && (n_tokens < 0 || V < 1))
+        return fail(SV_ERR_SHAPE, "need n_tokens >= 0 and V >= 1 (got %d, %d)", n_tokens, V);
+    if (uniforms && n_uniforms < 0)
+        return fail(SV_ERR_SHAPE, "n_uniforms must be >= 0 (got %d)", n_uniforms);
+    if (!aligned(counts, 4) || (block_table && !aligned(block_table, 4)) || (context_lens && !aligned(context_lens, 4)) ||
+        (tokens && !aligned(tokens, 4)) || (uniforms && !aligned(uniforms, 4)))
+        return fail(SV_ERR_ALIGN, "arrays must be 4-byte aligned");
+    sv::CheckParams p{};
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.tokens = tokens;
+    p.uniforms = uniforms;
+    p.counts = counts;
+    p.B = B;
+    p.T = T;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.n_tokens = tokens ? n_tokens : 0;
+    p.V = V;
+    p.n_uniforms = uniforms ? n_uniforms : 0;
+    const hipError_t e = sv::launch_check_inputs(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "input check launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int spec_verify_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
                          void *stream)
 {

@@ -160,6 +160,18 @@ struct TreeCommitParams {
 hipError_t launch_tree_commit(const TreeCommitParams &p, int kv_dtype, hipStream_t stream);
 
 hipError_t launch_kv_append(const AppendParams &p, int kv_dtype, hipStream_t stream);
+
+// Counting violations of the device-data preconditions (a debug aid).
+constexpr int kCheckCounts = 4;
+struct CheckParams {
+    const int32_t *block_table;   // [B][max_blocks] or null
+    const int32_t *context_lens;  // [B] or null
+    const int32_t *tokens;        // [B][n_tokens] or null
+    const float *uniforms;        // [B][n_uniforms] or null
+    int32_t *counts;              // [kCheckCounts]
+    int B, T, max_blocks, num_blocks, n_tokens, V, n_uniforms;
+};
+hipError_t launch_check_inputs(const CheckParams &p, hipStream_t stream);
 hipError_t launch_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
                            hipStream_t stream);
 

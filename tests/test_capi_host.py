@@ -203,3 +203,25 @@ def test_append_and_rollback_argument_checks():
     assert L.spec_verify_rollback(p, p, None, 2, 16, None) == 2
     assert L.spec_verify_rollback(p, p, None, 0, 5, None) == 2
     assert L.spec_verify_rollback(p, p + 2, None, 2, 5, None) == 5
+
+
+def test_check_inputs_argument_checks():
+    L = sv.lib()
+    buf = ctypes.create_string_buffer(1 << 12)
+    base = (ctypes.addressof(buf) + 255) & ~255
+
+    def call(**kw):
+        a = dict(table=base, lens=base, T=6, maxb=8, nb=16, tok=base, ntok=5, V=100, u=base, nu=6, B=2, counts=base)
+        a.update(kw)
+        return L.spec_verify_check_inputs(a["table"], a["lens"], a["T"], a["maxb"], a["nb"], a["tok"], a["ntok"],
+                                          a["V"], a["u"], a["nu"], a["B"], a["counts"], None)
+
+    assert call(counts=None) == 1
+    assert call(B=0) == 2
+    assert call(lens=None) == 1           # the table's visible pages come from the lengths
+    assert call(T=0) == 2
+    assert call(nb=0) == 2
+    assert call(V=0) == 2
+    assert call(nu=-1) == 2
+    assert call(counts=base + 2) == 5
+    assert len(L.sv_last_error()) > 0

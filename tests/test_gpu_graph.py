@@ -174,3 +174,30 @@ def test_graph_replay_tree_sampler_and_commit():
         return (torch.empty_like(base["k"]), torch.empty_like(base["v"]), torch.empty_like(base["lens"]))
 
     _replays_match(commit, commit_outputs, dev)
+
+
+def test_graph_replay_attention_balanced_and_check():
+    """Attention with balanced shares (prefix sums in the workspace, cut units
+    merged), fp8 and bf16, and the input check, captured and replayed."""
+    dev = torch.device("cuda", 0)
+    cases = []
+    for kv in ("bf16", "fp8"):
+        aa = [W.make_attn_from_lens(40 + i, 5, 5, 32, 8, 128, [700, 33, 2100, 5, 1290], kv=kv) for i in range(2)]
+        cases.append((aa, [upload_attn(a) for a in aa]))
+    for aa, tt in cases:
+        a = aa[0]
+        ws = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, -1), dev)
+
+        def outputs():
+            return (torch.empty((a.B, a.T, a.Hq, a.d), dtype=torch.float32, device=dev),
+                    torch.empty(sv.SV_CHECK_COUNTS, dtype=torch.int32, device=dev))
+
+        def call(o, stream, which):
+            t = tt[which]
+            sv.spec_verify_attn(t["q"], t["k"], t["v"], t["table"], t["lens"], o[0], ws,
+                                k_scale=t.get("ks"), v_scale=t.get("vs"), kv_dtype=a.kv_dtype, blocks_per_split=-1,
+                                stream=stream)
+            sv.spec_verify_check_inputs(a.B, block_table=t["table"], context_lens=t["lens"], T=a.T,
+                                        num_blocks=a.num_blocks, counts=o[1], stream=stream)
+
+        _replays_match(call, outputs, dev)

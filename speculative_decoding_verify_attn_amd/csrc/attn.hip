@@ -62,9 +62,11 @@ __device__ __forceinline__ int clamp_len(const AttnParams &p, int Lraw)
 // sequence.)
 __device__ __forceinline__ int bal_share(int total)
 {
-    int s = (total + kBalTargetWgs - 1) / kBalTargetWgs;
-    s = s < 4 ? 4 : s;
-    return s > kBalMaxShare ? kBalMaxShare : s;
+    const int s1 = (total + kBalTargetWgs - 1) / kBalTargetWgs;
+    if (s1 <= kBalOneShare)
+        return s1 < 4 ? 4 : s1;
+    const int s2 = (total + 2 * kBalTargetWgs - 1) / (2 * kBalTargetWgs);
+    return s2 > kBalMaxShare ? kBalMaxShare : s2;
 }
 
 struct UnitWork {
@@ -849,8 +851,7 @@ __global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_ke
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::SMEM];
     __shared__ float s_m[NW][64], s_l[NW][64];
-    __shared__ int s_pages[kMaxBps];
-    static_assert(kBalMaxShare <= kMaxBps, "a share's page ids fit the LDS list");
+    __shared__ int s_pages[BAL ? kBalMaxShare : kMaxBps];  // the segment's page ids
 
     if constexpr (!BAL) {
         int unit, split;

@@ -83,9 +83,9 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
     }
     size_t total = off;
     if (pl.balanced) {
-        // ceil(total / S) shares never exceed this many workgroups
-        // (S = kBalMaxShare, or S >= ceil(total / kBalTargetWgs))
-        const long long g = std::max<long long>(kBalTargetWgs, (pairs + kBalMaxShare - 1) / kBalMaxShare);
+        // ceil(total / S) shares never exceed this many workgroups (S is
+        // kBalMaxShare, or at least ceil(total / (2 * kBalTargetWgs)))
+        const long long g = std::max<long long>(2 * kBalTargetWgs, (pairs + kBalMaxShare - 1) / kBalMaxShare);
         pl.grid_bal = (int)g;
         const long long slots = units + g;
         size_t o = 0;

@@ -54,15 +54,18 @@ struct AttnPlan {
 
 // Balanced shares.  The (unit, page) pairs of the whole batch, units in
 // order b * Hkv + g and pages in order within a unit, are cut into equal
-// shares of S = min(kBalMaxShare, max(4, ceil(total / kBalTargetWgs))) pages,
-// one per workgroup, so ragged context lengths leave no long workgroup
-// behind.
+// shares of S pages, one per workgroup, so ragged context lengths leave no
+// long workgroup behind: S = max(4, ceil(total / kBalTargetWgs)) (one share
+// per compute unit) while that is at most kBalOneShare pages, else
+// S = min(kBalMaxShare, ceil(total / (2 * kBalTargetWgs))) (two per compute
+// unit, all resident at once, rather than a second round of a few).
 // Chosen by the planner for large batches of several sequences (at least
 // kBalMinPages pairs at the longest context, at most kBalMaxB sequences).
 constexpr int kSplitBalanced = -1;      // blocks_per_split value that asks for balanced shares
 constexpr int kBalMaxB = 1024;          // sequences (prefix sums held in LDS)
 constexpr int kBalTargetWgs = 256;      // shares aimed for: one per compute unit
-constexpr int kBalMaxShare = 512;      // pages per share (512 measured 16% faster than 1024 on a ragged batch)
+constexpr int kBalOneShare = 512;      // longest share at one workgroup per compute unit
+constexpr int kBalMaxShare = 1024;     // pages per share (page ids held in LDS)
 constexpr long long kBalMinPages = 65536;
 constexpr long long kBalMaxPages = 1LL << 30;  // (unit, page) pairs: positions stay in int
 

@@ -114,6 +114,8 @@ TreePlan plan_sample_tree(int B, int N, int V)
     off = align256(off + (size_t)B * ceil_div(V, kSampleSub) * 2 * 8);
     pl.off_coefs = off;  // chunk partials of every node's test normaliser
     off = align256(off + (size_t)B * N * pl.nchunk * 8);
+    pl.off_tree_c = off;  // coefficient of every node's test
+    off = align256(off + (size_t)B * N * 8);
     pl.total = off;
     return pl;
 }
@@ -649,6 +651,7 @@ int spec_verify_sample_tree(const float *target_logits, const float *draft_probs
     p.row_stats = ws + pl.off_stats;
     p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
     p.coefs = reinterpret_cast<double *>(ws + pl.off_coefs);
+    p.tree_c = reinterpret_cast<double *>(ws + pl.off_tree_c);
     p.parents = parents;
     p.path = path;
     p.B = B;

@@ -170,6 +170,16 @@ __device__ __forceinline__ double block_sum(double v, double *s_red)
 
 __device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
 
+// ptr[i] if ok, else fill.  The index is clamped to 0 instead of branching
+// around the load (ptr[0] must be readable), so that a run of such loads
+// stays in flight together.
+template <typename T>
+__device__ __forceinline__ T load_or(const T *ptr, size_t i, bool ok, T fill)
+{
+    const T v = ptr[ok ? i : 0];
+    return ok ? v : fill;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(SampleParams p)
 {
@@ -1271,92 +1281,159 @@ __device__ __forceinline__ double tree_z_share(const SampleParams &p, int b, int
     return z;
 }
 
-constexpr int kTreeSlots = 4;  // workgroups per (sequence, chunk) of a rank's launch
+constexpr int kLevelWaves = 16;                             // waves of a rank's workgroup
+constexpr int kLevelSlice = kSampleChunk / kLevelWaves;      // entries per wave: 512
+static_assert(kLevelSlice == 8 * kWave, "a slice is eight entries per lane");
 
-// One sibling rank: grid (slot x vocabulary chunk x sequence).  The children
-// of rank `rank` (>= 2) of the sequence are dealt to the slots in node
-// order; for child c with parent u the workgroup sums, over its chunk,
-// max(0, p_u(j) - C q_u(j)) with C = 1 + the normalisers of c's earlier
-// siblings of rank >= 2 (their partials are complete: they belong to earlier
-// launches); the sum over chunks is the normaliser Z of c's test.
+// This lane's eight entries of a 512-entry slice starting at entry `base` of
+// a row (n of them exist; n may be <= 0): float4 path entries base + lane*4
+// + k*256 + i, scalar path base + lane + k*64.  Loads never branch: a
+// missing entry reads the row's first and is replaced by `fill`.
 template <bool VEC>
-__global__ __launch_bounds__(kSampleThreads) void sv_tree_level_kernel(SampleParams p, int rank)
+__device__ __forceinline__ void load_slice(const float *row, int base, int n, float fill, float (&v)[8])
 {
-    __shared__ double s_red[kNWs];
-    __shared__ int s_par[kTreeMaxN], s_rank[kTreeMaxN];
-    __shared__ float s_M;
-    __shared__ double s_iZ, s_C;
+    const int lane = threadIdx.x & 63;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = lane * 4 + k * 256;
+            const bool ok = e < n;  // n is a multiple of 4 on this path
+            const float4 x = *reinterpret_cast<const float4 *>(row + (ok ? base + e : 0));
+            v[4 * k + 0] = ok ? x.x : fill; v[4 * k + 1] = ok ? x.y : fill;
+            v[4 * k + 2] = ok ? x.z : fill; v[4 * k + 3] = ok ? x.w : fill;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = lane + k * kWave;
+            const bool ok = e < n;
+            const float x = row[ok ? base + e : 0];
+            v[k] = ok ? x : fill;
+        }
+    }
+}
+
+// One sibling rank: grid (vocabulary chunk x sequence), sixteen waves per
+// workgroup, wave w on entries [512w, 512w + 512) of the chunk.  For every
+// child c of rank `rank` (>= 2) of the sequence, in node order, each wave
+// sums over its slice max(0, p_u(j) - C q_u(j)) (u the parent) with
+// C = 1 + the normalisers of c's earlier siblings of rank >= 2, i.e. the C
+// of c's previous sibling (kept in tree_c by the launch that tested it)
+// plus that sibling's normaliser (its chunk partials are complete: they
+// belong to an earlier launch).  The waves work independently, each
+// requesting a child's row statistics, C terms and slice together; one
+// barrier at the end sums the sixteen slices of each child into its chunk
+// partial.  The sum of a node's chunk partials is the normaliser Z of its
+// test.
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads * 4) void sv_tree_level_kernel(SampleParams p, int rank)
+{
+    __shared__ int s_par[kTreeMaxN], s_pv[kTreeMaxN], s_kid[kTreeMaxN], s_prev[kTreeMaxN];
+    __shared__ int s_nk;
+    __shared__ double s_part[kLevelWaves][kTreeMaxN];
     const int N = p.K + 1;
-    const int slot = blockIdx.x % kTreeSlots;
-    const int chunk = (blockIdx.x / kTreeSlots) % p.nchunk;
-    const int b = blockIdx.x / (kTreeSlots * p.nchunk);
+    const int chunk = blockIdx.x % p.nchunk;
+    const int b = blockIdx.x / p.nchunk;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     tree_load_parents(p, b, s_par);
     __syncthreads();
-    if (tid < N)
-        s_rank[tid] = tid > 0 ? tree_rank(s_par, tid) : 0;
-    __syncthreads();
-    const int base = chunk * kSampleChunk;
-    const int n = min(kSampleChunk, p.V - base);
-    const Temp t1{false, 1.0, 0.0f, 0.0f};
-    int q = 0;  // index among the children of this rank (uniform)
-    for (int c = 1; c < N; ++c) {
-        if (s_rank[c] != rank)
-            continue;
-        if (q++ % kTreeSlots != slot)
-            continue;
-        const int u = s_par[c];
-        const int row = b * N + u;
-        float v[kPer], w[kPer];
-        load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
-        load_chunk<VEC>(p.probs + (size_t)row * p.V + base, n, 0.0f, w);
-        if (wave == 0) {
-            float M;
-            double iZ;
-            tree_row_mz(p, row, M, iZ);
-            if (lane == 0) {
-                s_M = M;
-                s_iZ = iZ;
+    // thread c: node c's sibling rank and its previous sibling (the child of
+    // the same parent just before it; rank - 1)
+    bool mine = false;
+    if (tid >= 1 && tid < N) {
+        const int u = s_par[tid];
+        int r = 1, prev = -1;
+        for (int c2 = u + 1; c2 < tid; ++c2)
+            if (s_par[c2] == u) {
+                ++r;
+                prev = c2;
             }
-        } else if (wave == 1) {
-            // earlier siblings of rank >= 2, their shares requested together
-            double share[kTreeMaxN];
-            bool use[kTreeMaxN];
-#pragma unroll
-            for (int c2 = 1; c2 < kTreeMaxN; ++c2) {
-                use[c2] = c2 > u && c2 < c && s_par[c2] == u && s_rank[c2] >= 2;
-                share[c2] = use[c2] ? tree_z_share(p, b, c2) : 0.0;
-            }
-            double C = 1.0;
-#pragma unroll
-            for (int c2 = 1; c2 < kTreeMaxN; ++c2)
-                if (use[c2])
-                    C += wave_sum_f64(share[c2]);
-            if (lane == 0)
-                s_C = C;
+        s_pv[tid] = prev;
+        mine = r == rank;
+    }
+    if (wave == 0) {  // the children of this rank in node order (N <= 16 < 64)
+        const uint64_t m = __ballot(mine);
+        if (mine) {
+            const int pos = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+            s_kid[pos] = lane;
+            s_prev[pos] = s_pv[lane];
         }
-        __syncthreads();
-        const float M = s_M;
-        const double invZ = s_iZ, C = s_C;
+        if (lane == 0)
+            s_nk = __builtin_popcountll(m);
+    }
+    __syncthreads();
+    const int nk = __builtin_amdgcn_readfirstlane(s_nk);
+    if (nk == 0)
+        return;  // uniform over the workgroup
+    const int base = chunk * kSampleChunk + wave * kLevelSlice;
+    const int n = min(kLevelSlice, p.V - base);
+    const Temp t1{false, 1.0, 0.0f, 0.0f};
+    const bool fast = p.nchunk <= kWave;  // one chunk statistic per lane
+    const bool hp = rank > 2;             // the previous sibling has its own test (rank >= 2)
+    // Child j's loads, all requested together; the next child's are in
+    // flight while this one is summed.
+    struct Fetch {
+        RowStat st;
+        double zp, cp;
+        float v[8], w[8];
+        int c, prev, row;
+    };
+    auto fetch = [&](int j, Fetch &f) {
+        f.c = __builtin_amdgcn_readfirstlane(s_kid[j]);
+        f.prev = __builtin_amdgcn_readfirstlane(s_prev[j]);
+        f.row = b * N + __builtin_amdgcn_readfirstlane(s_par[f.c]);
+        const int pn = hp ? f.prev : f.c;  // (c: a valid address when unused)
+        f.st = load_or(static_cast<const RowStat *>(p.row_stats), (size_t)f.row * p.nchunk + lane,
+                       fast && lane < p.nchunk, RowStat{-__builtin_inff(), 0, 0.0});
+        f.zp = load_or(p.coefs, ((size_t)b * N + pn) * p.nchunk + lane, fast && hp && lane < p.nchunk, 0.0);
+        f.cp = load_or(p.tree_c, (size_t)b * N + pn, hp, 1.0);
+        load_slice<VEC>(p.logits + (size_t)f.row * p.V, base, n, -__builtin_inff(), f.v);
+        load_slice<VEC>(p.probs + (size_t)f.row * p.V, base, n, 0.0f, f.w);
+    };
+    auto finish = [&](int j, const Fetch &f) {
+        float M;
+        double invZ;
+        if (fast) {
+            M = wave_max_f32(f.st.m);
+            const double z = f.st.z > 0.0 ? f.st.z * exp((double)f.st.m - (double)M) : 0.0;
+            invZ = 1.0 / wave_sum_f64(z);
+        } else {
+            tree_row_mz(p, f.row, M, invZ);
+        }
+        const double C = hp ? f.cp + wave_sum_f64(fast ? f.zp : tree_z_share(p, b, f.prev)) : 1.0;
         double acc = 0.0;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int e = VEC ? ((k >> 2) * kSampleThreads + tid) * 4 + (k & 3) : k * kSampleThreads + tid;
-            const double r = target_prob_fast(v[k], base + e, M, invZ, t1, 0, -__builtin_inff()) - C * (double)w[k];
+        for (int k = 0; k < 8; ++k) {
+            const int e = VEC ? lane * 4 + (k >> 2) * 256 + (k & 3) : lane + k * kWave;
+            const double r = target_prob_fast(f.v[k], base + e, M, invZ, t1, 0, -__builtin_inff()) - C * (double)f.w[k];
             acc += r > 0.0 ? r : 0.0;
         }
         acc = wave_sum_f64(acc);
-        if (lane == 0)
-            s_red[wave] = acc;
-        __syncthreads();
-        if (tid == 0) {
-            double z = 0.0;
-#pragma unroll
-            for (int i = 0; i < kNWs; ++i)
-                z += s_red[i];
-            p.coefs[((size_t)b * N + c) * p.nchunk + chunk] = z;
+        if (lane == 0) {
+            s_part[wave][j] = acc;
+            if (chunk == 0 && wave == 0)
+                p.tree_c[(size_t)b * N + f.c] = C;  // for c's next sibling
         }
-        __syncthreads();  // s_M, s_C and s_red are reused by the next child
+    };
+    Fetch fa, fb;
+    fetch(0, fa);
+    for (int j = 0; j < nk; j += 2) {
+        if (j + 1 < nk)
+            fetch(j + 1, fb);
+        finish(j, fa);
+        if (j + 1 < nk) {
+            if (j + 2 < nk)
+                fetch(j + 2, fa);
+            finish(j + 1, fb);
+        }
+    }
+    __syncthreads();
+    if (tid < nk) {
+        double z = 0.0;
+#pragma unroll
+        for (int w2 = 0; w2 < kLevelWaves; ++w2)
+            z += s_part[w2][tid];
+        p.coefs[((size_t)b * N + s_kid[tid]) * p.nchunk + chunk] = z;
     }
 }
 
@@ -1613,19 +1690,19 @@ hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream)
     const dim3 block(kSampleThreads);
     const int N = p.K + 1;
     const dim3 g1((unsigned)(p.nchunk * p.B * N));
-    const dim3 gl((unsigned)(kTreeSlots * p.nchunk * p.B));
+    const dim3 gl((unsigned)(p.nchunk * p.B));
     const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
     const dim3 g3((unsigned)p.B);
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
         for (int r = 2; r <= p.tree_max_children; ++r)
-            hipLaunchKernelGGL(sv_tree_level_kernel<true>, gl, block, 0, stream, p, r);
+            hipLaunchKernelGGL(sv_tree_level_kernel<true>, gl, dim3(kSampleThreads * 4), 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
         for (int r = 2; r <= p.tree_max_children; ++r)
-            hipLaunchKernelGGL(sv_tree_level_kernel<false>, gl, block, 0, stream, p, r);
+            hipLaunchKernelGGL(sv_tree_level_kernel<false>, gl, dim3(kSampleThreads * 4), 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<false>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<false>, g3, block, 0, stream, p);
     }

@@ -100,6 +100,7 @@ struct SampleParams {
     const int32_t *parents;  // tree: [B][N] BFS parents (parents[b][0] < 0)
     int32_t *path;           // tree: [B][N] accepted node ids, then -1
     double *coefs;           // tree: [B][N][nchunk] chunk partials of each node's test normaliser
+    double *tree_c;          // tree: [B][N] coefficient C of each node's test (ranks >= 2)
     int tree_max_children;   // tree: children tested per node (ranks beyond are skipped)
     int typical;             // typical acceptance instead of the rejection rule
     double ty_eps, ty_delta; // its threshold min(eps, delta exp(-H))
@@ -128,7 +129,7 @@ hipError_t launch_sample(const SampleParams &p, hipStream_t stream);
 // Tree verification: B sequences of N <= 16 BFS-ordered nodes.
 struct TreePlan {
     int nchunk;
-    size_t off_state, off_stats, off_mass, off_coefs, total;
+    size_t off_state, off_stats, off_mass, off_coefs, off_tree_c, total;
 };
 TreePlan plan_sample_tree(int B, int N, int V);
 hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream);

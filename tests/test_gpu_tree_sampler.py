@@ -200,3 +200,12 @@ def test_gpu_output_law_follows_the_rows():
         pv = _chi2(np.bincount(toks[present, i], minlength=V).astype(np.float64), pt[i])
         print("position %d: %d samples, chi2 p=%.3g" % (i, present.sum(), pv))
         assert pv > 1e-3
+
+
+def test_star_tree_fifteen_sibling_ranks():
+    """A root with fifteen children: fifteen sibling tests in a row, each
+    normaliser's coefficient carried through fourteen rank launches."""
+    par = np.array([-1] + [0] * 15, np.int32)
+    for seed, noise in ((14, 0.3), (15, 2.0)):   # high and low acceptance
+        t = W.make_tree(seed, 8, par, 5000, 1.5, noise)
+        assert _compare(t, _run(t), "star tree noise %.1f" % noise) == 0

@@ -163,7 +163,7 @@ template <int D>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
     constexpr int PER = D / 64;  // floats per lane
-    constexpr int NB = 8;        // splits whose partial rows are requested at once
+    constexpr int NB = D == 128 ? 16 : 8;  // splits whose partial rows are requested at once
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int units = p.B * p.Hkv;
@@ -282,6 +282,7 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 // ---------------------------------------------------------------- MFMA kernel
 
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor (V#) of one physical page of one tensor, as four SGPRs:
@@ -414,6 +415,23 @@ __device__ __forceinline__ void tile_store(float *tile, const floatx4 (&acc)[D /
     }
 }
 
+// Stores row pair pp (row tiles 2pp, 2pp+1) of a wave's unnormalised O kept
+// in the 32x32 result layout (d = 128): lane l, register v holds head dims
+// 4i .. 4i+3 (one per dim tile u) of row 32pp + l%32, i = 8(v/4) + 4(l/32) +
+// v%4, into an LDS tile [32][D+4] (its rows 0..31).
+template <int NP>
+__device__ __forceinline__ void tile_store32(float *tile, const floatx16 (&acc)[4][NP], int lane, int pp)
+{
+    constexpr int OP = 128 + 4;
+    const int r = lane & 31, i0 = 4 * (lane >> 5);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + i0 + (v & 3);
+        *reinterpret_cast<float4 *>(tile + r * OP + 4 * i) =
+            make_float4(acc[0][pp][v], acc[1][pp][v], acc[2][pp][v], acc[3][pp][v]);
+    }
+}
+
 // Merges the NT wave tiles of rows r0 .. r1-1 of one workgroup and stores
 // the result: normalised output when slot < 0 (the workgroup saw the unit's
 // whole context), else the unnormalised partial (o, max, sum) in workspace
@@ -473,6 +491,9 @@ template <int D, int RG, bool FP8>
 struct MfmaShape {
     typedef PageGeom<D, FP8> PG;
     static constexpr int NW = kMfmaWaves<RG, FP8>;
+    // E4M3, d = 128, an even number of row tiles: PV runs on the 32x32x16
+    // matrix instruction (see mfma_segment).
+    static constexpr bool PV32 = FP8 && D == 128 && RG % 2 == 0;
     // Ring stages per wave: about 8 KB of copies in flight behind the page
     // being computed.  (Deeper rings measured slower: more requests queue at
     // the memory controllers without raising the stream rate.)
@@ -509,6 +530,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     constexpr int EB = PG::EB;
     constexpr int TPH = SH::TPH;
     constexpr int RW = SH::RW;
+    constexpr bool PV32 = SH::PV32;
+    constexpr int NP = PV32 ? RG / 2 : 1;  // row-tile pairs (PV32)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -584,15 +607,26 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     // P on the VALU.
     float m[RG], lpart[RG];
     floatx4 lsum[RG];
-    floatx4 acc[NDT][RG];
+    floatx4 acc[PV32 ? 1 : NDT][PV32 ? 1 : RG];
+    floatx16 acc32[PV32 ? 4 : 1][NP];  // PV32: O^T of dim tile u, row pair pp
 #pragma unroll
     for (int rt = 0; rt < RG; ++rt) {
         m[rt] = ninf;
         lpart[rt] = 0.0f;
         lsum[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (PV32) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            acc[dt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp)
+                acc32[u][pp] = floatx16{};
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RG; ++rt)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[dt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const short4v ones4 = __builtin_bit_cast(short4v, make_uint2(0x3F803F80u, 0x3F803F80u));
 
@@ -603,8 +637,10 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     const int head_off = g * D * EB;
     // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
     const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
-    // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK)
-    const int v_voff = head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
+    // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK); PV32: lane ->
+    // (dims 4*(l%32) .. +3, key 8*(l/32) + copy)
+    const int v_voff = PV32 ? head_off + 8 * (lane >> 5) * slot_stride + 4 * (lane & 31)
+                            : head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
     const uint32_t ring_lds =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * RW;
     unsigned char *ring = smem + wave * RW;
@@ -627,7 +663,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 #pragma unroll
         for (int n = 0; n < PG::NVI; ++n)
             dma_to_lds<PG::VBYTES>(lds + PG::PT + n * 64 * PG::VBYTES, dv, v_voff,
-                                   (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
+                                   PV32 ? n * slot_stride
+                                        : (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
         if constexpr (FP8) {
             const int soff = __builtin_amdgcn_readfirstlane(ph) * 4;
             dma_to_lds<4>(lds + 2 * PG::PT, dks, 0, soff);
@@ -663,7 +700,12 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         for (int i = 0; i < PG::NKI; ++i)
             kraw[i] = *reinterpret_cast<const uint4 *>(st + i * 1024 + lane * 16);
         uint32_t vr[4][NDT / 2];  // [key j][dims 2w, 2w+1 as bf16]
-        if constexpr (PG::VBYTES == 16) {
+        uint32_t vc[8];           // PV32: E4M3 codes of dims 4i..4i+3 (i = l%32) of key 8*(l/32) + j
+        if constexpr (PV32) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                vc[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + j * 256 + lane * 4);
+        } else if constexpr (PG::VBYTES == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(st + PG::PT + j * 1024 + lane * 16);
@@ -712,22 +754,50 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 
         // 3. V operands: slots past the context are cleared, then tile t's
         //    A operand (dim NDT*l16 + t of keys 4*q4 .. 4*q4+3) is gathered.
+        //    PV32: dim tile u's A operand is dim 4*(l%32) + u of keys
+        //    8*(l/32) .. +7 (codes are cleared before conversion; converting
+        //    them later measured faster).
         if (key0 + kBlock > L) {  // wave-uniform: only a sequence's last page
+            if constexpr (PV32) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t keep = slot_keep(true, key0 + 4 * q4 + j, L);
+                for (int j = 0; j < 8; ++j)
+                    vc[j] &= slot_keep(true, key0 + 8 * (lane >> 5) + j, L);
+            } else {
 #pragma unroll
-                for (int w2 = 0; w2 < NDT / 2; ++w2)
-                    vr[j][w2] &= keep;
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t keep = slot_keep(true, key0 + 4 * q4 + j, L);
+#pragma unroll
+                    for (int w2 = 0; w2 < NDT / 2; ++w2)
+                        vr[j][w2] &= keep;
+                }
             }
         }
-        short4v va4[NDT];
+        short4v va4[PV32 ? 1 : NDT];
+        bf16x8 va32[PV32 ? 4 : 1];
+        if constexpr (PV32) {
+            uint2 y[8];  // per key: dims (4i, 4i+1), (4i+2, 4i+3) as bf16 pairs
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-            const int w2 = t >> 1;
-            const uint32_t lo = (t & 1) ? pack_hi16(vr[0][w2], vr[1][w2]) : pack_lo16(vr[0][w2], vr[1][w2]);
-            const uint32_t hi = (t & 1) ? pack_hi16(vr[2][w2], vr[3][w2]) : pack_lo16(vr[2][w2], vr[3][w2]);
-            va4[t] = __builtin_bit_cast(short4v, make_uint2(lo, hi));
+            for (int j = 0; j < 8; ++j)
+                y[j] = e4m3x4_to_bf16x4(vc[j]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t w[4];
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const uint32_t a = u < 2 ? y[2 * w2].x : y[2 * w2].y;
+                    const uint32_t c = u < 2 ? y[2 * w2 + 1].x : y[2 * w2 + 1].y;
+                    w[w2] = (u & 1) ? pack_hi16(a, c) : pack_lo16(a, c);
+                }
+                va32[u] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const int w2 = t >> 1;
+                const uint32_t lo = (t & 1) ? pack_hi16(vr[0][w2], vr[1][w2]) : pack_lo16(vr[0][w2], vr[1][w2]);
+                const uint32_t hi = (t & 1) ? pack_hi16(vr[2][w2], vr[3][w2]) : pack_lo16(vr[2][w2], vr[3][w2]);
+                va4[t] = __builtin_bit_cast(short4v, make_uint2(lo, hi));
+            }
         }
 
         // E4M3 page scales: K's multiplies the scores (folded into the
@@ -772,9 +842,17 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 m[rt] = mnew;
                 lpart[rt] *= alpha;
                 lsum[rt] *= alpha;
+                if constexpr (PV32) {
+                    // the 32x32 result: lane l holds row l%16 of tile 2pp + (l%32)/16
+                    const float a2 = (((lane >> 4) & 1) == (rt & 1)) ? alpha : 1.0f;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    acc[dt][rt] *= alpha;
+                    for (int u = 0; u < 4; ++u)
+                        acc32[u][rt >> 1] *= a2;
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+                        acc[dt][rt] *= alpha;
+                }
             }
         }
         short4v pb[RG];
@@ -793,11 +871,28 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         // 6. O^T += V^T P^T over the page's 16 keys: A = V^T (dim row l16 of
         //    tile t, keys 4*q4..+3), B = P^T (keys 4*q4..+3, row l16), exactly
         //    the S^T output layout.
+        //    PV32: O^T (32 dims x 32 rows) += V^T (32 dims x 16 keys) P^T per
+        //    dim tile and row pair.  P^T's B operand (keys 8*(l/32) .. +7 of
+        //    row l%32 of the pair) is the two tiles' S^T-layout P with the
+        //    16-lane rows exchanged.
+        if constexpr (PV32) {
 #pragma unroll
-        for (int t = 0; t < NDT; ++t)
+            for (int pp = 0; pp < NP; ++pp) {
+                const uint2 a = __builtin_bit_cast(uint2, pb[2 * pp]), c = __builtin_bit_cast(uint2, pb[2 * pp + 1]);
+                const auto x0 = __builtin_amdgcn_permlane16_swap(a.x, c.x, false, false);
+                const auto x1 = __builtin_amdgcn_permlane16_swap(a.y, c.y, false, false);
+                const bf16x8 pbb = __builtin_bit_cast(bf16x8, make_uint4(x0[0], x1[0], x0[1], x1[1]));
 #pragma unroll
-            for (int rt = 0; rt < RG; ++rt)
-                acc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[t], pb[rt], acc[t][rt], 0, 0, 0);
+                for (int u = 0; u < 4; ++u)
+                    acc32[u][pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va32[u], pbb, acc32[u][pp], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+#pragma unroll
+                for (int rt = 0; rt < RG; ++rt)
+                    acc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[t], pb[rt], acc[t][rt], 0, 0, 0);
+        }
         if constexpr (!FP8) {
 #pragma unroll
             for (int rt = 0; rt < RG; ++rt)
@@ -829,7 +924,10 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     for (int rt0 = 0; rt0 < RG; rt0 += TPH) {
         if (rt0 > 0)
             __syncthreads();  // the previous phase's tiles are consumed
-        tile_store<D, RG, TPH>(reinterpret_cast<float *>(ring), acc, l16, q4, rt0);
+        if constexpr (PV32)
+            tile_store32<NP>(reinterpret_cast<float *>(ring), acc32, lane, rt0 / 2);
+        else
+            tile_store<D, RG, TPH>(reinterpret_cast<float *>(ring), acc, l16, q4, rt0);
         __syncthreads();
         merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, oslot, b, g,
                                          rt0 * 16, min(p.TG, (rt0 + TPH) * 16));

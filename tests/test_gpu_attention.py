@@ -27,6 +27,9 @@ SMALL = [
     (9, 2, 3, 16, 2, 64, [129, 100], "fp8"),
     (10, 2, 5, 8, 2, 64, [90, 300], "f32"),
     (11, 1, 1, 4, 4, 128, [1], "bf16"),                 # single query row, single key
+    (12, 3, 6, 64, 8, 128, [333, 6, 1100], "fp8"),      # E4M3, T*G = 48: row halves of two and one tiles
+    (13, 2, 16, 16, 4, 64, [500, 260], "fp8"),          # E4M3, d=64, T*G = 64
+    (14, 2, 5, 64, 8, 128, [2100, 47], "fp8"),          # E4M3, T*G = 40: the second half's last tile is padding
 ]
 
 
@@ -206,13 +209,15 @@ def test_balanced_shares_deterministic_with_garbage_workspace():
         assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("B", [1000, 1024])
-def test_balanced_shares_many_sequences(B):
+@pytest.mark.parametrize("B,T,Hq,d,kv", [(1000, 5, 16, 64, "bf16"), (1024, 5, 16, 64, "bf16"),
+                                         (1024, 7, 64, 128, "fp8")])
+def test_balanced_shares_many_sequences(B, T, Hq, d, kv):
     """Up to the 1024 sequences the balanced prefix sums hold: every thread
-    of the workgroup carries four sequences' page counts."""
+    of the workgroup carries four (8-wave E4M3 workgroups: two) sequences'
+    page counts."""
     rng = np.random.default_rng(B)
-    lens = [int(x) for x in rng.integers(5, 200, size=B)]
-    a = W.make_attn_from_lens(34, B, 5, 16, 8, 64, lens, kv="bf16", extra_blocks=2)
+    lens = [int(x) for x in rng.integers(T, 200, size=B)]
+    a = W.make_attn_from_lens(34, B, T, Hq, 8, d, lens, kv=kv, extra_blocks=2)
     out = run_attn(a, blocks_per_split=-1)
     rows = sample_rows(a, 2048, seed=3)
     err = _check(a, out, rows)

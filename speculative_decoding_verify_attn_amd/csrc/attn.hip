@@ -478,34 +478,63 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
     }
 }
 
-// Waves per workgroup of the matrix-core kernel, and row tiles merged per
-// epilogue phase (two phases for three or four row tiles keep the parked
-// output rows within a ring's size).  Measured: 8 waves streamed no faster
-// for bf16 (c2: 29.8 vs 28.9 us) and slower for E4M3 (c5b: 102 vs 82 us with
-// 8 waves, 121 with 6).
-template <int RG, bool FP8>
-constexpr int kMfmaWaves = 4;
-constexpr int kTilesPerPhase = 2;
+// Shared pages (E4M3, d = 128, three or four row tiles): the workgroup runs
+// 8 waves, two per SIMD.  Waves w and w+4 take the same pages (every 4th of
+// the run) and each owns two of the row tiles; wave w copies each page into
+// their common ring and a workgroup barrier per page hands it to wave w+4.
+// One wave per SIMD leaves about half of such a page's time in stalls (the
+// matrix instructions alone issue at near their peak rate from one wave);
+// the second wave fills them.  Not used for bf16, which streams at the
+// memory's rate with 4 waves.  Also measured: 8 waves each with every row
+// tile and every 8th page streamed no faster for bf16 (c2: 29.8 vs 28.9 us)
+// and slower for E4M3 (registers spill); 8 waves in which w and w+4 each copy
+// the same pages into their own rings doubled the memory traffic.
+#ifndef SV_SHARE_PAGES
+#define SV_SHARE_PAGES 1
+#endif
+template <int D, int RG, bool FP8>
+constexpr bool kSharePages = SV_SHARE_PAGES && FP8 && D == 128 && RG >= 3;
+constexpr int kPageWaves = 4;      // waves that split a run's pages
+constexpr int kTilesPerPhase = 2;  // row tiles merged per epilogue phase
 
 template <int D, int RG, bool FP8>
 struct MfmaShape {
     typedef PageGeom<D, FP8> PG;
-    static constexpr int NW = kMfmaWaves<RG, FP8>;
-    // E4M3, d = 128, an even number of row tiles: PV runs on the 32x32x16
-    // matrix instruction (see mfma_segment).
-    static constexpr bool PV32 = FP8 && D == 128 && RG % 2 == 0;
-    // Ring stages per wave: about 8 KB of copies in flight behind the page
-    // being computed.  (Deeper rings measured slower: more requests queue at
-    // the memory controllers without raising the stream rate.)
+    static constexpr bool SHARE = kSharePages<D, RG, FP8>;
+    static constexpr int HV = SHARE ? 2 : 1;          // waves per page stream
+    static constexpr int NWP = kPageWaves;            // page streams
+    static constexpr int NW = NWP * HV;               // waves per workgroup
+    static constexpr int RGW = (RG + HV - 1) / HV;    // row tiles per wave
+    // E4M3, d = 128, an even number of row tiles per wave: PV runs on the
+    // 32x32x16 matrix instruction (see mfma_segment).
+    static constexpr bool PV32 = FP8 && D == 128 && RGW % 2 == 0;
+    // PV32: the V slice moves as two 16-byte copies per page (key-major rows
+    // of 128 bytes) and each lane reads its keys' dims from other lanes'
+    // bytes once the copying wave's wait (and, with shared pages, the
+    // barrier) has passed; otherwise each lane reads back only its own copies.
+    static constexpr int NVI = PV32 ? 2 : PG::NVI;            // V copies per page
+    static constexpr int VB = PV32 ? 16 : PG::VBYTES;          // V copy width
+    static constexpr int NI = PG::NKI + NVI + (FP8 ? 2 : 0);  // copies per page
+    // Ring stages per page stream: about 8 KB of copies in flight behind the
+    // page being computed (shared pages: one page behind the page being
+    // waited for, which one barrier later is computed; 3 stages measured
+    // 67.8 us on c5b against 70-72 with 4 and 72.6 with 5).  (Deeper rings
+    // measured slower: more requests queue at the memory controllers without
+    // raising the stream rate.)
     static constexpr int NS0 = 1 + (8192 + PG::STAGE - 1) / PG::STAGE;
     static constexpr int NS = NS0 > 4 ? 4 : NS0;
     static constexpr int OP = D + 4;
-    static constexpr int TPH = RG < kTilesPerPhase ? RG : kTilesPerPhase;  // row tiles per epilogue phase
+    static constexpr int TPH = RGW < kTilesPerPhase ? RGW : kTilesPerPhase;  // row tiles per epilogue phase
     static constexpr int WT = TPH * 16 * OP;  // floats of one wave's parked O rows
-    // Each wave's LDS region holds its page ring, and at the end its O tile.
-    static constexpr int RW0 = NS * PG::STAGE > WT * 4 ? NS * PG::STAGE : WT * 4;
-    static constexpr int RW = (RW0 + 15) & ~15;
-    static constexpr int SMEM = NW * RW;
+    // LDS: the page rings (one per page stream, RSTRIDE bytes apart) and, at
+    // the end, each wave's parked O rows (PSTRIDE bytes apart).  With 4 waves
+    // a wave's ring and parked rows share one region.
+    static constexpr int RING = (NS * PG::STAGE + 15) & ~15;
+    static constexpr int PARK = (WT * 4 + 15) & ~15;
+    static constexpr int RW = RING > PARK ? RING : PARK;
+    static constexpr int RSTRIDE = SHARE ? RING : RW;
+    static constexpr int PSTRIDE = SHARE ? PARK : RW;
+    static constexpr int SMEM = NWP * RSTRIDE > NW * PSTRIDE ? NWP * RSTRIDE : NW * PSTRIDE;
 };
 
 // One run of pages of one (sequence b, KV head g) unit: pages blk_begin ..
@@ -529,12 +558,17 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     constexpr int NS = SH::NS;
     constexpr int EB = PG::EB;
     constexpr int TPH = SH::TPH;
-    constexpr int RW = SH::RW;
     constexpr bool PV32 = SH::PV32;
-    constexpr int NP = PV32 ? RG / 2 : 1;  // row-tile pairs (PV32)
+    constexpr bool SHARE = SH::SHARE;
+    constexpr int NWP = SH::NWP;           // page streams
+    constexpr int RGW = SH::RGW;           // row tiles of this wave
+    constexpr int NP = PV32 ? RGW / 2 : 1;  // row-tile pairs (PV32)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int pw = wave % NWP;                // page stream: pages pw, pw + NWP, ... of the run
+    const bool copier = wave < NWP;           // the wave that copies its stream's pages
+    const int rt_base = (wave / NWP) * RGW;   // first row tile of this wave
     const int lane = tid & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int T = p.T, G = p.G, TG = p.TG, Hkv = p.Hkv;
@@ -550,16 +584,16 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     int first[NS - 1];
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
-        const int i = wave + k * NW;
+        const int i = pw + k * NWP;
         first[k] = i < avail ? trow[i] : 0;
     }
     for (int i = tid; i < avail; i += NT)
         s_pages[i] = clamp_block(trow[i], p.num_blocks);
-    float4 qraw[RG][NDC][2];
-    uint32_t anc[RG];  // ancestor set of the lane's verify row (padding rows see everything)
+    float4 qraw[RGW][NDC][2];
+    uint32_t anc[RGW];  // ancestor set of the lane's verify row (padding rows see everything)
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
-        const int row = rt * 16 + l16;
+    for (int rt = 0; rt < RGW; ++rt) {
+        const int row = (rt_base + rt) * 16 + l16;
         const bool valid = row < TG;
         const int t = valid ? row / G : 0;
         anc[rt] = valid ? row_ancestors(p, b, t) : 0xFFFFFFFFu;
@@ -584,9 +618,9 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 
     // Q tile as the B operand of S^T = K Q^T (row = l16, eight dims), bf16,
     // pre-scaled into base-2 units.
-    bf16x8 qf[RG][NDC];
+    bf16x8 qf[RGW][NDC];
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
+    for (int rt = 0; rt < RGW; ++rt) {
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
             const float sc = p.qscale;
@@ -605,12 +639,12 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     // tile t, row l16).  bf16 storage gets its row sums from one extra MFMA
     // with an all-ones A operand; E4M3 storage scales P per page, so it sums
     // P on the VALU.
-    float m[RG], lpart[RG];
-    floatx4 lsum[RG];
-    floatx4 acc[PV32 ? 1 : NDT][PV32 ? 1 : RG];
+    float m[RGW], lpart[RGW];
+    floatx4 lsum[RGW];
+    floatx4 acc[PV32 ? 1 : NDT][PV32 ? 1 : RGW];
     floatx16 acc32[PV32 ? 4 : 1][NP];  // PV32: O^T of dim tile u, row pair pp
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
+    for (int rt = 0; rt < RGW; ++rt) {
         m[rt] = ninf;
         lpart[rt] = 0.0f;
         lsum[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -623,7 +657,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 acc32[u][pp] = floatx16{};
     } else {
 #pragma unroll
-        for (int rt = 0; rt < RG; ++rt)
+        for (int rt = 0; rt < RGW; ++rt)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 acc[dt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -638,20 +672,23 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
     const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
     // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK); PV32: lane ->
-    // (dims 4*(l%32) .. +3, key 8*(l/32) + copy)
-    const int v_voff = PV32 ? head_off + 8 * (lane >> 5) * slot_stride + 4 * (lane & 31)
+    // (bytes 16*(l%8) .. +15 of key l/8 + 8*copy)
+    const int v_voff = PV32 ? head_off + (lane >> 3) * slot_stride + 16 * (lane & 7)
                             : head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
     const uint32_t ring_lds =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + wave * RW;
-    unsigned char *ring = smem + wave * RW;
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + pw * SH::RSTRIDE;
+    const unsigned char *ring = smem + pw * SH::RSTRIDE;
     int4v dks{}, dvs{};
     if constexpr (FP8) {
         dks = page_desc(reinterpret_cast<const unsigned char *>(p.k_scale), 0, (uint32_t)p.num_blocks * 4u);
         dvs = page_desc(reinterpret_cast<const unsigned char *>(p.v_scale), 0, (uint32_t)p.num_blocks * 4u);
     }
 
-    // This wave's pages are blk_begin + wave + k*NW, k = 0, 1, ...
-    const int nk = npg > wave ? (npg - wave + NW - 1) / NW : 0;
+    // This wave's pages are blk_begin + pw + k*NWP, k = 0, 1, ...  With
+    // shared pages every wave runs the same number of steps (one barrier
+    // each); a stream with one page fewer skips its last step's work.
+    const int nk = npg > pw ? (npg - pw + NWP - 1) / NWP : 0;
+    const int nsteps = SHARE ? (npg + NWP - 1) / NWP : nk;
     auto issue = [&](int k, int ph) {
         const int stage = k % NS;
         const uint32_t lds = ring_lds + stage * PG::STAGE;
@@ -661,36 +698,53 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         for (int i = 0; i < PG::NKI; ++i)
             dma_to_lds<16>(lds + i * 1024, dk, k_voff, FP8 ? i * 64 : i * 32 * EB);
 #pragma unroll
-        for (int n = 0; n < PG::NVI; ++n)
-            dma_to_lds<PG::VBYTES>(lds + PG::PT + n * 64 * PG::VBYTES, dv, v_voff,
-                                   PV32 ? n * slot_stride
-                                        : (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
+        for (int n = 0; n < SH::NVI; ++n)
+            dma_to_lds<SH::VB>(lds + PG::PT + n * 64 * SH::VB, dv, v_voff,
+                               PV32 ? n * 8 * slot_stride
+                                    : (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
         if constexpr (FP8) {
             const int soff = __builtin_amdgcn_readfirstlane(ph) * 4;
             dma_to_lds<4>(lds + 2 * PG::PT, dks, 0, soff);
             dma_to_lds<4>(lds + 2 * PG::PT + 256, dvs, 0, soff);
         }
     };
+    // Waits until at most `younger` pages' copies are outstanding (they
+    // complete in issue order).
+    auto wait_pages = [&](int younger) {
+        if (younger >= 3)
+            wait_dma<3 * SH::NI>();
+        else if (younger == 2)
+            wait_dma<2 * SH::NI>();
+        else if (younger == 1)
+            wait_dma<SH::NI>();
+        else
+            wait_dma<0>();
+    };
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k)
-        if (k < nk)
+        if (copier && k < nk)
             issue(k, clamp_block(first[k], p.num_blocks));
     __syncthreads();  // s_pages ready
 
-    for (int k = 0; k < nk; ++k) {
-        if (k + NS - 1 < nk)
-            issue(k + NS - 1, s_pages[wave + (k + NS - 1) * NW]);
-        // wait for page k: the copies of up to NS-1 younger pages may stay in flight
-        const int younger = (nk - 1 - k) < (NS - 1) ? (nk - 1 - k) : (NS - 1);
-        if (younger >= 3)
-            wait_dma<3 * PG::NI>();
-        else if (younger == 2)
-            wait_dma<2 * PG::NI>();
-        else if (younger == 1)
-            wait_dma<PG::NI>();
-        else
-            wait_dma<0>();
-        const int pg = wave + k * NW;
+    for (int k = 0; k < nsteps; ++k) {
+        if constexpr (SHARE) {
+            // Page k has landed (pages k+1 .. k+NS-2 may stay in flight);
+            // after the barrier the partner may read it, and both waves are
+            // done with page k-1, whose stage the next copy reuses.
+            if (copier)
+                wait_pages(min(NS - 2, nk - 1 - k));
+            __syncthreads();
+            if (copier && k + NS - 1 < nk)
+                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * NWP]);
+            if (k >= nk)
+                continue;  // wave-uniform: this stream has one page fewer
+        } else {
+            if (k + NS - 1 < nk)
+                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * NWP]);
+            // wait for page k: the copies of up to NS-1 younger pages may stay in flight
+            wait_pages(min(NS - 1, nk - 1 - k));
+        }
+        const int pg = pw + k * NWP;
         const int key0 = (blk_begin + pg) * kBlock;
         const unsigned char *st = ring + (k % NS) * PG::STAGE;
 
@@ -704,7 +758,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         if constexpr (PV32) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                vc[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + j * 256 + lane * 4);
+                vc[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + (8 * (lane >> 5) + j) * 128 +
+                                                            4 * (lane & 31));
         } else if constexpr (PG::VBYTES == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -727,9 +782,9 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         }
 
         // 2. S^T = K Q^T (keys on M, rows on N).
-        floatx4 s[RG];
+        floatx4 s[RGW];
 #pragma unroll
-        for (int rt = 0; rt < RG; ++rt)
+        for (int rt = 0; rt < RGW; ++rt)
             s[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
 #pragma unroll
@@ -737,7 +792,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 const bf16x8 k0 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(kraw[i].x, kraw[i].y)));
                 const bf16x8 k1 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(kraw[i].z, kraw[i].w)));
 #pragma unroll
-                for (int rt = 0; rt < RG; ++rt) {
+                for (int rt = 0; rt < RGW; ++rt) {
                     s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[rt][2 * i], s[rt], 0, 0, 0);
                     s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[rt][2 * i + 1], s[rt], 0, 0, 0);
                 }
@@ -747,7 +802,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             for (int dc = 0; dc < NDC; ++dc) {
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, kraw[dc]);
 #pragma unroll
-                for (int rt = 0; rt < RG; ++rt)
+                for (int rt = 0; rt < RGW; ++rt)
                     s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][dc], s[rt], 0, 0, 0);
             }
         }
@@ -812,7 +867,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         //    sequence need it).
         if (key0 + kBlock - 1 > L - T) {
 #pragma unroll
-            for (int rt = 0; rt < RG; ++rt)
+            for (int rt = 0; rt < RGW; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (!key_visible(key0 + q4 * 4 + i, L, T, anc[rt]))
@@ -823,17 +878,17 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         //    kSlack; only then (a wave-uniform, rarely taken branch) are the
         //    row maxima reduced across lanes and the accumulators rescaled.
         //    So P = 2^(s - m) <= 2^kSlack always.
-        float mloc[RG];
+        float mloc[RGW];
         bool need = false;
 #pragma unroll
-        for (int rt = 0; rt < RG; ++rt) {
+        for (int rt = 0; rt < RGW; ++rt) {
             mloc[rt] = ksc * fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
             need = need || (mloc[rt] > m[rt] + kSlack);
         }
         if (__builtin_expect(__ballot(need) != 0, 0)) {
             __asm__ volatile("" ::: "memory");  // keep this block a real branch
 #pragma unroll
-            for (int rt = 0; rt < RG; ++rt) {
+            for (int rt = 0; rt < RGW; ++rt) {
                 float mx = mloc[rt];
                 mx = fmaxf(mx, xor_lane_f32(mx, 16));
                 mx = fmaxf(mx, xor_lane_f32(mx, 32));
@@ -855,9 +910,9 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 }
             }
         }
-        short4v pb[RG];
+        short4v pb[RGW];
 #pragma unroll
-        for (int rt = 0; rt < RG; ++rt) {
+        for (int rt = 0; rt < RGW; ++rt) {
             const float msafe = (m[rt] == ninf) ? 0.0f : m[rt];
             float pr[4];
 #pragma unroll
@@ -890,23 +945,24 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
 #pragma unroll
-                for (int rt = 0; rt < RG; ++rt)
+                for (int rt = 0; rt < RGW; ++rt)
                     acc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4[t], pb[rt], acc[t][rt], 0, 0, 0);
         }
         if constexpr (!FP8) {
 #pragma unroll
-            for (int rt = 0; rt < RG; ++rt)
+            for (int rt = 0; rt < RGW; ++rt)
                 lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb[rt], lsum[rt], 0, 0, 0);
         }
     }
 
     // ---- epilogue: each wave parks its (max, sum) rows and unnormalised
-    // tile in its own LDS region (its ring is idle once its copies have
-    // landed), and after one barrier a single pass merges the waves and
-    // writes the result.
+    // tile in its own LDS region (with 4 waves its ring, idle once its copies
+    // have landed; with shared pages after a barrier, once both waves of
+    // every stream are done with the rings), and after one barrier a single
+    // pass merges the waves of each row half and writes the result.
     wait_dma<0>();
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
+    for (int rt = 0; rt < RGW; ++rt) {
         float ls;
         if constexpr (FP8) {
             ls = lpart[rt];
@@ -916,21 +972,30 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             ls = lsum[rt][0];
         }
         if (q4 == 0) {
-            s_m[wave][rt * 16 + l16] = m[rt];
-            s_l[wave][rt * 16 + l16] = ls;
+            s_m[wave][(rt_base + rt) * 16 + l16] = m[rt];
+            s_l[wave][(rt_base + rt) * 16 + l16] = ls;
         }
     }
+    if constexpr (SHARE)
+        __syncthreads();  // the parked rows overwrite the rings
+    float *park = reinterpret_cast<float *>(smem + wave * SH::PSTRIDE);
 #pragma unroll
-    for (int rt0 = 0; rt0 < RG; rt0 += TPH) {
+    for (int rt0 = 0; rt0 < RGW; rt0 += TPH) {
         if (rt0 > 0)
             __syncthreads();  // the previous phase's tiles are consumed
         if constexpr (PV32)
-            tile_store32<NP>(reinterpret_cast<float *>(ring), acc32, lane, rt0 / 2);
+            tile_store32<NP>(park, acc32, lane, rt0 / 2);
         else
-            tile_store<D, RG, TPH>(reinterpret_cast<float *>(ring), acc, l16, q4, rt0);
+            tile_store<D, RGW, TPH>(park, acc, l16, q4, rt0);
         __syncthreads();
-        merge_waves_and_store<D, RG, NW>(p, reinterpret_cast<const float *>(smem), RW / 4, s_m, s_l, oslot, b, g,
-                                         rt0 * 16, min(p.TG, (rt0 + TPH) * 16));
+        // row half h: the tiles of waves h*NWP .. h*NWP + NWP-1
+#pragma unroll
+        for (int h = 0; h < SH::HV; ++h) {
+            const int r0 = (h * RGW + rt0) * 16, r1 = min(p.TG, (h * RGW + rt0 + TPH) * 16);
+            if (r0 < r1)
+                merge_waves_and_store<D, RGW, NWP>(p, reinterpret_cast<const float *>(smem + h * NWP * SH::PSTRIDE),
+                                                   SH::PSTRIDE / 4, s_m + h * NWP, s_l + h * NWP, oslot, b, g, r0, r1);
+        }
     }
 }
 
@@ -942,7 +1007,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 // meets.  The merge kernel finds a cut unit's partials from the same prefix
 // sums, which workgroup 0 leaves in the workspace.
 template <int D, int RG, bool FP8, bool BAL>
-__global__ __launch_bounds__((64 * kMfmaWaves<RG, FP8>), 1) void sv_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_mfma_kernel(AttnParams p)
 {
     typedef MfmaShape<D, RG, FP8> SH;
     constexpr int NW = SH::NW;
@@ -1181,7 +1246,7 @@ template <int D, int RG, bool FP8>
 hipError_t launch_mfma_rg(const AttnParams &p, hipStream_t s)
 {
     auto kern = p.balanced ? sv_attn_mfma_kernel<D, RG, FP8, true> : sv_attn_mfma_kernel<D, RG, FP8, false>;
-    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * kMfmaWaves<RG, FP8>), 0, s, p);
+    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * MfmaShape<D, RG, FP8>::NW), 0, s, p);
     return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ SMALL = [
     (12, 3, 6, 64, 8, 128, [333, 6, 1100], "fp8"),      # E4M3, T*G = 48: row halves of two and one tiles
     (13, 2, 16, 16, 4, 64, [500, 260], "fp8"),          # E4M3, d=64, T*G = 64
     (14, 2, 5, 64, 8, 128, [2100, 47], "fp8"),          # E4M3, T*G = 40: the second half's last tile is padding
+    (15, 2, 4, 64, 8, 128, [613, 4], "fp8"),            # E4M3, T*G = 32: two row tiles, one wave per page
 ]
 
 

@@ -178,11 +178,12 @@ def test_graph_replay_tree_sampler_and_commit():
 
 def test_graph_replay_attention_balanced_and_check():
     """Attention with balanced shares (prefix sums in the workspace, cut units
-    merged), fp8 and bf16, and the input check, captured and replayed."""
+    merged), fp8 and bf16 (fp8 also with four row tiles: two waves per page),
+    and the input check, captured and replayed."""
     dev = torch.device("cuda", 0)
     cases = []
-    for kv in ("bf16", "fp8"):
-        aa = [W.make_attn_from_lens(40 + i, 5, 5, 32, 8, 128, [700, 33, 2100, 5, 1290], kv=kv) for i in range(2)]
+    for kv, T, Hq in (("bf16", 5, 32), ("fp8", 5, 32), ("fp8", 7, 64)):
+        aa = [W.make_attn_from_lens(40 + i, 5, T, Hq, 8, 128, [700, 33, 2100, 7, 1290], kv=kv) for i in range(2)]
         cases.append((aa, [upload_attn(a) for a in aa]))
     for aa, tt in cases:
         a = aa[0]

@@ -798,11 +798,16 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     __shared__ double s_th[16];
     __shared__ int s_acc[16];
     __shared__ int s_n;
-    __shared__ double s_part[kNWs][2];
+    __shared__ double s_part[kDecideMaxSpw][kNWs][2];
 
+    // This workgroup covers sub-chunks sub0 .. sub0 + nsh - 1 of sequence b
+    // (the statistics and the tests are done once for all of them).
     const int nsub = (p.V + kSampleSub - 1) / kSampleSub;
-    const int b = blockIdx.x / nsub;
-    const int sub = blockIdx.x - b * nsub;
+    const int spw = p.spw;
+    const int ngrp = (nsub + spw - 1) / spw;
+    const int b = blockIdx.x / ngrp;
+    const int sub0 = (blockIdx.x - b * ngrp) * spw;
+    const int nsh = min(spw, nsub - sub0);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int K = p.K, K1 = K + 1, V = p.V;
@@ -945,42 +950,58 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     const int arg = s_A[n];
     const float tau = s_tau[n];
 
-    // 3. Mass of this sub-chunk: residual (or bonus) weights and plain
-    //    target mass.
-    const int base = sub * kSampleSub;
-    const int cnt = min(kSampleSub, V - base);
-    float lv[4], qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    load_sub<VEC>(p.logits + ((size_t)b * K1 + n) * V + base, cnt, -__builtin_inff(), lv);
-    if (residual)
-        load_sub<VEC>(p.probs + ((size_t)b * K + n) * V + base, cnt, 0.0f, qv);
-    double sw = 0.0, sp = 0.0;
+    // 3. Mass of each sub-chunk: residual (or bonus) weights and plain
+    //    target mass (every sub-chunk's entries requested at once).
+    float lv[kDecideMaxSpw][4], qv[kDecideMaxSpw][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, tp, arg, tau);
-        sp += pj;
-        if (residual) {
-            const double r = pj - (double)qv[k];
-            sw += r > 0.0 ? r : 0.0;
-        } else {
-            sw += pj;
+    for (int j = 0; j < kDecideMaxSpw; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qv[j][k] = 0.0f;
+        if (j < nsh) {  // uniform
+            const int base = (sub0 + j) * kSampleSub;
+            const int cnt = min(kSampleSub, V - base);
+            load_sub<VEC>(p.logits + ((size_t)b * K1 + n) * V + base, cnt, -__builtin_inff(), lv[j]);
+            if (residual)
+                load_sub<VEC>(p.probs + ((size_t)b * K + n) * V + base, cnt, 0.0f, qv[j]);
         }
     }
-    sw = wave_sum_f64(sw);
-    sp = wave_sum_f64(sp);
-    if (lane == 0) {
-        s_part[wave][0] = sw;
-        s_part[wave][1] = sp;
+#pragma unroll
+    for (int j = 0; j < kDecideMaxSpw; ++j) {
+        if (j >= nsh)
+            break;  // uniform
+        const int base = (sub0 + j) * kSampleSub;
+        double sw = 0.0, sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double pj = target_prob_fast(lv[j][k], base + tid * 4 + k, M, invZ, tp, arg, tau);
+            sp += pj;
+            if (residual) {
+                const double r = pj - (double)qv[j][k];
+                sw += r > 0.0 ? r : 0.0;
+            } else {
+                sw += pj;
+            }
+        }
+        sw = wave_sum_f64(sw);
+        sp = wave_sum_f64(sp);
+        if (lane == 0) {
+            s_part[j][wave][0] = sw;
+            s_part[j][wave][1] = sp;
+        }
     }
     __syncthreads();
-    if (tid < 2) {
-        double t = s_part[0][tid];
+    if (tid < 2 * nsh) {
+        const int j = tid >> 1, c = tid & 1;
+        double t = s_part[j][0][c];
 #pragma unroll
         for (int w = 1; w < kNWs; ++w)
-            t += s_part[w][tid];
-        p.sub_mass[((size_t)b * nsub + sub) * 2 + tid] = t;
+            t += s_part[j][w][c];
+        p.sub_mass[((size_t)b * nsub + sub0 + j) * 2 + c] = t;
     }
 
     // The first workgroup of the sequence records what the draw needs.
+    const int sub = sub0;
     if (sub == 0 && tid == 0) {
         SeqState ss;
         ss.n = n;
@@ -1657,11 +1678,19 @@ __global__ void sv_fill_zero_kernel(uint4 *p, size_t n16, unsigned char *tail, s
 
 }  // namespace
 
-hipError_t launch_sample(const SampleParams &p, hipStream_t stream)
+hipError_t launch_sample(const SampleParams &p0, hipStream_t stream)
 {
+    // Decide: one workgroup per sub-chunk while the grid fits in one round of
+    // resident workgroups (about 2048); larger batches give each workgroup up
+    // to kDecideMaxSpw consecutive sub-chunks, so the statistics merge and the
+    // tests (two dependent round trips) are not repeated per sub-chunk.
+    SampleParams p = p0;
+    const long long nsub = (p.V + kSampleSub - 1) / kSampleSub;
+    const long long want = (nsub * p.B + 2047) / 2048;
+    p.spw = (int)(want < 1 ? 1 : (want > kDecideMaxSpw ? kDecideMaxSpw : want));
     const dim3 block(kSampleThreads);
     const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
-    const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
+    const dim3 g2((unsigned)(((nsub + p.spw - 1) / p.spw) * p.B));
     const dim3 g3((unsigned)p.B);
     const dim3 gc((unsigned)(p.B * (p.K + 1)));
     const dim3 gh = g1;

@@ -80,6 +80,7 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream);
 constexpr int kSampleChunk = 8192;  // vocabulary entries per sampler workgroup
 constexpr int kSampleSub = 1024;    // entries per sub-chunk (unit of the draw's rescan)
 constexpr int kSampleThreads = 256;
+constexpr int kDecideMaxSpw = 4;     // sub-chunks one decide workgroup covers at most
 constexpr int kMaxSampleChunks = 2048;  // V <= 2048 * 8192
 
 struct SampleParams {
@@ -111,6 +112,7 @@ struct SampleParams {
     double *sub_mass;        // [B][ceil(V/1024)][2] {residual weight, target mass}
     int B, K, V, nchunk;
     int vec4;                // rows start 16-byte aligned and V % 4 == 0
+    int spw;                 // chain decide: consecutive sub-chunks per workgroup (1..kDecideMaxSpw; set by launch_sample)
 };
 
 struct SamplePlan {

@@ -42,6 +42,8 @@ SHAPES = [
     (5, 12, 6, 30001, 3.0, 2.0),    # scalar path, several chunks
     (6, 256, 2, 64, 0.5, 0.1),      # high acceptance
     (7, 40, 5, 16384, 3.0, 3.0),    # low acceptance, exact chunk multiple
+    (8, 64, 3, 99001, 2.0, 1.5),    # decide workgroups of 4 sub-chunks, the last one with 1; scalar path
+    (9, 100, 2, 50000, 3.0, 1.0),   # decide workgroups of 3 sub-chunks, the last one with 1
 ]
 
 

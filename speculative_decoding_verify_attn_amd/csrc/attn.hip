@@ -159,11 +159,13 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 // entries of splits past the context are discarded.  Balanced shares: the
 // unit's first slot and its number of partials come from the prefix sums the
 // attention kernel left in the workspace, then the same loads follow.
-template <int D>
+// NB: splits whose partial rows are requested at once (16 for many fixed
+// splits: c5b's 32 splits 10.1 -> 9.0 us; else 8, whose fewer registers keep
+// more waves resident: balanced shares at B = 64 12.0 us against 15.6).
+template <int D, int NB>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
     constexpr int PER = D / 64;  // floats per lane
-    constexpr int NB = D == 128 ? 16 : 8;  // splits whose partial rows are requested at once
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int units = p.B * p.Hkv;
@@ -1281,9 +1283,11 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
     const long long waves = (long long)p.B * p.Hkv * p.TG;
     const dim3 grid((unsigned)((waves + 3) / 4));
     if (p.d == 64)
-        hipLaunchKernelGGL(sv_attn_merge_kernel<64>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8>), grid, dim3(256), 0, stream, p);
+    else if (!p.balanced && p.max_splits > 8)
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 16>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL(sv_attn_merge_kernel<128>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

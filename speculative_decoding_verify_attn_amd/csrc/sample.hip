@@ -1471,12 +1471,18 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
     __shared__ int s_path[kMaxN];
     __shared__ int s_n, s_t;
     __shared__ double s_coef;
-    __shared__ double s_part[kNWs][2];
+    __shared__ double s_part[kDecideMaxSpw][kNWs][2];
 
     const int N = p.K + 1, V = p.V;
+    // This workgroup covers sub-chunks sub0 .. sub0 + nsh - 1 of sequence b
+    // (the walk is done once for all of them).
     const int nsub = (V + kSampleSub - 1) / kSampleSub;
-    const int b = blockIdx.x / nsub;
-    const int sub = blockIdx.x - b * nsub;
+    const int spw = p.spw;
+    const int ngrp = (nsub + spw - 1) / spw;
+    const int b = blockIdx.x / ngrp;
+    const int sub0 = (blockIdx.x - b * ngrp) * spw;
+    const int nsh = min(spw, nsub - sub0);
+    const int sub = sub0;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const Temp t1{false, 1.0, 0.0f, 0.0f};
@@ -1597,38 +1603,54 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
     const float M = s_M[t];
     const double invZ = s_iZ[t];
 
-    // 3. Mass of this sub-chunk: final weights and plain target mass.
-    const int base = sub * kSampleSub;
-    const int cnt = min(kSampleSub, V - base);
-    float lv[4], qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    load_sub<VEC>(p.logits + ((size_t)b * N + t) * V + base, cnt, ninf, lv);
-    if (coef > 0.0)
-        load_sub<VEC>(p.probs + ((size_t)b * N + t) * V + base, cnt, 0.0f, qv);
-    double sw = 0.0, sp = 0.0;
+    // 3. Mass of each sub-chunk: final weights and plain target mass (every
+    //    sub-chunk's entries requested at once).
+    float lv[kDecideMaxSpw][4], qv[kDecideMaxSpw][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, t1, 0, ninf);
-        sp += pj;
-        if (coef > 0.0) {
-            const double r = pj - coef * (double)qv[k];
-            sw += r > 0.0 ? r : 0.0;
-        } else {
-            sw += pj;
+    for (int j = 0; j < kDecideMaxSpw; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qv[j][k] = 0.0f;
+        if (j < nsh) {  // uniform
+            const int base = (sub0 + j) * kSampleSub;
+            const int cnt = min(kSampleSub, V - base);
+            load_sub<VEC>(p.logits + ((size_t)b * N + t) * V + base, cnt, ninf, lv[j]);
+            if (coef > 0.0)
+                load_sub<VEC>(p.probs + ((size_t)b * N + t) * V + base, cnt, 0.0f, qv[j]);
         }
     }
-    sw = wave_sum_f64(sw);
-    sp = wave_sum_f64(sp);
-    if (lane == 0) {
-        s_part[wave][0] = sw;
-        s_part[wave][1] = sp;
+#pragma unroll
+    for (int j = 0; j < kDecideMaxSpw; ++j) {
+        if (j >= nsh)
+            break;  // uniform
+        const int base = (sub0 + j) * kSampleSub;
+        double sw = 0.0, sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double pj = target_prob_fast(lv[j][k], base + tid * 4 + k, M, invZ, t1, 0, ninf);
+            sp += pj;
+            if (coef > 0.0) {
+                const double r = pj - coef * (double)qv[j][k];
+                sw += r > 0.0 ? r : 0.0;
+            } else {
+                sw += pj;
+            }
+        }
+        sw = wave_sum_f64(sw);
+        sp = wave_sum_f64(sp);
+        if (lane == 0) {
+            s_part[j][wave][0] = sw;
+            s_part[j][wave][1] = sp;
+        }
     }
     __syncthreads();
-    if (tid < 2) {
-        double acc = s_part[0][tid];
+    if (tid < 2 * nsh) {
+        const int j = tid >> 1, c = tid & 1;
+        double acc = s_part[j][0][c];
 #pragma unroll
         for (int w = 1; w < kNWs; ++w)
-            acc += s_part[w][tid];
-        p.sub_mass[((size_t)b * nsub + sub) * 2 + tid] = acc;
+            acc += s_part[j][w][c];
+        p.sub_mass[((size_t)b * nsub + sub0 + j) * 2 + c] = acc;
     }
 
     // 4. The first workgroup of the sequence writes the state of the draw and
@@ -1714,13 +1736,17 @@ hipError_t launch_sample(const SampleParams &p0, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_sample_tree(const SampleParams &p, hipStream_t stream)
+hipError_t launch_sample_tree(const SampleParams &p0, hipStream_t stream)
 {
+    SampleParams p = p0;  // decide workgroups per sequence: as in launch_sample
+    const long long nsub = (p.V + kSampleSub - 1) / kSampleSub;
+    const long long want = (nsub * p.B + 2047) / 2048;
+    p.spw = (int)(want < 1 ? 1 : (want > kDecideMaxSpw ? kDecideMaxSpw : want));
     const dim3 block(kSampleThreads);
     const int N = p.K + 1;
     const dim3 g1((unsigned)(p.nchunk * p.B * N));
     const dim3 gl((unsigned)(p.nchunk * p.B));
-    const dim3 g2((unsigned)(((p.V + kSampleSub - 1) / kSampleSub) * p.B));
+    const dim3 g2((unsigned)(((nsub + p.spw - 1) / p.spw) * p.B));
     const dim3 g3((unsigned)p.B);
     if (p.vec4) {
         hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);

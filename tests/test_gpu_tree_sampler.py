@@ -78,6 +78,8 @@ CASES = [
     (4, "binary3", 12, 777, 2.0, 0.7),      # scalar path
     (5, "wide5x2", 8, 8193, 1.0, 0.3),      # two chunks and a 1-entry tail, high acceptance
     (6, "chain5", 16, 32000, 3.0, 1.0),
+    (7, "wide5x2", 24, 99001, 2.0, 1.0),    # decide workgroups of 2 sub-chunks, the last one with 1; scalar path
+    (8, "binary3", 48, 50000, 3.0, 1.0),    # decide workgroups of 2 sub-chunks, the last one with 1
 ]
 
 

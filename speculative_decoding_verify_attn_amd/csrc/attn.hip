@@ -357,7 +357,8 @@ __device__ __forceinline__ uint4 to_bf16x8(uint2 v)
 
 // Geometry of one 16-token page of one KV head as it travels HBM -> LDS.
 // Every lane reads back from LDS exactly the bytes its own copies wrote, so
-// the only synchronisation a page needs is the wave's own vmcnt wait.
+// the only synchronisation a page needs is the wave's own vmcnt wait (the
+// E4M3 32x32x16 PV path and shared pages differ: see MfmaShape).
 //   K: lane l = (slot l%16, lane group q4 = l/16) carries the A operand of
 //      S^T = K Q^T for every 32-wide head-dim chunk dc (eight dims per lane).
 //      bf16: one 16-byte copy per chunk; E4M3: one 16-byte copy carries two
@@ -487,10 +488,12 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
 // One wave per SIMD leaves about half of such a page's time in stalls (the
 // matrix instructions alone issue at near their peak rate from one wave);
 // the second wave fills them.  Not used for bf16, which streams at the
-// memory's rate with 4 waves.  Also measured: 8 waves each with every row
-// tile and every 8th page streamed no faster for bf16 (c2: 29.8 vs 28.9 us)
-// and slower for E4M3 (registers spill); 8 waves in which w and w+4 each copy
-// the same pages into their own rings doubled the memory traffic.
+// memory's rate with 4 waves (shared pages measured slower there: 70B-layer
+// shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
+// each with every row tile and every 8th page streamed no faster for bf16
+// (c2: 29.8 vs 28.9 us) and slower for E4M3 (registers spill); 8 waves in
+// which w and w+4 each copy the same pages into their own rings doubled the
+// memory traffic.
 #ifndef SV_SHARE_PAGES
 #define SV_SHARE_PAGES 1
 #endif

@@ -110,7 +110,7 @@ def probe_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, file=sys.stderr, flush=True)
         sys.exit(2)
     if args.probe == "copy":

@@ -43,7 +43,7 @@ typedef enum {
     SV_OK = 0,
     SV_ERR_NULL = 1,        /* a required pointer is NULL                          */
     SV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
-    SV_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement       */
+    SV_ERR_UNSUPPORTED = 3, /* a valid request the library does not implement      */
     SV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returned   */
     SV_ERR_ALIGN = 5,       /* a pointer lacks the alignment stated for it         */
     SV_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing  */

@@ -159,9 +159,10 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 // entries of splits past the context are discarded.  Balanced shares: the
 // unit's first slot and its number of partials come from the prefix sums the
 // attention kernel left in the workspace, then the same loads follow.
-// NB: splits whose partial rows are requested at once (16 for many fixed
-// splits: c5b's 32 splits 10.1 -> 9.0 us; else 8, whose fewer registers keep
-// more waves resident: balanced shares at B = 64 12.0 us against 15.6).
+// NB: splits whose partial rows are requested at once (16 or 32 for many
+// fixed splits, where the grid has few waves: c5b's 32 splits 10.1 us with
+// 8, 9.0 with 16; else 8, whose fewer registers keep more waves resident:
+// balanced shares at B = 64 12.0 us against 15.6 with 16).
 template <int D, int NB>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
@@ -1287,6 +1288,8 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
     const dim3 grid((unsigned)((waves + 3) / 4));
     if (p.d == 64)
         hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8>), grid, dim3(256), 0, stream, p);
+    else if (!p.balanced && p.max_splits > 16)
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 32>), grid, dim3(256), 0, stream, p);
     else if (!p.balanced && p.max_splits > 8)
         hipLaunchKernelGGL((sv_attn_merge_kernel<128, 16>), grid, dim3(256), 0, stream, p);
     else

@@ -21,12 +21,13 @@
 //
 // Matrix-core kernel (bf16 / E4M3 storage), per wave and page:
 //   * the page's K and V slices (16 slots x d) stream HBM -> LDS with direct
-//     buffer-to-LDS copies into a 4-stage ring, so three pages are in flight
-//     while one is computed and no registers hold data in flight;
+//     buffer-to-LDS copies into a small ring (about 8 KB in flight behind
+//     the page being computed), so no registers hold data in flight;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, query rows on N);
-//     each lane reads back its own K operand, Q sits in registers as bf16;
-//   * V is transposed once through LDS into a swizzled [dim][slot] tile
-//     written over the consumed K slice (conflict-free writes and reads);
+//     K moves as whole slot rows and each lane reads its operand from an
+//     XOR-swizzled position (conflict-free), Q sits in registers as bf16;
+//   * each lane reads four keys' worth of V head dims and builds the PV A
+//     operand with byte permutes (no transpose through LDS);
 //   * S^T leaves each lane holding one query row's P for four keys, which is
 //     exactly the B operand of v_mfma_f32_16x16x16_bf16 for O^T += V^T P^T,
 //     so P needs no cross-lane shuffle; bf16 row sums come from the same
@@ -357,14 +358,16 @@ __device__ __forceinline__ uint4 to_bf16x8(uint2 v)
 }
 
 // Geometry of one 16-token page of one KV head as it travels HBM -> LDS.
-// Every lane reads back from LDS exactly the bytes its own copies wrote, so
-// the only synchronisation a page needs is the wave's own vmcnt wait (the
-// E4M3 32x32x16 PV path and shared pages differ: see MfmaShape).
-//   K: lane l = (slot l%16, lane group q4 = l/16) carries the A operand of
-//      S^T = K Q^T for every 32-wide head-dim chunk dc (eight dims per lane).
-//      bf16: one 16-byte copy per chunk; E4M3: one 16-byte copy carries two
-//      chunks (sixteen dims), so the chunk -> dim map is permuted the same way
-//      on the Q side.
+// A wave reads back only bytes that its own copies wrote, once its vmcnt
+// wait has passed (shared pages add a barrier: see MfmaShape).
+//   K: each copy instruction moves whole 256-byte (bf16, d = 128) slot rows
+//      of the slice, several slots per copy; whole rows stream faster from
+//      HBM than the same bytes cut into 64-byte pieces of 16 rows.  Lane
+//      l = (slot l%16, lane group q4 = l/16) then reads from LDS the A
+//      operand of S^T = K Q^T for every 32-wide head-dim chunk dc (eight
+//      dims): bf16: piece 4*dc + q4 of its slot; E4M3: one 16-byte piece
+//      carries two chunks (sixteen dims), so the chunk -> dim map is permuted
+//      the same way on the Q side.
 //   V: lane l = (dim group m = l%16, key group q4 = l/16) carries, for each
 //      of the keys 4*q4 .. 4*q4+3, the NDT = D/16 consecutive head dims
 //      NDT*m .. NDT*m+NDT-1.  Row m of PV dim tile t is head dim NDT*m + t,
@@ -391,6 +394,21 @@ struct PageGeom {
     static constexpr int NVI = 4 * VPK;                // V copies per page
     static constexpr int NI = NKI + NVI + (FP8 ? 2 : 0);  // copies per page
     static_assert(NVI * 64 * VBYTES == PT, "V copies cover the page slice");
+    // K copies move whole slot rows: a row of the head's slice is KPS
+    // 16-byte pieces, a copy carries KSPC consecutive slots, and within a row
+    // the pieces are stored XOR-swizzled by kswz(slot), so that the 16 lanes
+    // reading one piece of 16 different slots hit distinct LDS banks.
+    static constexpr int KPS = D * EB / 16;   // pieces per slot row
+    static constexpr int KSPC = 64 / KPS;     // slots per copy
+    static constexpr int KRPB = 16 / KPS;     // slots per 256-byte LDS row
+    static_assert(NKI * KSPC == 16, "K copies cover the page's 16 slots");
+    static __device__ __forceinline__ int kswz(int slot) { return (slot / KRPB) % KPS; }
+    // byte offset, within the K slice in LDS, of piece pc (head dims
+    // 16*pc/EB .. +16/EB) of slot `slot`
+    static __device__ __forceinline__ int kread(int slot, int pc)
+    {
+        return (slot / KSPC) * 1024 + ((slot % KSPC) * KPS + (pc ^ kswz(slot))) * 16;
+    }
     // first head dim of lane group q4 in MFMA chunk dc
     static __device__ __forceinline__ int qdim(int dc, int q4)
     {
@@ -675,8 +693,13 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     const int slot_stride = Hkv * D * EB;                          // bytes between slots of a page
     const uint32_t page_bytes = (uint32_t)slot_stride * kBlock;    // bytes of one page (all heads)
     const int head_off = g * D * EB;
-    // K copy: lane -> (slot l16, dims of lane group q4), 16 bytes per chunk copy
-    const int k_voff = head_off + l16 * slot_stride + (FP8 ? q4 * 16 : q4 * 8 * EB);
+    // K copy i: lane -> slot i*KSPC + lane/KPS, piece (lane%KPS) ^ kswz(slot)
+    int k_voff[PG::NKI];
+#pragma unroll
+    for (int i = 0; i < PG::NKI; ++i) {
+        const int r = lane / PG::KPS;
+        k_voff[i] = head_off + r * slot_stride + ((lane % PG::KPS) ^ PG::kswz(i * PG::KSPC + r)) * 16;
+    }
     // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK); PV32: lane ->
     // (bytes 16*(l%8) .. +15 of key l/8 + 8*copy)
     const int v_voff = PV32 ? head_off + (lane >> 3) * slot_stride + 16 * (lane & 7)
@@ -702,7 +725,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         const int4v dv = page_desc(vbase, __builtin_amdgcn_readfirstlane(ph), page_bytes);
 #pragma unroll
         for (int i = 0; i < PG::NKI; ++i)
-            dma_to_lds<16>(lds + i * 1024, dk, k_voff, FP8 ? i * 64 : i * 32 * EB);
+            dma_to_lds<16>(lds + i * 1024, dk, k_voff[i], i * PG::KSPC * slot_stride);
 #pragma unroll
         for (int n = 0; n < SH::NVI; ++n)
             dma_to_lds<SH::VB>(lds + PG::PT + n * 64 * SH::VB, dv, v_voff,
@@ -754,11 +777,11 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         const int key0 = (blk_begin + pg) * kBlock;
         const unsigned char *st = ring + (k % NS) * PG::STAGE;
 
-        // 1. Read back this lane's K and V bytes of the page.
+        // 1. Read back this lane's K operands and V bytes of the page.
         uint4 kraw[PG::NKI];
 #pragma unroll
         for (int i = 0; i < PG::NKI; ++i)
-            kraw[i] = *reinterpret_cast<const uint4 *>(st + i * 1024 + lane * 16);
+            kraw[i] = *reinterpret_cast<const uint4 *>(st + PG::kread(l16, 4 * i + q4));
         uint32_t vr[4][NDT / 2];  // [key j][dims 2w, 2w+1 as bf16]
         uint32_t vc[8];           // PV32: E4M3 codes of dims 4i..4i+3 (i = l%32) of key 8*(l/32) + j
         if constexpr (PV32) {

@@ -61,12 +61,7 @@ typedef enum {
 typedef enum {
     SV_ATTN_AUTO = 0,  /* matrix cores for bf16/fp8 storage, vector ALU for fp32  */
     SV_ATTN_VALU = 1,  /* vector-ALU kernel, any storage type                      */
-    SV_ATTN_MFMA = 2,  /* matrix-core kernel (bf16 and fp8 storage only)           */
-    /* Flag, OR-ed into one of the above, for measurement only: enqueue just
-     * the main attention kernel.  When the context is split (see
-     * spec_verify_attn_ex) `out` is then NOT written; the unnormalised
-     * partials stay in the workspace. */
-    SV_ATTN_MAIN_ONLY = 0x100
+    SV_ATTN_MFMA = 2   /* matrix-core kernel (bf16 and fp8 storage only)           */
 } sv_attn_algo;
 
 int sv_abi_version(void);
@@ -157,6 +152,33 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
                         float sm_scale, void *workspace, size_t workspace_bytes,
                         void *stream, int algo, int blocks_per_split,
                         void *main_done_event);
+
+/* MEASUREMENT ONLY -- not part of the verify step.  Validates exactly as
+ * spec_verify_attn_ex, then enqueues the main attention kernel alone, so
+ * that back-to-back calls between two events time that kernel by itself.
+ * When the planner (or blocks_per_split) splits a sequence's context, `out`
+ * is NOT written: the unnormalised partials stay in the workspace and the
+ * split merge that spec_verify_attn_ex would run next is skipped.  Never use
+ * its `out` as a result. */
+int spec_verify_attn_timing_main_only(const float *q, const void *k_cache, const void *v_cache,
+                                      const float *k_scale, const float *v_scale,
+                                      const int32_t *block_table, const int32_t *context_lens,
+                                      float *out, int B, int T, int Hq, int Hkv, int d,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int kv_dtype, float sm_scale, void *workspace,
+                                      size_t workspace_bytes, void *stream, int algo,
+                                      int blocks_per_split);
+
+/* MEASUREMENT ONLY -- not part of the verify step.  The practical HBM read
+ * ceiling the attention kernel is compared with: one plain streaming read
+ * of `bytes` bytes (a positive multiple of 16) at the 16-byte aligned device
+ * pointer `src`, contiguous chunks per workgroup.  Each thread leaves a
+ * float in `sink` (device memory of at least
+ * spec_verify_probe_read_sink_floats() floats), so the reads cannot be
+ * dropped; its values mean nothing. */
+size_t spec_verify_probe_read_sink_floats(void);
+int spec_verify_probe_read(const void *src, size_t bytes, float *sink, size_t sink_floats,
+                           void *stream);
 
 /* ------------------------------------------------------------------------
  * spec_verify_sample: the rejection sampler of the verify step.

@@ -22,7 +22,6 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK = 0
 SV_KV_F32, SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1, 2
 SV_ATTN_AUTO, SV_ATTN_VALU, SV_ATTN_MFMA = 0, 1, 2
-SV_ATTN_MAIN_ONLY = 0x100  # measurement flag: main kernel only (out not written when split)
 BLOCK_SIZE = 16
 
 _lib = None
@@ -61,6 +60,12 @@ def lib():
         L.spec_verify_attn.argtypes = attn_args
         L.spec_verify_attn_ex.restype = I
         L.spec_verify_attn_ex.argtypes = attn_args + [I, I, P]
+        L.spec_verify_attn_timing_main_only.restype = I
+        L.spec_verify_attn_timing_main_only.argtypes = attn_args + [I, I]
+        L.spec_verify_probe_read_sink_floats.restype = S
+        L.spec_verify_probe_read_sink_floats.argtypes = []
+        L.spec_verify_probe_read.restype = I
+        L.spec_verify_probe_read.argtypes = [P, S, P, S, P]
         L.spec_verify_attn_tree.restype = I
         L.spec_verify_attn_tree.argtypes = [P] * 9 + [I] * 9 + [F, P, S, P, I, I]
         L.spec_verify_sample_workspace_size.restype = S
@@ -123,6 +128,11 @@ def attn_workspace_size(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split=0
     return n
 
 
+def attn_shape_supported(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split=0) -> bool:
+    """Whether spec_verify_attn accepts this shape (its workspace query is non-zero)."""
+    return lib().spec_verify_attn_workspace_size_ex(B, T, Hq, Hkv, d, max_blocks_per_seq, blocks_per_split) != 0
+
+
 def sample_workspace_size(B, K, V) -> int:
     n = lib().spec_verify_sample_workspace_size(B, K, V)
     if n == 0:
@@ -164,6 +174,39 @@ def spec_verify_attn(q, k_cache, v_cache, block_table, context_lens, out, worksp
         kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(stream, q.device), int(algo), int(blocks_per_split), main_done_event))
     return out
+
+
+def spec_verify_attn_timing_main_only(q, k_cache, v_cache, block_table, context_lens, out, workspace, *,
+                                      k_scale=None, v_scale=None, sm_scale=None, kv_dtype=None, stream=None,
+                                      algo=SV_ATTN_AUTO, blocks_per_split=0):
+    """MEASUREMENT ONLY: enqueues the main attention kernel alone (no split
+    merge), so back-to-back calls time that kernel; `out` is not a result
+    (it is not written when the context is split)."""
+    B, T, Hq, d = q.shape
+    num_blocks, bs, Hkv, d2 = k_cache.shape
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    if sm_scale is None:
+        sm_scale = 1.0 / (d ** 0.5)
+    _check("spec_verify_attn_timing_main_only", lib().spec_verify_attn_timing_main_only(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
+        kv_dtype, float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream, q.device), int(algo), int(blocks_per_split)))
+
+
+def probe_read_sink(device) -> torch.Tensor:
+    """A sink tensor for spec_verify_probe_read."""
+    return torch.empty(int(lib().spec_verify_probe_read_sink_floats()), dtype=torch.float32, device=device)
+
+
+def spec_verify_probe_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None):
+    """MEASUREMENT ONLY: one streaming read of the first nbytes of src (the
+    practical HBM read ceiling)."""
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the source tensor")
+    _check("spec_verify_probe_read", lib().spec_verify_probe_read(
+        _ptr(src), int(nbytes), _ptr(sink), sink.numel(), _stream_handle(stream, src.device)))
 
 
 def spec_verify_attn_tree(q, k_cache, v_cache, block_table, context_lens, tree_mask, out, workspace, *,

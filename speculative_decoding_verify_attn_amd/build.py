@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["capi.cpp", "attn.hip", "sample.hip", "kvcache.hip", "check.hip"]
+SOURCES = ["capi.cpp", "attn.hip", "sample.hip", "kvcache.hip", "check.hip", "probe.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc emits no packed fp32 add/mul/fma (v_pk_*_f32).

@@ -230,7 +230,7 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
               const int32_t *block_table, const int32_t *context_lens, const uint32_t *tree_mask, float *out, int B,
               int T, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq, int num_blocks, int kv_dtype,
               float sm_scale, void *workspace, size_t workspace_bytes, void *stream, int algo, int blocks_per_split,
-              void *main_done_event)
+              void *main_done_event, bool main_only)
 {
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(SV_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and out must be non-NULL");
@@ -250,8 +250,6 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
         return fail(SV_ERR_SHAPE, "k_scale / v_scale must be NULL unless kv_dtype is E4M3");
     if (!(std::isfinite(sm_scale)) || sm_scale <= 0.0f)
         return fail(SV_ERR_SHAPE, "sm_scale must be finite and positive");
-    const bool main_only = (algo & SV_ATTN_MAIN_ONLY) != 0;
-    algo &= ~SV_ATTN_MAIN_ONLY;
     if (algo != SV_ATTN_AUTO && algo != SV_ATTN_VALU && algo != SV_ATTN_MFMA)
         return fail(SV_ERR_UNSUPPORTED, "unknown algo %d", algo);
     if (algo == SV_ATTN_MFMA && kv_dtype == SV_KV_F32)
@@ -351,7 +349,38 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
 {
     return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, nullptr, out, B, T, Hq, Hkv,
                      d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace, workspace_bytes,
-                     stream, algo, blocks_per_split, main_done_event);
+                     stream, algo, blocks_per_split, main_done_event, false);
+}
+
+size_t spec_verify_probe_read_sink_floats(void) { return (size_t)sv::kProbeWgs * sv::kProbeThreads; }
+
+int spec_verify_probe_read(const void *src, size_t bytes, float *sink, size_t sink_floats, void *stream)
+{
+    if (!src || !sink)
+        return fail(SV_ERR_NULL, "src and sink must be non-NULL");
+    if (bytes == 0 || bytes % 16)
+        return fail(SV_ERR_SHAPE, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+    if (sink_floats < spec_verify_probe_read_sink_floats())
+        return fail(SV_ERR_SHAPE, "sink holds %zu floats, needs %zu", sink_floats,
+                    spec_verify_probe_read_sink_floats());
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return fail(SV_ERR_ALIGN, "src must be 16-byte and sink 4-byte aligned");
+    const hipError_t e = sv::launch_probe_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "read probe launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_verify_attn_timing_main_only(const float *q, const void *k_cache, const void *v_cache,
+                                      const float *k_scale, const float *v_scale, const int32_t *block_table,
+                                      const int32_t *context_lens, float *out, int B, int T, int Hq, int Hkv,
+                                      int d, int block_size, int max_blocks_per_seq, int num_blocks, int kv_dtype,
+                                      float sm_scale, void *workspace, size_t workspace_bytes, void *stream,
+                                      int algo, int blocks_per_split)
+{
+    return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, nullptr, out, B, T, Hq, Hkv,
+                     d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace, workspace_bytes,
+                     stream, algo, blocks_per_split, nullptr, true);
 }
 
 int spec_verify_attn_tree(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
@@ -364,7 +393,7 @@ int spec_verify_attn_tree(const float *q, const void *k_cache, const void *v_cac
         return fail(SV_ERR_NULL, "tree_mask must be non-NULL (spec_verify_attn is the chain)");
     return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, tree_mask, out, B, T, Hq,
                      Hkv, d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace,
-                     workspace_bytes, stream, algo, blocks_per_split, nullptr);
+                     workspace_bytes, stream, algo, blocks_per_split, nullptr, false);
 }
 
 int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,

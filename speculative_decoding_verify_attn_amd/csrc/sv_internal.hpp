@@ -178,6 +178,12 @@ struct CheckParams {
     int B, T, max_blocks, num_blocks, n_tokens, V, n_uniforms;
 };
 hipError_t launch_check_inputs(const CheckParams &p, hipStream_t stream);
+// Measurement only: a plain streaming read of a device buffer (the practical
+// HBM read ceiling); the sink holds kProbeWgs * kProbeThreads floats.
+constexpr int kProbeWgs = 1024;
+constexpr int kProbeThreads = 256;
+hipError_t launch_probe_read(const void *src, size_t bytes, float *sink, hipStream_t stream);
+
 hipError_t launch_rollback(const int32_t *num_accepted, int32_t *context_lens, int32_t *pages_in_use, int B, int K,
                            hipStream_t stream);
 

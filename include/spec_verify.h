@@ -153,6 +153,30 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
                         void *stream, int algo, int blocks_per_split,
                         void *main_done_event);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * attention of spec_verify_attn, with the planner's split, using a static
+ * device scratch array of the library instead of a caller workspace.  The
+ * results are those of spec_verify_attn bit for bit.  Nothing is allocated:
+ * the array (spec_verify_attn_noalloc_max_bytes() bytes, 32 MiB) lives in the
+ * library's code object, one copy per GPU, held until the process ends; the
+ * first call on a device looks up its address there (hipGetSymbolAddress)
+ * with that device current.  A shape whose split needs more scratch than the
+ * array holds (spec_verify_attn_workspace_size > the maximum) returns
+ * SV_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and give undefined results; calls in one
+ * stream order are safe.  Nothing in the array needs clearing between calls.
+ * Arguments, errors and the device the work runs on (that of `stream`) as
+ * spec_verify_attn. */
+size_t spec_verify_attn_noalloc_max_bytes(void);
+int spec_verify_attn_noalloc(const float *q, const void *k_cache, const void *v_cache,
+                             const float *k_scale, const float *v_scale,
+                             const int32_t *block_table, const int32_t *context_lens,
+                             float *out, int B, int T, int Hq, int Hkv, int d,
+                             int block_size, int max_blocks_per_seq, int num_blocks,
+                             int kv_dtype, float sm_scale, void *stream);
+
 /* MEASUREMENT ONLY -- not part of the verify step.  Validates exactly as
  * spec_verify_attn_ex, then enqueues the main attention kernel alone, so
  * that back-to-back calls between two events time that kernel by itself.

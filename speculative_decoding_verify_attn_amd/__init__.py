@@ -62,6 +62,10 @@ def lib():
         L.spec_verify_attn_ex.argtypes = attn_args + [I, I, P]
         L.spec_verify_attn_timing_main_only.restype = I
         L.spec_verify_attn_timing_main_only.argtypes = attn_args + [I, I]
+        L.spec_verify_attn_noalloc_max_bytes.restype = S
+        L.spec_verify_attn_noalloc_max_bytes.argtypes = []
+        L.spec_verify_attn_noalloc.restype = I
+        L.spec_verify_attn_noalloc.argtypes = [P] * 8 + [I] * 9 + [F, P]
         L.spec_verify_probe_read_sink_floats.restype = S
         L.spec_verify_probe_read_sink_floats.argtypes = []
         L.spec_verify_probe_read.restype = I
@@ -207,6 +211,29 @@ def spec_verify_probe_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor, s
         raise ValueError("nbytes exceeds the source tensor")
     _check("spec_verify_probe_read", lib().spec_verify_probe_read(
         _ptr(src), int(nbytes), _ptr(sink), sink.numel(), _stream_handle(stream, src.device)))
+
+
+def attn_noalloc_max_bytes() -> int:
+    """Size of the static scratch behind spec_verify_attn_noalloc."""
+    return int(lib().spec_verify_attn_noalloc_max_bytes())
+
+
+def spec_verify_attn_noalloc(q, k_cache, v_cache, block_table, context_lens, out, *,
+                             k_scale=None, v_scale=None, sm_scale=None, kv_dtype=None, stream=None):
+    """spec_verify_attn without a workspace: the library's static device
+    scratch stands in for it (see include/spec_verify.h; calls that overlap
+    in time on one GPU race)."""
+    B, T, Hq, d = q.shape
+    num_blocks, bs, Hkv, d2 = k_cache.shape
+    if kv_dtype is None:
+        kv_dtype = kv_dtype_of(k_cache)
+    if sm_scale is None:
+        sm_scale = 1.0 / (d ** 0.5)
+    _check("spec_verify_attn_noalloc", lib().spec_verify_attn_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), B, T, Hq, Hkv, d, bs, block_table.shape[1], num_blocks,
+        kv_dtype, float(sm_scale), _stream_handle(stream, q.device)))
+    return out
 
 
 def spec_verify_attn_tree(q, k_cache, v_cache, block_table, context_lens, tree_mask, out, workspace, *,

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/spec_verify.h"
 #include "sv_internal.hpp"
@@ -36,6 +37,59 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+// Scratch memory of spec_verify_attn_noalloc: the split partials and prefix
+// sums that spec_verify_attn keeps in the caller's workspace, held instead in
+// a static device array.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: host code only ever uses the device address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kNoAllocMaxDevices];  // device address of `scratch`, per device (null: not looked up yet)
+
+// The device address of `scratch` on the device that `stream` belongs to (the
+// current device for the NULL stream), looked up once per device with that
+// device current.
+int noalloc_scratch(hipStream_t stream, void **ptr)
+{
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(SV_ERR_HIP, "finding the stream's device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kNoAllocMaxDevices)
+        return fail(SV_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch supports", dev,
+                    kNoAllocMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return fail(SV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(SV_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess && e2 != hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess || !p)
+            return fail(SV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SV_OK;
+}
 
 }  // namespace
 
@@ -350,6 +404,29 @@ int spec_verify_attn_ex(const float *q, const void *k_cache, const void *v_cache
     return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, nullptr, out, B, T, Hq, Hkv,
                      d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, workspace, workspace_bytes,
                      stream, algo, blocks_per_split, main_done_event, false);
+}
+
+size_t spec_verify_attn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int spec_verify_attn_noalloc(const float *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                             const float *v_scale, const int32_t *block_table, const int32_t *context_lens,
+                             float *out, int B, int T, int Hq, int Hkv, int d, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int kv_dtype, float sm_scale, void *stream)
+{
+    // the plan of spec_verify_attn (the planner's split), so results agree bit for bit
+    const size_t need = spec_verify_attn_workspace_size(B, T, Hq, Hkv, d, max_blocks_per_seq);
+    if (need > kNoAllocScratchBytes)
+        return fail(SV_ERR_UNSUPPORTED, "this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                                        "(use spec_verify_attn with a workspace)", need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    const int st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != SV_OK)
+        return st;
+    // need == 0 (a shape the planner rejects) falls through to attn_impl's own
+    // validation, which names the problem
+    return attn_impl(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, nullptr, out, B, T, Hq, Hkv,
+                     d, block_size, max_blocks_per_seq, num_blocks, kv_dtype, sm_scale, ws, kNoAllocScratchBytes,
+                     stream, SV_ATTN_AUTO, 0, nullptr, false);
 }
 
 size_t spec_verify_probe_read_sink_floats(void) { return (size_t)sv::kProbeWgs * sv::kProbeThreads; }

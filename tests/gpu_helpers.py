@@ -75,6 +75,25 @@ def sample_rows(a: W.AttnInputs, n, seed=0):
     return np.unique(np.concatenate([np.array(fixed, dtype=np.int64), extra.astype(np.int64)]))
 
 
+def unit_rows(a: W.AttnInputs, seed=0):
+    """Flat row indices with at least one row of every (sequence, KV head)
+    unit: a random (verify row, head of the group) per unit, plus the last
+    verify row of the group's first and last head.  Returns (rows, units
+    covered)."""
+    rng = np.random.default_rng(seed)
+    G = a.Hq // a.Hkv
+    rows = []
+    for b in range(a.B):
+        for g in range(a.Hkv):
+            t = int(rng.integers(0, a.T))
+            rows.append((b * a.T + t) * a.Hq + g * G + int(rng.integers(0, G)))
+            rows.append((b * a.T + a.T - 1) * a.Hq + g * G)
+            rows.append((b * a.T + a.T - 1) * a.Hq + g * G + G - 1)
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    units = {(int(r) // (a.T * a.Hq), (int(r) % a.Hq) // G) for r in rows}
+    return rows, units
+
+
 def upload_sample(s: W.SampleInputs):
     d = dev()
     return {

@@ -10,7 +10,7 @@ import torch
 
 import speculative_decoding_verify_attn_amd as sv
 import workloads as W
-from .gpu_helpers import TOL, oracle_attn, row_rel_err, run_attn, sample_rows, upload_attn
+from .gpu_helpers import TOL, oracle_attn, row_rel_err, run_attn, sample_rows, unit_rows, upload_attn
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,27 @@ def test_forced_splits_merge(bps):
     assert _check(a, out_v) <= TOL[a.kv_dtype]
 
 
+# Many fixed splits: the merge variants that prefetch 16 or 32 splits' rows.
+# bps=4 over 313 pages gives 79 splits (more than the 32 requested at once,
+# and more than one statistic per lane); bps=16 gives 20 (the 32-split
+# prefetch, partly empty).  The short sequence has 2 splits, so most of its
+# prefetched slots are discarded (never written in this call: the workspace
+# starts filled with 0xAB).  Every row is compared, for both kernels.
+@pytest.mark.parametrize("bps", [4, 16])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_forced_many_splits_merge(bps, kv):
+    a = W.make_attn_from_lens(24, 3, 6, 32, 8, 128, [5000, 80, 1500], kv=kv)
+    t = upload_attn(a)
+    for algo in (sv.SV_ATTN_AUTO, sv.SV_ATTN_VALU):
+        ws = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, bps),
+                                t["q"].device)
+        ws.fill_(0xAB)
+        out = run_attn(a, t, algo=algo, blocks_per_split=bps, ws=ws)
+        err = _check(a, out)
+        print("bps %d %s algo %d: max row rel err %.3e" % (bps, kv, algo, err))
+        assert err <= TOL[a.kv_dtype]
+
+
 def test_deterministic_and_workspace_reusable():
     # a workspace full of garbage must not matter: nothing in it is read before written
     a = W.make_attn_from_lens(22, 4, 5, 64, 8, 128, [2000, 33, 700, 1024], kv="bf16")
@@ -101,23 +122,23 @@ def test_physical_placement_is_invisible():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5a", "c5b"])
+# Full-size configurations in the launch configuration bench.py times (the
+# planner's split).  c1, c2, c5a and c5b: every output row.  c3 and c4 (whose
+# balanced shares cut units at arbitrary pages): at least one row of every
+# (sequence, KV head) unit plus 384 sampled rows, and the covered units are
+# asserted to be all of them.
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b"])
 def test_config_full_size(name):
     a = W.make_attn(name, seed=0)
     out = run_attn(a)
-    rows = None if name == "c1" else sample_rows(a, 384, seed=1)
+    if name in ("c3", "c4"):
+        rows, units = unit_rows(a, seed=1)
+        assert len(units) == a.B * a.Hkv
+        rows = np.union1d(rows, sample_rows(a, 384, seed=2))
+    else:
+        rows = None
     err = _check(a, out, rows)
     print("%s max row rel err %.3e over %s rows" % (name, err, "all" if rows is None else len(rows)))
-    assert err <= TOL[a.kv_dtype]
-    assert torch.isfinite(out).all()
-
-
-def test_config_ragged_full_size():
-    a = W.make_attn("c4", seed=0)
-    out = run_attn(a)
-    rows = sample_rows(a, 384, seed=2)
-    err = _check(a, out, rows)
-    print("c4 max row rel err %.3e" % err)
     assert err <= TOL[a.kv_dtype]
     assert torch.isfinite(out).all()
 

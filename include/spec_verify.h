@@ -96,7 +96,7 @@ int spec_verify_workspace_clear(void *workspace, size_t bytes, void *stream);
  * context_lens [B] int32, T <= L_b <= 16*max_blocks_per_seq.
  * out          [B,T,Hq,d] float32, 16-byte aligned; fully overwritten.
  * T            = K+1 verify rows per sequence, 1..16.
- * Hq % Hkv == 0; T*(Hq/Hkv) <= 64; d in {64,128}; block_size == 16;
+ * Hq % Hkv == 0; T*(Hq/Hkv) <= 128; d in {64,128}; block_size == 16;
  * max_blocks_per_seq <= 65536 (contexts up to 1M tokens).
  * sm_scale     softmax scale, normally 1/sqrt(d).
  * workspace    >= spec_verify_attn_workspace_size(...) bytes, 256-byte
@@ -259,7 +259,7 @@ int spec_verify_sample_typical(const float *target_logits, const int32_t *draft_
  *   other sets give undefined (but memory-safe) results.  The chain's sets
  *   {0..t} make this spec_verify_attn_ex exactly.
  * Every other argument, the workspace and the errors as spec_verify_attn_ex
- * (T <= 16, T*Hq/Hkv <= 64). */
+ * (T <= 16, T*Hq/Hkv <= 128). */
 int spec_verify_attn_tree(const float *q, const void *k_cache, const void *v_cache,
                           const float *k_scale, const float *v_scale,
                           const int32_t *block_table, const int32_t *context_lens,

@@ -462,7 +462,7 @@ __device__ __forceinline__ void tile_store32(float *tile, const floatx16 (&acc)[
 // per-wave row max (base-2 units) and row sum.
 template <int D, int RG, int NT>
 __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles, int pitch,
-                                                      const float (*sm)[64], const float (*sl)[64],
+                                                      const float (*sm)[kMaxRows], const float (*sl)[kMaxRows],
                                                       int slot, int b, int g, int r0, int r1)
 {
     constexpr int OP = D + 4;
@@ -506,9 +506,11 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
 // their common ring and a workgroup barrier per page hands it to wave w+4.
 // One wave per SIMD leaves about half of such a page's time in stalls (the
 // matrix instructions alone issue at near their peak rate from one wave);
-// the second wave fills them.  Not used for bf16, which streams at the
-// memory's rate with 4 waves (shared pages measured slower there: 70B-layer
-// shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
+// the second wave fills them.  bf16 storage uses them only for more than
+// four row tiles (T*G > 64, e.g. 16-node trees at G = 8), where one wave
+// cannot hold every row tile's accumulators: with up to four row tiles it
+// streams at the memory's rate with 4 waves (shared pages measured slower
+// there: 70B-layer shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
 // each with every row tile and every 8th page streamed no faster for bf16
 // (c2: 29.8 vs 28.9 us) and slower for E4M3 (registers spill); 8 waves in
 // which w and w+4 each copy the same pages into their own rings doubled the
@@ -517,7 +519,7 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
 #define SV_SHARE_PAGES 1
 #endif
 template <int D, int RG, bool FP8>
-constexpr bool kSharePages = SV_SHARE_PAGES && FP8 && D == 128 && RG >= 3;
+constexpr bool kSharePages = (SV_SHARE_PAGES && FP8 && D == 128 && RG >= 3) || RG > 4;
 constexpr int kPageWaves = 4;      // waves that split a run's pages
 constexpr int kTilesPerPhase = 2;  // row tiles merged per epilogue phase
 
@@ -558,7 +560,16 @@ struct MfmaShape {
     static constexpr int RW = RING > PARK ? RING : PARK;
     static constexpr int RSTRIDE = SHARE ? RING : RW;
     static constexpr int PSTRIDE = SHARE ? PARK : RW;
-    static constexpr int SMEM = NWP * RSTRIDE > NW * PSTRIDE ? NWP * RSTRIDE : NW * PSTRIDE;
+    // Four row tiles per wave with shared pages (seven or eight row tiles in
+    // all): the bf16 Q operands of the workgroup's rows wait in LDS, behind
+    // the rings, instead of in registers (those would not fit beside four
+    // tiles' accumulators).  Tile t, chunk dc: 64 lanes x 16 bytes at
+    // QOFF + (t * NDC + dc) * 1024.
+    static constexpr bool QLDS = SHARE && RGW >= 4;
+    static constexpr int QOFF = NWP * RSTRIDE;
+    static constexpr int QBYTES = QLDS ? HV * RGW * PG::NDC * 1024 : 0;
+    static constexpr int LOOP_LDS = QOFF + QBYTES;
+    static constexpr int SMEM = LOOP_LDS > NW * PSTRIDE ? LOOP_LDS : NW * PSTRIDE;
 };
 
 // One run of pages of one (sequence b, KV head g) unit: pages blk_begin ..
@@ -569,8 +580,8 @@ struct MfmaShape {
 // -1 when the sequence has a single split.  Called by every thread of the
 // workgroup.
 template <int D, int RG, bool FP8>
-__device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char *smem, float (*s_m)[64],
-                                             float (*s_l)[64], int *s_pages, const int b, const int g,
+__device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char *smem, float (*s_m)[kMaxRows],
+                                             float (*s_l)[kMaxRows], int *s_pages, const int b, const int g,
                                              const int blk_begin, const int cap, const int slot, const bool fixed)
 {
     typedef MfmaShape<D, RG, FP8> SH;
@@ -642,7 +653,11 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 
     // Q tile as the B operand of S^T = K Q^T (row = l16, eight dims), bf16,
     // pre-scaled into base-2 units.
-    bf16x8 qf[RGW][NDC];
+    // (QLDS: the first page stream's waves store their row tiles' operands
+    // in LDS, which the prologue's barrier publishes to the other streams.)
+    constexpr bool QLDS = SH::QLDS;
+    bf16x8 qf[QLDS ? 1 : RGW][NDC];
+    unsigned char *const qlds = smem + SH::QOFF;
 #pragma unroll
     for (int rt = 0; rt < RGW; ++rt) {
 #pragma unroll
@@ -654,9 +669,21 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             u.y = f32x2_to_bf16x2(a.z * sc, a.w * sc);
             u.z = f32x2_to_bf16x2(c.x * sc, c.y * sc);
             u.w = f32x2_to_bf16x2(c.z * sc, c.w * sc);
-            qf[rt][dc] = __builtin_bit_cast(bf16x8, u);
+            if constexpr (QLDS) {
+                if (pw == 0)
+                    *reinterpret_cast<uint4 *>(qlds + (((rt_base + rt) * NDC + dc) * 64 + lane) * 16) = u;
+            } else {
+                qf[rt][dc] = __builtin_bit_cast(bf16x8, u);
+            }
         }
     }
+    // Q operand of row tile rt (of this wave) and chunk dc
+    auto qop = [&](int rt, int dc) -> bf16x8 {
+        if constexpr (QLDS)
+            return *reinterpret_cast<const bf16x8 *>(qlds + (((rt_base + rt) * NDC + dc) * 64 + lane) * 16);
+        else
+            return qf[rt][dc];
+    };
 
     // Running state per row tile: reference maximum m (base-2 units), the
     // row sums and the unnormalised outputs O^T (lane: dims NDT*(4*q4+i)+t of
@@ -822,8 +849,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 const bf16x8 k1 = __builtin_bit_cast(bf16x8, to_bf16x8(make_uint2(kraw[i].z, kraw[i].w)));
 #pragma unroll
                 for (int rt = 0; rt < RGW; ++rt) {
-                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[rt][2 * i], s[rt], 0, 0, 0);
-                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[rt][2 * i + 1], s[rt], 0, 0, 0);
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop(rt, 2 * i), s[rt], 0, 0, 0);
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop(rt, 2 * i + 1), s[rt], 0, 0, 0);
                 }
             }
         } else {
@@ -832,7 +859,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, kraw[dc]);
 #pragma unroll
                 for (int rt = 0; rt < RGW; ++rt)
-                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][dc], s[rt], 0, 0, 0);
+                    s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qop(rt, dc), s[rt], 0, 0, 0);
             }
         }
 
@@ -1017,10 +1044,12 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         else
             tile_store<D, RGW, TPH>(park, acc, l16, q4, rt0);
         __syncthreads();
-        // row half h: the tiles of waves h*NWP .. h*NWP + NWP-1
+        // row half h: the tiles of waves h*NWP .. h*NWP + NWP-1 (a phase
+        // never reaches past the half's own RGW tiles into the next half's)
 #pragma unroll
         for (int h = 0; h < SH::HV; ++h) {
-            const int r0 = (h * RGW + rt0) * 16, r1 = min(p.TG, (h * RGW + rt0 + TPH) * 16);
+            const int r0 = (h * RGW + rt0) * 16;
+            const int r1 = min(p.TG, (h * RGW + min(rt0 + TPH, RGW)) * 16);
             if (r0 < r1)
                 merge_waves_and_store<D, RGW, NWP>(p, reinterpret_cast<const float *>(smem + h * NWP * SH::PSTRIDE),
                                                    SH::PSTRIDE / 4, s_m + h * NWP, s_l + h * NWP, oslot, b, g, r0, r1);
@@ -1042,7 +1071,7 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_m
     constexpr int NW = SH::NW;
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::SMEM];
-    __shared__ float s_m[NW][64], s_l[NW][64];
+    __shared__ float s_m[NW][kMaxRows], s_l[NW][kMaxRows];
     __shared__ int s_pages[BAL ? kBalMaxShare : kMaxBps];  // the segment's page ids
 
     if constexpr (!BAL) {
@@ -1156,16 +1185,18 @@ __device__ __forceinline__ float load_kv(const void *base, size_t idx)
     }
 }
 
-template <int D, int KVT>
+// MAXR: the most query rows per unit (T*G) this instantiation serves (64 or
+// kMaxRows; the smaller one keeps its outputs in half the registers).
+template <int D, int KVT, int MAXR>
 __global__ __launch_bounds__(kAttnThreads) void sv_attn_valu_kernel(AttnParams p)
 {
     constexpr int OP = D + 4;
     constexpr int KP = D + 1;
-    constexpr int PER = (kMaxRows * D + kAttnThreads - 1) / kAttnThreads;
-    __shared__ __attribute__((aligned(16))) float s_q[kMaxRows * OP];  // later: obuf
-    __shared__ float s_k[kBlock * KP], s_v[kBlock * D], s_p[kMaxRows * (kBlock + 1)];
-    __shared__ float s_alpha[kMaxRows], s_mrow[64], s_lrow[64];
-    __shared__ uint32_t s_anc[kMaxRows];
+    constexpr int PER = (MAXR * D + kAttnThreads - 1) / kAttnThreads;
+    __shared__ __attribute__((aligned(16))) float s_q[MAXR * OP];  // later: obuf
+    __shared__ float s_k[kBlock * KP], s_v[kBlock * D], s_p[MAXR * (kBlock + 1)];
+    __shared__ float s_alpha[MAXR], s_mrow[MAXR], s_lrow[MAXR];
+    __shared__ uint32_t s_anc[MAXR];
 
     UnitWork w;
     if (!decode_work(p, w))
@@ -1287,18 +1318,28 @@ hipError_t launch_mfma_d(const AttnParams &p, hipStream_t s)
     case 1: return launch_mfma_rg<D, 1, FP8>(p, s);
     case 2: return launch_mfma_rg<D, 2, FP8>(p, s);
     case 3: return launch_mfma_rg<D, 3, FP8>(p, s);
-    default: return launch_mfma_rg<D, 4, FP8>(p, s);
+    case 4: return launch_mfma_rg<D, 4, FP8>(p, s);
+    case 5: return launch_mfma_rg<D, 5, FP8>(p, s);
+    case 6: return launch_mfma_rg<D, 6, FP8>(p, s);
+    case 7: return launch_mfma_rg<D, 7, FP8>(p, s);
+    default: return launch_mfma_rg<D, 8, FP8>(p, s);
+    }
+}
+
+template <int D, int MAXR>
+hipError_t launch_valu_dr(const AttnParams &p, int kv, hipStream_t s)
+{
+    switch (kv) {
+    case 0: return launch(sv_attn_valu_kernel<D, 0, MAXR>, p, s);
+    case 1: return launch(sv_attn_valu_kernel<D, 1, MAXR>, p, s);
+    default: return launch(sv_attn_valu_kernel<D, 2, MAXR>, p, s);
     }
 }
 
 template <int D>
 hipError_t launch_valu_d(const AttnParams &p, int kv, hipStream_t s)
 {
-    switch (kv) {
-    case 0: return launch(sv_attn_valu_kernel<D, 0>, p, s);
-    case 1: return launch(sv_attn_valu_kernel<D, 1>, p, s);
-    default: return launch(sv_attn_valu_kernel<D, 2>, p, s);
-    }
+    return p.TG <= 64 ? launch_valu_dr<D, 64>(p, kv, s) : launch_valu_dr<D, kMaxRows>(p, kv, s);
 }
 
 }  // namespace

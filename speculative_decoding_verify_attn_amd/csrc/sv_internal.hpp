@@ -9,7 +9,7 @@
 namespace sv {
 
 constexpr int kBlock = 16;          // tokens per KV page
-constexpr int kMaxRows = 64;        // T * (Hq/Hkv) per (sequence, kv head) unit
+constexpr int kMaxRows = 128;       // T * (Hq/Hkv) per (sequence, kv head) unit
 constexpr int kMaxSplits = 128;     // context splits per unit
 constexpr int kMaxBps = 512;        // context pages per split
 constexpr int kAttnThreads = 256;   // 4 waves per workgroup

@@ -63,7 +63,7 @@ def _attn(**kw):
     (dict(B=0), 2),
     (dict(T=17), 2),
     (dict(Hq=30), 2),
-    (dict(Hq=128, Hkv=8), 3),     # T*G = 80 > 64
+    (dict(Hq=256, Hkv=8), 3),     # T*G = 160 > 128
     (dict(d=96), 3),
     (dict(bs=32), 3),
     (dict(kv=7), 3),

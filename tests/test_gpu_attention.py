@@ -31,6 +31,18 @@ SMALL = [
     (13, 2, 16, 16, 4, 64, [500, 260], "fp8"),          # E4M3, d=64, T*G = 64
     (14, 2, 5, 64, 8, 128, [2100, 47], "fp8"),          # E4M3, T*G = 40: the second half's last tile is padding
     (15, 2, 4, 64, 8, 128, [613, 4], "fp8"),            # E4M3, T*G = 32: two row tiles, one wave per page
+    # more than 64 rows per KV head (more than four row tiles): two waves per
+    # page, each owning half the row tiles; with four tiles per wave the Q
+    # operands wait in LDS
+    (16, 2, 9, 64, 8, 128, [600, 40], "bf16"),          # T*G = 72: five row tiles
+    (17, 2, 16, 64, 8, 128, [700, 30], "bf16"),         # T*G = 128: eight row tiles, Q in LDS
+    (18, 3, 12, 64, 8, 128, [900, 12, 301], "bf16"),    # T*G = 96: six row tiles
+    (19, 2, 14, 64, 8, 128, [513, 77], "fp8"),          # E4M3, T*G = 112: seven tiles (32x32 PV, Q in LDS)
+    (20, 2, 16, 32, 4, 64, [400, 16], "bf16"),          # d=64, T*G = 128
+    (21, 2, 10, 64, 8, 128, [1300, 90], "fp8"),         # E4M3, T*G = 80: five tiles (16x16 PV)
+    (22, 2, 16, 64, 8, 128, [800, 100], "fp8"),         # E4M3, T*G = 128
+    (23, 2, 11, 32, 4, 64, [333, 11], "fp8"),           # E4M3, d=64, T*G = 88
+    (24, 2, 13, 64, 8, 128, [250, 140], "f32"),         # fp32 (vector ALU), T*G = 104
 ]
 
 
@@ -162,6 +174,37 @@ def _random_shapes(n, seed):
 
 
 RANDOM = _random_shapes(24, 2024)
+
+
+def _random_wide_shapes(n, seed):
+    """As _random_shapes, with 64 < T*G <= 128 (five to eight row tiles)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([8, 16]))
+        T = int(rng.integers(1, 17))
+        if not 64 < T * G <= 128:
+            continue
+        B = int(rng.integers(1, 5))
+        kv = str(rng.choice(["f32", "bf16", "fp8"]))
+        lens = [int(rng.integers(T, 900)) for _ in range(B)]
+        bps = int(rng.choice([0, 4, 8, 32, -1])) if kv != "f32" else int(rng.choice([0, 8]))
+        out.append((len(out), B, T, Hkv * G, Hkv, d, lens, kv, bps))
+    return out
+
+
+RANDOM_WIDE = _random_wide_shapes(12, 2026)
+
+
+@pytest.mark.parametrize("case", RANDOM_WIDE, ids=[str(c[0]) for c in RANDOM_WIDE])
+def test_random_wide_shapes(case):
+    i, B, T, Hq, Hkv, d, lens, kv, bps = case
+    a = W.make_attn_from_lens(900 + i, B, T, Hq, Hkv, d, lens, kv=kv, extra_blocks=2)
+    out = run_attn(a, blocks_per_split=bps)
+    err = _check(a, out)
+    assert err <= TOL[a.kv_dtype], (case, err)
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=[str(c[0]) for c in RANDOM])

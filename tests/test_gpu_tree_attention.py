@@ -85,6 +85,22 @@ def test_random_tree_per_sequence_and_splits(kv):
         assert err <= TOL[a.kv_dtype]
 
 
+@pytest.mark.parametrize("shape,kv", [("wide5x2", "bf16"), ("binary3", "bf16"), ("top3-2-1", "fp8")])
+def test_tree_at_70b_geometry(shape, kv):
+    """Sixteen-node trees at the 70B layer's GQA ratio (Hq=64, Hkv=8: up to
+    128 rows per KV head), ragged contexts, the planner's split and balanced
+    shares."""
+    par = W.tree_parents(W.TREE_SHAPES[shape])
+    N = par.shape[0]
+    B = 3
+    a = W.make_attn_from_lens(11, B, N, 64, 8, 128, [N, 900, 5000], kv=kv, extra_blocks=2)
+    masks = oracle.tree_masks(np.broadcast_to(par, (B, N)))
+    for bps in (0, -1):
+        err = _err(a, _run_tree(a, masks, bps=bps), masks)
+        print("%s %s bps %d: max row rel err %.3e" % (shape, kv, bps, err))
+        assert err <= TOL[a.kv_dtype]
+
+
 def test_chain_sets_equal_the_chain_call():
     B, T = 3, 6
     a = W.make_attn_from_lens(9, B, T, 32, 8, 128, [6, 250, 1200], kv="bf16")

@@ -98,20 +98,28 @@ static_assert(sizeof(RowCut) == kRowCutBytes, "workspace slot of RowCut");
 struct Temp {
     bool greedy;
     double inv;    // 1 / T in fp64
+    double l2inv;  // log2(e) / T in fp64
     float c_hi;    // log2(e) / T split into two floats for the exponent
     float c_lo;
 };
 
-__device__ __forceinline__ Temp temp_of(const SampleParams &p, int b)
+// The temperature's constants from 1 / T (greedy: T <= 0 or NaN).
+__device__ __forceinline__ Temp temp_from_inv(bool greedy, double inv)
 {
     Temp t;
-    const float T = p.temperature ? p.temperature[b] : 1.0f;
-    t.greedy = !(T > 0.0f);
-    t.inv = t.greedy ? 1.0 : 1.0 / (double)T;
-    const double c = 1.4426950408889634074 * t.inv;
-    t.c_hi = (float)c;
-    t.c_lo = (float)(c - (double)t.c_hi);
+    t.greedy = greedy;
+    t.inv = inv;
+    t.l2inv = 1.4426950408889634074 * inv;
+    t.c_hi = (float)t.l2inv;
+    t.c_lo = (float)(t.l2inv - (double)t.c_hi);
     return t;
+}
+
+__device__ __forceinline__ Temp temp_of(const SampleParams &p, int b)
+{
+    const float T = p.temperature ? p.temperature[b] : 1.0f;
+    const bool greedy = !(T > 0.0f);
+    return temp_from_inv(greedy, greedy ? 1.0 : 1.0 / (double)T);
 }
 
 // Loads this thread's 32 entries of a chunk: entries tid*4 + k*1024 .. +3
@@ -263,10 +271,14 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(Samp
 }
 
 // Target probability p~_j of entry j from its logit, the row maximum M, 1/Z
-// and the temperature, to about one fp32 ulp: the argument (l - M) / T is
-// formed in fp64 and split into a float hi and the remainder lo; exp(hi)
-// comes from the accurate fp32 exp and exp(lo) = 1 + lo to second order
-// (|lo| <= ulp(hi)/2); products in fp64.  Greedy rows are one-hot at `arg`.
+// and the temperature, to about one fp32 ulp: the base-2 argument
+// t = (l - M) log2(e) / T is formed in fp64 (l - M is exact there) and split
+// into a float hi and the remainder lo; 2^hi comes from the hardware exp2
+// (v_exp_f32, about 1 ulp) and 2^lo = 1 + lo ln 2 to second order
+// (|lo| <= ulp(hi)/2); products in fp64.  (The hardware exp2 replaced the
+// library expf of the natural-base split: the same accuracy, a third of the
+// vector instructions per entry, which the decide pass is bound by at large
+// batches.)  Greedy rows are one-hot at `arg`.
 __device__ __forceinline__ double target_prob_fast(float l, int j, float M, double invZ, const Temp &tp, int arg,
                                                    float tau)
 {
@@ -274,12 +286,12 @@ __device__ __forceinline__ double target_prob_fast(float l, int j, float M, doub
         return j == arg ? 1.0 : 0.0;
     if (!(l >= tau))
         return 0.0;  // outside the top-p set
-    const double a = ((double)l - (double)M) * tp.inv;
-    if (!(a > -104.0))
+    const double t = ((double)l - (double)M) * tp.l2inv;
+    if (!(t > -150.0))
         return 0.0;  // underflows in fp32 (and catches l = -inf)
-    const float hi = (float)a;
-    const double lo = a - (double)hi;
-    return (double)expf(hi) * (1.0 + lo) * invZ;
+    const float hi = (float)t;
+    const double lo = t - (double)hi;
+    return (double)__builtin_amdgcn_exp2f(hi) * __builtin_fma(lo, 0.69314718055994530942, 1.0) * invZ;
 }
 
 // Same quantity in fp64 throughout (used for the K acceptance tests).
@@ -1047,10 +1059,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_pick_kernel(SamplePa
     const bool residual = ss.coef > 0.0;
     const float M = ss.m;
     const double invZ = ss.inv_z;
-    Temp tp;
-    tp.greedy = ss.greedy != 0;
-    tp.inv = ss.inv_t;
-    tp.c_hi = tp.c_lo = 0.0f;  // (row sums are not recomputed here)
+    const Temp tp = temp_from_inv(ss.greedy != 0, ss.inv_t);
     const float *lrow = p.logits + ((size_t)b * K1 + ss.row) * V;
     const float *qrow = p.probs ? p.probs + ((size_t)b * p.qrows + ss.qrow) * V : nullptr;
 
@@ -1388,7 +1397,7 @@ __global__ __launch_bounds__(kSampleThreads * 4) void sv_tree_level_kernel(Sampl
         return;  // uniform over the workgroup
     const int base = chunk * kSampleChunk + wave * kLevelSlice;
     const int n = min(kLevelSlice, p.V - base);
-    const Temp t1{false, 1.0, 0.0f, 0.0f};
+    const Temp t1 = temp_from_inv(false, 1.0);
     const bool fast = p.nchunk <= kWave;  // one chunk statistic per lane
     const bool hp = rank > 2;             // the previous sibling has its own test (rank >= 2)
     // Child j's loads, all requested together; the next child's are in
@@ -1485,7 +1494,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
     const int sub = sub0;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const Temp t1{false, 1.0, 0.0f, 0.0f};
+    const Temp t1 = temp_from_inv(false, 1.0);
     const float ninf = -__builtin_inff();
 
     // 1. Everything the walk reads, requested together: each node's token,

@@ -309,15 +309,20 @@ __device__ __forceinline__ int4v page_desc(const unsigned char *base, int page, 
 // Issued from inline assembly so that the kernel, not the compiler, decides
 // how many copies stay in flight; completion is awaited with wait_dma<N>().
 // lgkmcnt(0) first: the copy may overwrite LDS that this wave has only just
-// finished reading.
+// finished reading.  s_nop 4: a vector-memory instruction that reads an SGPR
+// written by a VALU instruction (v_readlane of a spilled SGPR, readfirstlane)
+// needs five wait states in between, and the compiler's hazard check does not
+// look inside inline assembly; without them the copy can take the SGPR's
+// previous value as its offset or descriptor (seen: a spilled soffset reloaded
+// one instruction before the copy, which then fetched the wrong key).
 template <int BYTES>
 __device__ __forceinline__ void dma_to_lds(uint32_t lds, int4v desc, int voff, int soff)
 {
     if constexpr (BYTES == 16)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                      :: "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds) : "memory");
     else
-        asm volatile("s_waitcnt lgkmcnt(0)\n\tbuffer_load_dword %0, %1, %2 offen lds"
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
                      :: "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds) : "memory");
 }
 

@@ -134,6 +134,56 @@ def test_physical_placement_is_invisible():
     assert torch.equal(o1, o2)
 
 
+def test_split_calls_back_to_back():
+    """One workspace, filled with garbage first, serves calls with different
+    split counts (and hence different partial-slot layouts) back to back,
+    with and without waiting in between; every call must match the oracle and
+    repeat bit for bit."""
+    cases = [(41, [2000, 33, 700, 1024], 16), (42, [1500, 1499, 17], 24), (43, [900, 6, 300, 880], 8),
+             (44, [4096] * 3, 0)]
+    ins = [W.make_attn_from_lens(seed, len(lens), 6, 32, 8, 128, lens, kv="bf16") for seed, lens, _ in cases]
+    ts = [upload_attn(a) for a in ins]
+    need = max(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, bps) for a, (_, _, bps) in zip(ins, cases))
+    ws = sv.alloc_workspace(need, ts[0]["q"].device)
+    ws.fill_(0xAB)
+    outs = []
+    for rep in range(2):
+        cur = []
+        for a, t, (_, _, bps) in zip(ins, ts, cases):
+            out = torch.full((a.B, a.T, a.Hq, a.d), float("nan"), dtype=torch.float32, device=t["q"].device)
+            sv.spec_verify_attn(t["q"], t["k"], t["v"], t["table"], t["lens"], out, ws, kv_dtype=a.kv_dtype,
+                                blocks_per_split=bps)
+            cur.append(out)
+            if rep == 1:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        outs.append(cur)
+    for a, o0, o1 in zip(ins, outs[0], outs[1]):
+        assert _check(a, o0) <= TOL[a.kv_dtype]
+        assert torch.equal(o0, o1)
+
+
+# Every wide row count (five to eight row tiles per KV head: shared pages,
+# Q operands in LDS at seven and eight) for both head sizes and both
+# low-precision storages, under balanced shares, a forced fixed split and the
+# planner's choice.  Regression: under register pressure the compiler
+# reloaded a spilled copy offset into an SGPR one instruction before the
+# inline-assembly LDS copy that reads it, which needs five wait states in
+# between; the copy then fetched the wrong key's V bytes (all rows wrong at
+# d = 64 with eight tiles and at d = 128 E4M3 with five and six).
+WIDE = [(kv, d, T) for kv in ("bf16", "fp8") for d in (64, 128) for T in (10, 12, 14, 16)]
+
+
+@pytest.mark.parametrize("kv,d,T", WIDE, ids=["%s-d%d-T%d" % c for c in WIDE])
+def test_wide_rows_every_split_mode(kv, d, T):
+    Hq, Hkv = (32, 4) if d == 64 else (64, 8)
+    a = W.make_attn_from_lens(20, 2, T, Hq, Hkv, d, [400, 16], kv=kv, extra_blocks=2)
+    t = upload_attn(a)
+    for bps in (-1, 4, 0):
+        out = run_attn(a, t, blocks_per_split=bps)
+        assert _check(a, out) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
+
+
 # Full-size configurations in the launch configuration bench.py times (the
 # planner's split).  c1, c2, c5a and c5b: every output row.  c3 and c4 (whose
 # balanced shares cut units at arbitrary pages): at least one row of every

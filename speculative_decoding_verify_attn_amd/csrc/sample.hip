@@ -43,6 +43,8 @@
 // an order-preserving 32-bit key of the logit finds the cut exactly.  The
 // output per row is the cut logit tau (every l >= tau is kept) and
 // 1 / kept mass.
+#include <atomic>
+
 #include "sv_device.hpp"
 #include "sv_internal.hpp"
 
@@ -799,6 +801,65 @@ __device__ __forceinline__ void load_sub(const float *row, int n, float fill, fl
     }
 }
 
+// Chosen-row weights and plain target mass of sub-chunks sub0 .. sub0+nsh-1
+// of one sequence, into s_part[j][wave][0 / 1] (each sub-chunk summed in its
+// own fixed order).  The weight of entry j is max(0, p~_j - coef * q_j)
+// (the draft row is read only when coef > 0), else p~_j.  The loads run one
+// sub-chunk ahead of the sums, so a workgroup that covers several sub-chunks
+// keeps two in flight while holding registers for two.
+template <bool VEC>
+__device__ __forceinline__ void sub_chunk_masses(const float *lrow, const float *qrow, double coef, int sub0,
+                                                 int nsh, int V, float M, double invZ, const Temp &tp, int arg,
+                                                 float tau, double (*s_part)[kNWs][2])
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    auto load = [&](int j, float (&lv)[4], float (&qv)[4]) {
+        const int base = (sub0 + j) * kSampleSub;
+        const int cnt = min(kSampleSub, V - base);
+        load_sub<VEC>(lrow + base, cnt, -__builtin_inff(), lv);
+        if (coef > 0.0) {
+            load_sub<VEC>(qrow + base, cnt, 0.0f, qv);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qv[k] = 0.0f;
+        }
+    };
+    auto mass = [&](int j, const float (&lv)[4], const float (&qv)[4]) {
+        const int base = (sub0 + j) * kSampleSub;
+        double sw = 0.0, sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double pj = target_prob_fast(lv[k], base + tid * 4 + k, M, invZ, tp, arg, tau);
+            sp += pj;
+            if (coef > 0.0) {
+                const double r = pj - coef * (double)qv[k];
+                sw += r > 0.0 ? r : 0.0;
+            } else {
+                sw += pj;
+            }
+        }
+        sw = wave_sum_f64(sw);
+        sp = wave_sum_f64(sp);
+        if (lane == 0) {
+            s_part[j][wave][0] = sw;
+            s_part[j][wave][1] = sp;
+        }
+    };
+    float la[4], qa[4], lb[4], qb[4];
+    load(0, la, qa);
+    for (int j = 0; j < nsh; j += 2) {  // nsh >= 1, uniform
+        if (j + 1 < nsh)
+            load(j + 1, lb, qb);
+        mass(j, la, qa);
+        if (j + 1 >= nsh)
+            break;
+        if (j + 2 < nsh)
+            load(j + 2, la, qa);
+        mass(j + 1, lb, qb);
+    }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
 {
@@ -963,45 +1024,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     const float tau = s_tau[n];
 
     // 3. Mass of each sub-chunk: residual (or bonus) weights and plain
-    //    target mass (every sub-chunk's entries requested at once).
-    float lv[kDecideMaxSpw][4], qv[kDecideMaxSpw][4];
-#pragma unroll
-    for (int j = 0; j < kDecideMaxSpw; ++j) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qv[j][k] = 0.0f;
-        if (j < nsh) {  // uniform
-            const int base = (sub0 + j) * kSampleSub;
-            const int cnt = min(kSampleSub, V - base);
-            load_sub<VEC>(p.logits + ((size_t)b * K1 + n) * V + base, cnt, -__builtin_inff(), lv[j]);
-            if (residual)
-                load_sub<VEC>(p.probs + ((size_t)b * K + n) * V + base, cnt, 0.0f, qv[j]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kDecideMaxSpw; ++j) {
-        if (j >= nsh)
-            break;  // uniform
-        const int base = (sub0 + j) * kSampleSub;
-        double sw = 0.0, sp = 0.0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double pj = target_prob_fast(lv[j][k], base + tid * 4 + k, M, invZ, tp, arg, tau);
-            sp += pj;
-            if (residual) {
-                const double r = pj - (double)qv[j][k];
-                sw += r > 0.0 ? r : 0.0;
-            } else {
-                sw += pj;
-            }
-        }
-        sw = wave_sum_f64(sw);
-        sp = wave_sum_f64(sp);
-        if (lane == 0) {
-            s_part[j][wave][0] = sw;
-            s_part[j][wave][1] = sp;
-        }
-    }
+    //    target mass.
+    sub_chunk_masses<VEC>(p.logits + ((size_t)b * K1 + n) * V, p.probs + ((size_t)b * K + n) * V,
+                          residual ? 1.0 : 0.0, sub0, nsh, V, M, invZ, tp, arg, tau, s_part);
     __syncthreads();
     if (tid < 2 * nsh) {
         const int j = tid >> 1, c = tid & 1;
@@ -1612,46 +1637,9 @@ __global__ __launch_bounds__(kSampleThreads) void sv_tree_decide_kernel(SamplePa
     const float M = s_M[t];
     const double invZ = s_iZ[t];
 
-    // 3. Mass of each sub-chunk: final weights and plain target mass (every
-    //    sub-chunk's entries requested at once).
-    float lv[kDecideMaxSpw][4], qv[kDecideMaxSpw][4];
-#pragma unroll
-    for (int j = 0; j < kDecideMaxSpw; ++j) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qv[j][k] = 0.0f;
-        if (j < nsh) {  // uniform
-            const int base = (sub0 + j) * kSampleSub;
-            const int cnt = min(kSampleSub, V - base);
-            load_sub<VEC>(p.logits + ((size_t)b * N + t) * V + base, cnt, ninf, lv[j]);
-            if (coef > 0.0)
-                load_sub<VEC>(p.probs + ((size_t)b * N + t) * V + base, cnt, 0.0f, qv[j]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kDecideMaxSpw; ++j) {
-        if (j >= nsh)
-            break;  // uniform
-        const int base = (sub0 + j) * kSampleSub;
-        double sw = 0.0, sp = 0.0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const double pj = target_prob_fast(lv[j][k], base + tid * 4 + k, M, invZ, t1, 0, ninf);
-            sp += pj;
-            if (coef > 0.0) {
-                const double r = pj - coef * (double)qv[j][k];
-                sw += r > 0.0 ? r : 0.0;
-            } else {
-                sw += pj;
-            }
-        }
-        sw = wave_sum_f64(sw);
-        sp = wave_sum_f64(sp);
-        if (lane == 0) {
-            s_part[j][wave][0] = sw;
-            s_part[j][wave][1] = sp;
-        }
-    }
+    // 3. Mass of each sub-chunk: final weights and plain target mass.
+    sub_chunk_masses<VEC>(p.logits + ((size_t)b * N + t) * V, p.probs + ((size_t)b * N + t) * V, coef, sub0, nsh,
+                          V, M, invZ, t1, 0, ninf, s_part);
     __syncthreads();
     if (tid < 2 * nsh) {
         const int j = tid >> 1, c = tid & 1;
@@ -1707,18 +1695,57 @@ __global__ void sv_fill_zero_kernel(uint4 *p, size_t n16, unsigned char *tail, s
             tail[i] = 0;
 }
 
+// Workgroups of one decide kernel that the device holds at once: compute
+// units times the kernel's resident workgroups per unit, queried on first use
+// per device and kernel (slot `which`) and kept.  0 if the query fails.
+constexpr int kSpwMaxDevices = 64;
+std::atomic<int> g_resident[kSpwMaxDevices][4];
+
+long long resident_workgroups(const void *kernel, int which, hipStream_t stream)
+{
+    int dev = 0;
+    if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+        dev >= kSpwMaxDevices)
+        return 0;
+    int r = g_resident[dev][which].load(std::memory_order_relaxed);
+    if (r == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kSampleThreads, 0) != hipSuccess ||
+            cus <= 0 || per <= 0)
+            return 0;
+        r = cus * per;
+        g_resident[dev][which].store(r, std::memory_order_relaxed);
+    }
+    return r;
+}
+
+// Sub-chunks per decide workgroup for `total` (sequence, sub-chunk) pairs:
+// the fewest that keep the grid within one resident round (2048 workgroups
+// assumed if the occupancy query fails), at most kDecideMaxSpw.
+int decide_spw(long long total, const void *kernel, int which, hipStream_t stream)
+{
+    long long slots = resident_workgroups(kernel, which, stream);
+    if (slots <= 0)
+        slots = 2048;
+    const long long want = (total + slots - 1) / slots;
+    return (int)(want < 1 ? 1 : (want > kDecideMaxSpw ? kDecideMaxSpw : want));
+}
+
 }  // namespace
 
 hipError_t launch_sample(const SampleParams &p0, hipStream_t stream)
 {
     // Decide: one workgroup per sub-chunk while the grid fits in one round of
-    // resident workgroups (about 2048); larger batches give each workgroup up
-    // to kDecideMaxSpw consecutive sub-chunks, so the statistics merge and the
-    // tests (two dependent round trips) are not repeated per sub-chunk.
+    // resident workgroups; larger batches give each workgroup consecutive
+    // sub-chunks (up to kDecideMaxSpw), so that the statistics merge and the
+    // tests (two dependent round trips) run once per workgroup and the whole
+    // grid stays resident.
     SampleParams p = p0;
     const long long nsub = (p.V + kSampleSub - 1) / kSampleSub;
-    const long long want = (nsub * p.B + 2047) / 2048;
-    p.spw = (int)(want < 1 ? 1 : (want > kDecideMaxSpw ? kDecideMaxSpw : want));
+    p.spw = decide_spw(nsub * p.B, p.vec4 ? (const void *)sv_sample_decide_kernel<true>
+                                          : (const void *)sv_sample_decide_kernel<false>,
+                       p.vec4 ? 0 : 1, stream);
     const dim3 block(kSampleThreads);
     const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
     const dim3 g2((unsigned)(((nsub + p.spw - 1) / p.spw) * p.B));
@@ -1749,8 +1776,9 @@ hipError_t launch_sample_tree(const SampleParams &p0, hipStream_t stream)
 {
     SampleParams p = p0;  // decide workgroups per sequence: as in launch_sample
     const long long nsub = (p.V + kSampleSub - 1) / kSampleSub;
-    const long long want = (nsub * p.B + 2047) / 2048;
-    p.spw = (int)(want < 1 ? 1 : (want > kDecideMaxSpw ? kDecideMaxSpw : want));
+    p.spw = decide_spw(nsub * p.B, p.vec4 ? (const void *)sv_tree_decide_kernel<true>
+                                          : (const void *)sv_tree_decide_kernel<false>,
+                       p.vec4 ? 2 : 3, stream);
     const dim3 block(kSampleThreads);
     const int N = p.K + 1;
     const dim3 g1((unsigned)(p.nchunk * p.B * N));

@@ -80,7 +80,7 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream);
 constexpr int kSampleChunk = 8192;  // vocabulary entries per sampler workgroup
 constexpr int kSampleSub = 1024;    // entries per sub-chunk (unit of the draw's rescan)
 constexpr int kSampleThreads = 256;
-constexpr int kDecideMaxSpw = 4;     // sub-chunks one decide workgroup covers at most
+constexpr int kDecideMaxSpw = 16;    // sub-chunks one decide workgroup covers at most
 constexpr int kMaxSampleChunks = 2048;  // V <= 2048 * 8192
 
 struct SampleParams {

@@ -61,9 +61,12 @@ __device__ __forceinline__ int clamp_len(const AttnParams &p, int Lraw)
 // dies round robin with the block index.  (Giving each die the units of its
 // own KV heads measured 9% slower on a ragged batch, 3% faster on one long
 // sequence.)
-__device__ __forceinline__ int bal_share(int total)
+// one_per_cu: the kernel's 8-wave workgroups fill a compute unit each.
+__device__ __forceinline__ int bal_share(int total, bool one_per_cu)
 {
     const int s1 = (total + kBalTargetWgs - 1) / kBalTargetWgs;
+    if (one_per_cu)
+        return s1 < 4 ? 4 : (s1 > kBalMaxShareOne ? kBalMaxShareOne : s1);
     if (s1 <= kBalOneShare)
         return s1 < 4 ? 4 : s1;
     const int s2 = (total + 2 * kBalTargetWgs - 1) / (2 * kBalTargetWgs);
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
     int Lraw = 0;
     if (p.balanced) {
         const int nblk = (clamp_len(p, p.context_lens[b]) + kBlock - 1) / kBlock;
-        const int S = bal_share(p.Hkv * p.bal_prefix[p.B]);
+        const int S = bal_share(p.Hkv * p.bal_prefix[p.B], p.bal_one != 0);
         const int start = p.Hkv * p.bal_prefix[b] + g * nblk;
         ns = nblk > 0 ? (start + nblk - 1) / S - start / S + 1 : 0;
         if (ns <= 1)
@@ -517,24 +520,25 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
 // streams at the memory's rate with 4 waves (shared pages measured slower
 // there: 70B-layer shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
 // each with every row tile and every 8th page streamed no faster for bf16
-// (c2: 29.8 vs 28.9 us) and slower for E4M3 (registers spill); 8 waves in
-// which w and w+4 each copy the same pages into their own rings doubled the
-// memory traffic.
-#ifndef SV_SHARE_PAGES
-#define SV_SHARE_PAGES 1
-#endif
-template <int D, int RG, bool FP8>
-constexpr bool kSharePages = (SV_SHARE_PAGES && FP8 && D == 128 && RG >= 3) || RG > 4;
-constexpr int kPageWaves = 4;      // waves that split a run's pages
+// with fixed splits (8B-layer shape: 29.1 vs 28.3 us) and slower for E4M3
+// (registers spill); they are used for balanced shares with at most two row
+// tiles (ragged 64-sequence batch 430 -> 419 us: see attn_page_streams);
+// handing pages out from an LDS counter instead of every 8th page measured
+// the same there (and gives up run-to-run bit equality); 8 waves in which w
+// and w+4 each copy the same pages into their own rings doubled the memory
+// traffic.
 constexpr int kTilesPerPhase = 2;  // row tiles merged per epilogue phase
 
-template <int D, int RG, bool FP8>
+template <int D, int RG, bool FP8, bool BAL>
 struct MfmaShape {
     typedef PageGeom<D, FP8> PG;
-    static constexpr bool SHARE = kSharePages<D, RG, FP8>;
-    static constexpr int HV = SHARE ? 2 : 1;          // waves per page stream
-    static constexpr int NWP = kPageWaves;            // page streams
+    static constexpr bool SHARE = attn_share_pages(D, RG, FP8);
+    static constexpr int HV = SHARE ? 2 : 1;                      // waves per page stream
+    static constexpr int NWP = attn_page_streams(D, RG, FP8, BAL);  // page streams
     static constexpr int NW = NWP * HV;               // waves per workgroup
+    static_assert(NW == attn_waves(D, RG, FP8, BAL), "workgroup shape");
+    // page ids a balanced share holds (one share per compute unit for 8 waves)
+    static constexpr int PCAP_BAL = NW == 8 ? kBalMaxShareOne : kBalMaxShare;
     static constexpr int RGW = (RG + HV - 1) / HV;    // row tiles per wave
     // E4M3, d = 128, an even number of row tiles per wave: PV runs on the
     // 32x32x16 matrix instruction (see mfma_segment).
@@ -584,12 +588,12 @@ struct MfmaShape {
 // splits (fixed = true) the slot given is that of (unit, split), replaced by
 // -1 when the sequence has a single split.  Called by every thread of the
 // workgroup.
-template <int D, int RG, bool FP8>
+template <int D, int RG, bool FP8, bool BAL>
 __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char *smem, float (*s_m)[kMaxRows],
                                              float (*s_l)[kMaxRows], int *s_pages, const int b, const int g,
                                              const int blk_begin, const int cap, const int slot, const bool fixed)
 {
-    typedef MfmaShape<D, RG, FP8> SH;
+    typedef MfmaShape<D, RG, FP8, BAL> SH;
     typedef typename SH::PG PG;
     constexpr int NW = SH::NW;
     constexpr int NT = 64 * NW;          // threads
@@ -627,8 +631,22 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         const int i = pw + k * NWP;
         first[k] = i < avail ? trow[i] : 0;
     }
-    for (int i = tid; i < avail; i += NT)
-        s_pages[i] = clamp_block(trow[i], p.num_blocks);
+    // (all of the run's table entries are requested before any is stored:
+    // a load-store loop would wait one round trip per NT entries, which
+    // under full streaming load took ~10 us per run of 528 pages)
+    constexpr int kPer = ((BAL ? SH::PCAP_BAL : kMaxBps) + NT - 1) / NT;
+    int tv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * NT;
+        tv[j] = i < avail ? trow[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * NT;
+        if (i < avail)
+            s_pages[i] = clamp_block(tv[j], p.num_blocks);
+    }
     float4 qraw[RGW][NDC][2];
     uint32_t anc[RGW];  // ancestor set of the lane's verify row (padding rows see everything)
 #pragma unroll
@@ -1070,14 +1088,14 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 // meets.  The merge kernel finds a cut unit's partials from the same prefix
 // sums, which workgroup 0 leaves in the workspace.
 template <int D, int RG, bool FP8, bool BAL>
-__global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8, BAL>::NW), 1) void sv_attn_mfma_kernel(AttnParams p)
 {
-    typedef MfmaShape<D, RG, FP8> SH;
+    typedef MfmaShape<D, RG, FP8, BAL> SH;
     constexpr int NW = SH::NW;
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::SMEM];
     __shared__ float s_m[NW][kMaxRows], s_l[NW][kMaxRows];
-    __shared__ int s_pages[BAL ? kBalMaxShare : kMaxBps];  // the segment's page ids
+    __shared__ int s_pages[BAL ? SH::PCAP_BAL : kMaxBps];  // the segment's page ids
 
     if constexpr (!BAL) {
         int unit, split;
@@ -1085,7 +1103,7 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_m
         if (unit >= p.B * p.Hkv)
             return;
         const int b = unit / p.Hkv;
-        mfma_segment<D, RG, FP8>(p, smem, s_m, s_l, s_pages, b, unit - b * p.Hkv, split * p.bps, p.bps,
+        mfma_segment<D, RG, FP8, BAL>(p, smem, s_m, s_l, s_pages, b, unit - b * p.Hkv, split * p.bps, p.bps,
                                  unit * p.max_splits + split, true);
         return;
     }
@@ -1130,7 +1148,7 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_m
             for (int i = tid; i <= p.B; i += NT)
                 p.bal_prefix[i] = s_P[i];
         total = p.Hkv * s_P[p.B];
-        const int S = bal_share(total);
+        const int S = bal_share(total, SH::NW == 8);
         pos = (int)blockIdx.x * S;
         if (pos >= total)
             return;
@@ -1165,7 +1183,7 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8>::NW), 1) void sv_attn_m
             slot = __builtin_amdgcn_readfirstlane((off == 0 && send == uend) ? -1
                                                                               : sb * p.Hkv + gg + (int)blockIdx.x);
         }
-        mfma_segment<D, RG, FP8>(p, smem, s_m, s_l, s_pages, b, g, blk_begin, cap, slot, false);
+        mfma_segment<D, RG, FP8, BAL>(p, smem, s_m, s_l, s_pages, b, g, blk_begin, cap, slot, false);
         pos += cap;
         if (pos >= end)
             return;
@@ -1310,8 +1328,12 @@ hipError_t launch(Kernel k, const AttnParams &p, hipStream_t stream)
 template <int D, int RG, bool FP8>
 hipError_t launch_mfma_rg(const AttnParams &p, hipStream_t s)
 {
-    auto kern = p.balanced ? sv_attn_mfma_kernel<D, RG, FP8, true> : sv_attn_mfma_kernel<D, RG, FP8, false>;
-    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * MfmaShape<D, RG, FP8>::NW), 0, s, p);
+    if (p.balanced)
+        hipLaunchKernelGGL((sv_attn_mfma_kernel<D, RG, FP8, true>), dim3(p.grid),
+                           dim3(64 * MfmaShape<D, RG, FP8, true>::NW), 0, s, p);
+    else
+        hipLaunchKernelGGL((sv_attn_mfma_kernel<D, RG, FP8, false>), dim3(p.grid),
+                           dim3(64 * MfmaShape<D, RG, FP8, false>::NW), 0, s, p);
     return hipGetLastError();
 }
 

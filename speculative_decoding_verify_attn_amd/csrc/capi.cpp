@@ -353,6 +353,8 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.tree_mask = tree_mask;
     p.out = out;
     p.balanced = (pl.balanced && use_mfma) ? 1 : 0;
+    // the share rule follows the kernel's workgroup shape (8 waves: one share per compute unit)
+    p.bal_one = (p.balanced && sv::attn_waves(d, (T * (Hq / Hkv) + 15) / 16, fp8, true) == 8) ? 1 : 0;
     p.part_o = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_o : pl.off_part_o));
     p.part_ml = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_ml : pl.off_part_ml));
     p.bal_prefix = p.balanced ? reinterpret_cast<int *>(ws + pl.off_prefix) : nullptr;
@@ -368,8 +370,15 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.bps = pl.bps;
     p.max_splits = pl.max_splits;
     // fixed splits: 8 * ceil(units / 8) * max_splits workgroups (see
-    // work_item in attn.hip); balanced shares: the plan's grid
-    const long long wgs = p.balanced ? (long long)pl.grid_bal : ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits;
+    // work_item in attn.hip); balanced shares: the most shares the rule can
+    // make from at most units * max_blocks pairs (one per compute unit:
+    // shares of up to kBalMaxShareOne pages; else the plan's grid, which also
+    // sizes the workspace)
+    const long long pairs = (long long)B * Hkv * max_blocks_per_seq;
+    const long long wgs = !p.balanced  ? ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits
+                          : p.bal_one ? std::max<long long>(sv::kBalTargetWgs,
+                                                             (pairs + sv::kBalMaxShareOne - 1) / sv::kBalMaxShareOne)
+                                      : (long long)pl.grid_bal;
     if (wgs > 0x7FFFFFF0LL)
         return fail(SV_ERR_SHAPE, "too many workgroups");
     p.grid = (int)wgs;

@@ -12,7 +12,29 @@ constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kMaxRows = 128;       // T * (Hq/Hkv) per (sequence, kv head) unit
 constexpr int kMaxSplits = 128;     // context splits per unit
 constexpr int kMaxBps = 512;        // context pages per split
-constexpr int kAttnThreads = 256;   // 4 waves per workgroup
+constexpr int kAttnThreads = 256;   // 4 waves per workgroup (vector-ALU kernel)
+
+// Workgroup shape of the matrix-core attention kernel for head size d, rg
+// 16-row tiles per KV head, E4M3 storage (fp8) and balanced shares (bal).
+// Shared pages (two waves per page stream, each holding half of the row
+// tiles) for E4M3 with d = 128 and three or more tiles, and for more than
+// four tiles.  Otherwise every wave holds every row tile and streams pages of
+// its own: 4 waves, one per SIMD, except that balanced shares with at most
+// two tiles run 8 (two per SIMD, one workgroup per compute unit): two 4-wave
+// workgroups on one compute unit do not progress alike (the one dispatched
+// first finished a 528-page share ~25% sooner), so the unit idled at the
+// end; one 8-wave workgroup per unit finishes its waves together.  (Fixed
+// splits measured faster with 4 waves: 64-page splits of an 8B-layer shape
+// 28.3 against 29.1 us.)
+constexpr bool attn_share_pages(int d, int rg, bool fp8) { return (fp8 && d == 128 && rg >= 3) || rg > 4; }
+constexpr int attn_page_streams(int d, int rg, bool fp8, bool bal)
+{
+    return (bal && !attn_share_pages(d, rg, fp8) && rg <= 2) ? 8 : 4;
+}
+constexpr int attn_waves(int d, int rg, bool fp8, bool bal)
+{
+    return attn_share_pages(d, rg, fp8) ? 8 : attn_page_streams(d, rg, fp8, bal);
+}
 
 // Everything one attention launch needs.  Sizes are validated by the caller.
 struct AttnParams {
@@ -30,6 +52,7 @@ struct AttnParams {
                            // balanced shares: slot = unit + workgroup
     int *bal_prefix;       // balanced shares: [B+1] pages of the sequences before b (written by workgroup 0)
     int balanced;          // 1: every workgroup takes an equal share of all (unit, page) pairs
+    int bal_one;           // balanced shares: 1 = one share per compute unit (8-wave workgroups)
     int B, T, Hq, Hkv, G, TG, d;
     int max_blocks, num_blocks;
     int bps;               // context blocks per split (multiple of 8)
@@ -55,17 +78,20 @@ struct AttnPlan {
 // Balanced shares.  The (unit, page) pairs of the whole batch, units in
 // order b * Hkv + g and pages in order within a unit, are cut into equal
 // shares of S pages, one per workgroup, so ragged context lengths leave no
-// long workgroup behind: S = max(4, ceil(total / kBalTargetWgs)) (one share
-// per compute unit) while that is at most kBalOneShare pages, else
-// S = min(kBalMaxShare, ceil(total / (2 * kBalTargetWgs))) (two per compute
-// unit, all resident at once, rather than a second round of a few).
+// long workgroup behind.  8-wave workgroups (one fills a compute unit):
+// S = min(kBalMaxShareOne, max(4, ceil(total / kBalTargetWgs))), one share
+// per compute unit.  4-wave workgroups: the same while S is at most
+// kBalOneShare pages, else S = min(kBalMaxShare, ceil(total / (2 *
+// kBalTargetWgs))) (two per compute unit, all resident at once, rather than a
+// second round of a few).
 // Chosen by the planner for large batches of several sequences (at least
 // kBalMinPages pairs at the longest context, at most kBalMaxB sequences).
 constexpr int kSplitBalanced = -1;      // blocks_per_split value that asks for balanced shares
 constexpr int kBalMaxB = 1024;          // sequences (prefix sums held in LDS)
 constexpr int kBalTargetWgs = 256;      // shares aimed for: one per compute unit
 constexpr int kBalOneShare = 512;      // longest share at one workgroup per compute unit
-constexpr int kBalMaxShare = 1024;     // pages per share (page ids held in LDS)
+constexpr int kBalMaxShare = 1024;     // pages per share, two per compute unit (page ids held in LDS)
+constexpr int kBalMaxShareOne = 2048;  // pages per share, one per compute unit
 constexpr long long kBalMinPages = 65536;
 constexpr long long kBalMaxPages = 1LL << 30;  // (unit, page) pairs: positions stay in int
 

@@ -154,7 +154,8 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
         reinterpret_cast<float2 *>(p.part_ml)[base + row] = make_float2(mrow[row], lrow[row]);
 }
 
-// Split merge (flash-decoding second pass): one wave per (unit, row).
+// Split merge (flash-decoding second pass): one wave per R consecutive rows
+// of one unit (R = 1 unless the grid would exceed one resident round).
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s o_s 2^(m_s - M) / L.
 // Lanes hold one split's statistics each (reduced with DPP) and slices of
 // the head dim.  Fixed splits: the context length, the statistics and the
@@ -162,21 +163,24 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 // inside the workspace), so the common case costs one round trip to memory;
 // entries of splits past the context are discarded.  Balanced shares: the
 // unit's first slot and its number of partials come from the prefix sums the
-// attention kernel left in the workspace, then the same loads follow.
+// attention kernel left in the workspace, then the same loads follow (for
+// all R rows at once).
 // NB: splits whose partial rows are requested at once (16 or 32 for many
 // fixed splits, where the grid has few waves: c5b's 32 splits 10.1 us with
 // 8, 9.0 with 16; else 8, whose fewer registers keep more waves resident:
 // balanced shares at B = 64 12.0 us against 15.6 with 16).
-template <int D, int NB>
+template <int D, int NB, int R>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
     constexpr int PER = D / 64;  // floats per lane
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int units = p.B * p.Hkv;
-    if (gw >= units * p.TG)
+    const int TG = p.TG;
+    const int ngrp = (TG + R - 1) / R;  // groups of R consecutive rows per unit, one wave each
+    if (gw >= units * ngrp)
         return;
-    const int unit = gw / p.TG, row = gw - unit * p.TG;
+    const int unit = gw / ngrp, row0 = (gw - unit * ngrp) * R;
     const int b = unit / p.Hkv, g = unit - b * p.Hkv;
     const float ninf = -__builtin_inff();
     size_t slot0;
@@ -196,24 +200,30 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
         cnt = p.max_splits;
         Lraw = p.context_lens[b];
     }
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + slot0 * p.TG + row;
-    const float *po = p.part_o + (slot0 * p.TG + row) * D + lane * PER;
-    const size_t sstride = (size_t)p.TG * D;  // floats between splits' partial rows
-
-    const float2 st0 = lane < cnt ? ml[(size_t)lane * p.TG] : make_float2(ninf, 0.0f);
-    float o[NB][PER];
+    const size_t sstride = (size_t)TG * D;  // floats between splits' partial rows
+    // every row's statistics and first NB partial rows, requested together
+    float2 st0[R];
+    float o[R][NB][PER];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        const bool valid = row < TG;
+        const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + slot0 * TG + row;
+        const float *po = p.part_o + (slot0 * TG + row) * D + lane * PER;
+        st0[r] = (valid && lane < cnt) ? ml[(size_t)lane * TG] : make_float2(ninf, 0.0f);
 #pragma unroll
-        for (int k = 0; k < PER; ++k)
-            o[j][k] = 0.0f;
-        if (j < cnt) {
-            if constexpr (PER == 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(po + j * sstride);
-                o[j][0] = v.x;
-                o[j][1] = v.y;
-            } else {
-                o[j][0] = po[j * sstride];
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                o[r][j][k] = 0.0f;
+            if (valid && j < cnt) {
+                if constexpr (PER == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(po + j * sstride);
+                    o[r][j][0] = v.x;
+                    o[r][j][1] = v.y;
+                } else {
+                    o[r][j][0] = po[j * sstride];
+                }
             }
         }
     }
@@ -224,66 +234,74 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
             return;  // written directly by the attention kernel
     }
 
-    float mloc = lane < ns ? st0.x : ninf;
-    for (int s = lane + kWave; s < ns; s += kWave)
-        mloc = fmaxf(mloc, ml[(size_t)s * p.TG].x);
-    const float M = wave_max_f32(mloc);
-    double Lsum = 0.0;
-    if (lane < ns && st0.x != ninf)
-        Lsum = (double)(st0.y * __builtin_amdgcn_exp2f(st0.x - M));
-    for (int s = lane + kWave; s < ns; s += kWave) {
-        const float2 v = ml[(size_t)s * p.TG];
-        if (v.x != ninf)
-            Lsum += (double)(v.y * __builtin_amdgcn_exp2f(v.x - M));
-    }
-    const float inv = (float)(1.0 / wave_sum_f64(Lsum));
-
-    float acc[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k)
-        acc[k] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        if (j < ns) {  // uniform
-            const float mj = readlane_f32(st0.x, j);
-            const float f = (mj == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
-#pragma unroll
-            for (int k = 0; k < PER; ++k)
-                acc[k] += f * o[j][k];
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row >= TG)
+            break;  // uniform
+        const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + slot0 * TG + row;
+        const float *po = p.part_o + (slot0 * TG + row) * D + lane * PER;
+        float mloc = lane < ns ? st0[r].x : ninf;
+        for (int s = lane + kWave; s < ns; s += kWave)
+            mloc = fmaxf(mloc, ml[(size_t)s * TG].x);
+        const float M = wave_max_f32(mloc);
+        double Lsum = 0.0;
+        if (lane < ns && st0[r].x != ninf)
+            Lsum = (double)(st0[r].y * __builtin_amdgcn_exp2f(st0[r].x - M));
+        for (int s = lane + kWave; s < ns; s += kWave) {
+            const float2 v = ml[(size_t)s * TG];
+            if (v.x != ninf)
+                Lsum += (double)(v.y * __builtin_amdgcn_exp2f(v.x - M));
         }
-    }
-    for (int s0 = NB; s0 < ns; s0 += NB) {
-        float f[NB];
+        const float inv = (float)(1.0 / wave_sum_f64(Lsum));
+
+        float acc[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            acc[k] = 0.0f;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const int s = s0 + j;
-            f[j] = 0.0f;
+            if (j < ns) {  // uniform
+                const float mj = readlane_f32(st0[r].x, j);
+                const float f = (mj == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
 #pragma unroll
-            for (int k = 0; k < PER; ++k)
-                o[j][k] = 0.0f;
-            if (s < ns) {
-                const float ms = ml[(size_t)s * p.TG].x;
-                f[j] = (ms == ninf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-                if constexpr (PER == 2) {
-                    const float2 v = *reinterpret_cast<const float2 *>(po + s * sstride);
-                    o[j][0] = v.x;
-                    o[j][1] = v.y;
-                } else {
-                    o[j][0] = po[s * sstride];
-                }
+                for (int k = 0; k < PER; ++k)
+                    acc[k] += f * o[r][j][k];
             }
         }
+        for (int s0 = NB; s0 < ns; s0 += NB) {
+            float f[NB], ov[NB][PER];
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+            for (int j = 0; j < NB; ++j) {
+                const int s = s0 + j;
+                f[j] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < PER; ++k)
-                acc[k] += f[j] * o[j][k];
+                for (int k = 0; k < PER; ++k)
+                    ov[j][k] = 0.0f;
+                if (s < ns) {
+                    const float ms = ml[(size_t)s * TG].x;
+                    f[j] = (ms == ninf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+                    if constexpr (PER == 2) {
+                        const float2 v = *reinterpret_cast<const float2 *>(po + s * sstride);
+                        ov[j][0] = v.x;
+                        ov[j][1] = v.y;
+                    } else {
+                        ov[j][0] = po[s * sstride];
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int k = 0; k < PER; ++k)
+                    acc[k] += f[j] * ov[j][k];
+        }
+        const int t = row / p.G, hh = row - t * p.G;
+        float *dst = p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hh) * D + lane * PER;
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            dst[k] = acc[k] * inv;
     }
-    const int t = row / p.G, hh = row - t * p.G;
-    float *dst = p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)g * p.G + hh) * D + lane * PER;
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-        dst[k] = acc[k] * inv;
 }
 
 // ---------------------------------------------------------------- MFMA kernel
@@ -1375,16 +1393,34 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
 {
     if (!p.balanced && p.max_splits <= 1)
         return hipSuccess;
-    const long long waves = (long long)p.B * p.Hkv * p.TG;
+    // One wave per group of R rows of a unit: R = 1 while one wave per row
+    // fits in one resident round (about 8192 waves), else 2 or 4 (a unit's
+    // rows then share one wave, whose loads for all of them are in flight
+    // together)
+    const long long rows = (long long)p.B * p.Hkv * p.TG;
+    const int R = rows <= 8192 ? 1 : (rows <= 16384 ? 2 : 4);
+    const long long waves = (long long)p.B * p.Hkv * ((p.TG + R - 1) / R);
     const dim3 grid((unsigned)((waves + 3) / 4));
-    if (p.d == 64)
-        hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8>), grid, dim3(256), 0, stream, p);
-    else if (!p.balanced && p.max_splits > 16)
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 32>), grid, dim3(256), 0, stream, p);
-    else if (!p.balanced && p.max_splits > 8)
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 16>), grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8>), grid, dim3(256), 0, stream, p);
+    if (p.d == 64) {
+        if (R == 1)
+            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 1>), grid, dim3(256), 0, stream, p);
+        else if (R == 2)
+            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 2>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 4>), grid, dim3(256), 0, stream, p);
+    } else if (!p.balanced && p.max_splits > 16) {
+        const dim3 g1((unsigned)((rows + 3) / 4));
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 32, 1>), g1, dim3(256), 0, stream, p);
+    } else if (!p.balanced && p.max_splits > 8) {
+        const dim3 g1((unsigned)((rows + 3) / 4));
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 16, 1>), g1, dim3(256), 0, stream, p);
+    } else if (R == 1) {
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 1>), grid, dim3(256), 0, stream, p);
+    } else if (R == 2) {
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 2>), grid, dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 4>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -163,6 +163,22 @@ def test_split_calls_back_to_back():
         assert torch.equal(o0, o1)
 
 
+# E4M3 over long runs: runs of 512 pages give every page stream of 4 (or 8)
+# waves 128 (64) pages, each with its own K and V page scales; shared pages
+# (three row tiles) and own pages (one and two row tiles), both head sizes,
+# a forced fixed split and balanced shares.
+LONG_E4M3 = [(5, 64, 8, 128), (4, 32, 8, 128), (2, 16, 8, 128), (4, 32, 4, 64)]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d", LONG_E4M3, ids=["T%d-Hq%d-Hkv%d-d%d" % c for c in LONG_E4M3])
+def test_e4m3_long_runs(T, Hq, Hkv, d):
+    a = W.make_attn_from_lens(51, 2, T, Hq, Hkv, d, [9000, 8200], kv="fp8", extra_blocks=2)
+    t = upload_attn(a)
+    for bps in (512, -1):
+        out = run_attn(a, t, blocks_per_split=bps)
+        assert _check(a, out) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
+
+
 # Every wide row count (five to eight row tiles per KV head: shared pages,
 # Q operands in LDS at seven and eight) for both head sizes and both
 # low-precision storages, under balanced shares, a forced fixed split and the

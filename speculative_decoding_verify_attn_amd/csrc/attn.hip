@@ -580,8 +580,9 @@ struct MfmaShape {
     static constexpr int TPH = RGW < kTilesPerPhase ? RGW : kTilesPerPhase;  // row tiles per epilogue phase
     static constexpr int WT = TPH * 16 * OP;  // floats of one wave's parked O rows
     // LDS: the page rings (one per page stream, RSTRIDE bytes apart) and, at
-    // the end, each wave's parked O rows (PSTRIDE bytes apart).  With 4 waves
-    // a wave's ring and parked rows share one region.
+    // the end, each wave's parked O rows (PSTRIDE bytes apart).  Without
+    // shared pages (one wave per stream) a wave's ring and parked rows share
+    // one region.
     static constexpr int RING = (NS * PG::STAGE + 15) & ~15;
     static constexpr int PARK = (WT * 4 + 15) & ~15;
     static constexpr int RW = RING > PARK ? RING : PARK;
@@ -1053,10 +1054,10 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     }
 
     // ---- epilogue: each wave parks its (max, sum) rows and unnormalised
-    // tile in its own LDS region (with 4 waves its ring, idle once its copies
-    // have landed; with shared pages after a barrier, once both waves of
-    // every stream are done with the rings), and after one barrier a single
-    // pass merges the waves of each row half and writes the result.
+    // tile in its own LDS region (without shared pages its ring, idle once
+    // its copies have landed; with shared pages after a barrier, once both
+    // waves of every stream are done with the rings), and after one barrier a
+    // single pass merges the waves of each row half and writes the result.
     wait_dma<0>();
 #pragma unroll
     for (int rt = 0; rt < RGW; ++rt) {

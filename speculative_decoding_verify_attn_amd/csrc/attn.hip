@@ -532,11 +532,12 @@ __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const
 // their common ring and a workgroup barrier per page hands it to wave w+4.
 // One wave per SIMD leaves about half of such a page's time in stalls (the
 // matrix instructions alone issue at near their peak rate from one wave);
-// the second wave fills them.  bf16 storage uses them only for more than
-// four row tiles (T*G > 64, e.g. 16-node trees at G = 8), where one wave
-// cannot hold every row tile's accumulators: with up to four row tiles it
-// streams at the memory's rate with 4 waves (shared pages measured slower
-// there: 70B-layer shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
+// the second wave fills them.  bf16 storage uses them for more than four
+// row tiles (T*G > 64, e.g. 16-node trees at G = 8), where one wave cannot
+// hold every row tile's accumulators, and for four under balanced shares
+// (see attn_share_pages); otherwise with up to four row tiles it streams at
+// the memory's rate with 4 waves (shared pages measured slower there:
+// 70B-layer shape 196 -> 231 us, 131k context 106 -> 125 us).  Also measured: 8 waves
 // each with every row tile and every 8th page streamed no faster for bf16
 // with fixed splits (8B-layer shape: 29.1 vs 28.3 us) and slower for E4M3
 // (registers spill); they are used for balanced shares with at most two row
@@ -550,7 +551,7 @@ constexpr int kTilesPerPhase = 2;  // row tiles merged per epilogue phase
 template <int D, int RG, bool FP8, bool BAL>
 struct MfmaShape {
     typedef PageGeom<D, FP8> PG;
-    static constexpr bool SHARE = attn_share_pages(D, RG, FP8);
+    static constexpr bool SHARE = attn_share_pages(D, RG, FP8, BAL);
     static constexpr int HV = SHARE ? 2 : 1;                      // waves per page stream
     static constexpr int NWP = attn_page_streams(D, RG, FP8, BAL);  // page streams
     static constexpr int NW = NWP * HV;               // waves per workgroup

@@ -17,23 +17,29 @@ constexpr int kAttnThreads = 256;   // 4 waves per workgroup (vector-ALU kernel)
 // Workgroup shape of the matrix-core attention kernel for head size d, rg
 // 16-row tiles per KV head, E4M3 storage (fp8) and balanced shares (bal).
 // Shared pages (two waves per page stream, each holding half of the row
-// tiles) for E4M3 with d = 128 and three or more tiles, and for more than
-// four tiles.  Otherwise every wave holds every row tile and streams pages of
-// its own: 4 waves, one per SIMD, except that balanced shares with at most
-// two tiles run 8 (two per SIMD, one workgroup per compute unit): two 4-wave
-// workgroups on one compute unit do not progress alike (the one dispatched
-// first finished a 528-page share ~25% sooner), so the unit idled at the
-// end; one 8-wave workgroup per unit finishes its waves together.  (Fixed
-// splits measured faster with 4 waves: 64-page splits of an 8B-layer shape
-// 28.3 against 29.1 us.)
-constexpr bool attn_share_pages(int d, int rg, bool fp8) { return (fp8 && d == 128 && rg >= 3) || rg > 4; }
+// tiles) for E4M3 with d = 128 and three or more tiles, for more than four
+// tiles, and for four tiles under balanced shares (ragged 64-sequence batch
+// with 16 verify rows: 504 -> 488 us; with three tiles, the 70B-layer shape,
+// they measured slower: 196 -> 216 us; with fixed splits slower too).
+// Otherwise every wave holds every row tile and streams pages of its own: 4
+// waves, one per SIMD, except that balanced shares with at most two tiles run
+// 8 (two per SIMD, one workgroup per compute unit): two 4-wave workgroups on
+// one compute unit do not progress alike (the one dispatched first finished a
+// 528-page share ~25% sooner), so the unit idled at the end; one 8-wave
+// workgroup per unit finishes its waves together.  (Fixed splits measured
+// faster with 4 waves: 64-page splits of an 8B-layer shape 28.3 against
+// 29.1 us.)
+constexpr bool attn_share_pages(int d, int rg, bool fp8, bool bal)
+{
+    return (fp8 && d == 128 && rg >= 3) || rg > 4 || (bal && rg == 4);
+}
 constexpr int attn_page_streams(int d, int rg, bool fp8, bool bal)
 {
-    return (bal && !attn_share_pages(d, rg, fp8) && rg <= 2) ? 8 : 4;
+    return (bal && !attn_share_pages(d, rg, fp8, bal) && rg <= 2) ? 8 : 4;
 }
 constexpr int attn_waves(int d, int rg, bool fp8, bool bal)
 {
-    return attn_share_pages(d, rg, fp8) ? 8 : attn_page_streams(d, rg, fp8, bal);
+    return attn_share_pages(d, rg, fp8, bal) ? 8 : attn_page_streams(d, rg, fp8, bal);
 }
 
 // Everything one attention launch needs.  Sizes are validated by the caller.

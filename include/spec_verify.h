@@ -130,9 +130,12 @@ int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache,
  * B*Hkv*max_blocks_per_seq <= 2^30, else SV_ERR_UNSUPPORTED): the
  * (sequence, KV head, page) triples of the whole batch, in that order, are
  * cut on the device, from context_lens, into equal runs of S pages, one per
- * workgroup, so a ragged batch leaves no long workgroup behind:
- * S = max(4, ceil(total / 256)) while that is at most 512, else
- * S = min(1024, ceil(total / 512)).  The planner uses them for
+ * workgroup, so a ragged batch leaves no long workgroup behind.  With 8-wave
+ * workgroups -- at most two or exactly four 16-row tiles of verify rows per
+ * KV head, E4M3 with d = 128 and three or more tiles, or more than four
+ * tiles -- S = min(2048, max(4, ceil(total / 256))), one run per compute
+ * unit; otherwise (4 waves) S = max(4, ceil(total / 256)) while that is at
+ * most 512, else S = min(1024, ceil(total / 512)).  The planner uses them for
  * batches of two or more sequences with B*Hkv*max_blocks_per_seq >= 65536
  * when the matrix-core kernel runs.  Results agree with the fixed split up
  * to the order of floating-point additions.

@@ -179,15 +179,15 @@ def test_e4m3_long_runs(T, Hq, Hkv, d):
         assert _check(a, out) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
 
 
-# Every wide row count (five to eight row tiles per KV head: shared pages,
-# Q operands in LDS at seven and eight) for both head sizes and both
-# low-precision storages, under balanced shares, a forced fixed split and the
-# planner's choice.  Regression: under register pressure the compiler
+# Every row count from four to eight row tiles per KV head (shared pages:
+# for four tiles under balanced shares only; Q operands in LDS at seven and
+# eight) for both head sizes and both low-precision storages, under balanced
+# shares, a forced fixed split and the planner's choice.  Regression: under register pressure the compiler
 # reloaded a spilled copy offset into an SGPR one instruction before the
 # inline-assembly LDS copy that reads it, which needs five wait states in
 # between; the copy then fetched the wrong key's V bytes (all rows wrong at
 # d = 64 with eight tiles and at d = 128 E4M3 with five and six).
-WIDE = [(kv, d, T) for kv in ("bf16", "fp8") for d in (64, 128) for T in (10, 12, 14, 16)]
+WIDE = [(kv, d, T) for kv in ("bf16", "fp8") for d in (64, 128) for T in (7, 8, 10, 12, 14, 16)]
 
 
 @pytest.mark.parametrize("kv,d,T", WIDE, ids=["%s-d%d-T%d" % c for c in WIDE])

@@ -356,6 +356,24 @@ def test_balanced_shares_many_sequences(B, T, Hq, d, kv):
     assert torch.isfinite(out).all()
 
 
+def test_balanced_shares_capped_more_than_one_round():
+    """More (sequence, KV head, page) pairs than 256 shares of the largest
+    run an 8-wave workgroup holds (2048 pages): the shares are capped, the
+    grid exceeds the compute units, and every unit (1024 here, 2.5 GB of KV)
+    is still covered once."""
+    rng = np.random.default_rng(7)
+    B, T, Hq, Hkv, d = 64, 2, 16, 16, 64
+    lens = [int(x) for x in rng.integers(8000, 11000, size=B)]
+    a = W.make_attn_from_lens(7, B, T, Hq, Hkv, d, lens, kv="bf16", extra_blocks=2)
+    assert Hkv * sum((L + 15) // 16 for L in lens) > 256 * 2048
+    t = upload_attn(a)
+    rows, units = unit_rows(a, seed=3)
+    assert len(units) == B * Hkv
+    for bps in (-1, 0):
+        out = run_attn(a, t, blocks_per_split=bps)
+        assert _check(a, out, rows) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
+
+
 RANDOM_BAL = [c for c in _random_shapes(40, 2025) if c[7] != "f32"][:12]
 
 

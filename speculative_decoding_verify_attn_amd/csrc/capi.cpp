@@ -137,8 +137,11 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
     }
     size_t total = off;
     if (pl.balanced) {
-        // ceil(total / S) shares never exceed this many workgroups (S is
-        // kBalMaxShare, or at least ceil(total / (2 * kBalTargetWgs)))
+        // ceil(total / S) shares never exceed this many workgroups (4-wave
+        // shares: S is kBalMaxShare, or at least ceil(total / (2 *
+        // kBalTargetWgs)); 8-wave shares, one per compute unit, are fewer:
+        // at most max(kBalTargetWgs, ceil(total / kBalMaxShareOne)), the grid
+        // such a call launches, see attn_impl)
         const long long g = std::max<long long>(2 * kBalTargetWgs, (pairs + kBalMaxShare - 1) / kBalMaxShare);
         pl.grid_bal = (int)g;
         const long long slots = units + g;

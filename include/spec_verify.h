@@ -135,7 +135,10 @@ int spec_verify_attn(const float *q, const void *k_cache, const void *v_cache,
  * KV head, E4M3 with d = 128 and three or more tiles, or more than four
  * tiles -- S = min(2048, max(4, ceil(total / 256))), one run per compute
  * unit; otherwise (4 waves) S = max(4, ceil(total / 256)) while that is at
- * most 512, else S = min(1024, ceil(total / 512)).  The planner uses them for
+ * most 512, else S = min(1024, ceil(total / 512)).  With at most two tiles
+ * and an even Hkv a workgroup runs KV heads 2j and 2j+1 side by side: the
+ * runs then cut the (sequence, head pair, page) triples, total being half
+ * the pages of the batch's (sequence, KV head) units.  The planner uses them for
  * batches of two or more sequences with B*Hkv*max_blocks_per_seq >= 65536
  * when the matrix-core kernel runs.  Results agree with the fixed split up
  * to the order of floating-point additions.

@@ -57,8 +57,11 @@ __device__ __forceinline__ int clamp_len(const AttnParams &p, int Lraw)
 // Pages per balanced share for `total` (unit, page) pairs.  Share j (the
 // block index) is pairs [j*S, (j+1)*S) of the batch's list (units in order
 // b * Hkv + g, pages in order within a unit); a unit cut by several shares
-// leaves partials in slots unit + j, consecutive in j.  Shares go to the
-// dies round robin with the block index.  (Giving each die the units of its
+// leaves partials in slots unit + j, consecutive in j.  With head groups
+// (bal_heads) the list holds (group, page) pairs, groups in order
+// b * (Hkv / hg) + g / hg, and head g's partials go to slots
+// (group + j) * hg + g % hg.  Shares go to the dies round robin with the
+// block index.  (Giving each die the units of its
 // own KV heads measured 9% slower on a ragged batch, 3% faster on one long
 // sequence.)
 // one_per_cu: the kernel's 8-wave workgroups fill a compute unit each.
@@ -183,24 +186,29 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
     const int unit = gw / ngrp, row0 = (gw - unit * ngrp) * R;
     const int b = unit / p.Hkv, g = unit - b * p.Hkv;
     const float ninf = -__builtin_inff();
-    size_t slot0;
+    size_t slot0, sst = 1;  // first slot, slots between consecutive partials
     int cnt, ns = 0;  // partials that may be read; partials of the unit
     int Lraw = 0;
     if (p.balanced) {
+        // head groups: group b * (Hkv / hg) + g / hg, partials in slots
+        // (group + share) * hg + g % hg
+        const int hg = p.bal_hg, ngr = p.Hkv / hg, gi = g / hg;
         const int nblk = (clamp_len(p, p.context_lens[b]) + kBlock - 1) / kBlock;
-        const int S = bal_share(p.Hkv * p.bal_prefix[p.B], p.bal_one != 0);
-        const int start = p.Hkv * p.bal_prefix[b] + g * nblk;
+        const int S = bal_share(ngr * p.bal_prefix[p.B], p.bal_one != 0);
+        const int start = ngr * p.bal_prefix[b] + gi * nblk;
         ns = nblk > 0 ? (start + nblk - 1) / S - start / S + 1 : 0;
         if (ns <= 1)
             return;  // written directly by the attention kernel (or no context)
-        slot0 = (size_t)unit + start / S;
+        slot0 = ((size_t)b * ngr + gi + start / S) * hg + (g - gi * hg);
+        sst = (size_t)hg;
         cnt = ns;
     } else {
         slot0 = (size_t)unit * p.max_splits;
         cnt = p.max_splits;
         Lraw = p.context_lens[b];
     }
-    const size_t sstride = (size_t)TG * D;  // floats between splits' partial rows
+    const size_t sstride = sst * TG * D;  // floats between consecutive partials' rows
+    const size_t mstride = sst * TG;      // (max, sum) pairs between them
     // every row's statistics and first NB partial rows, requested together
     float2 st0[R];
     float o[R][NB][PER];
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
         const bool valid = row < TG;
         const float2 *ml = reinterpret_cast<const float2 *>(p.part_ml) + slot0 * TG + row;
         const float *po = p.part_o + (slot0 * TG + row) * D + lane * PER;
-        st0[r] = (valid && lane < cnt) ? ml[(size_t)lane * TG] : make_float2(ninf, 0.0f);
+        st0[r] = (valid && lane < cnt) ? ml[(size_t)lane * mstride] : make_float2(ninf, 0.0f);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -243,13 +251,13 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
         const float *po = p.part_o + (slot0 * TG + row) * D + lane * PER;
         float mloc = lane < ns ? st0[r].x : ninf;
         for (int s = lane + kWave; s < ns; s += kWave)
-            mloc = fmaxf(mloc, ml[(size_t)s * TG].x);
+            mloc = fmaxf(mloc, ml[(size_t)s * mstride].x);
         const float M = wave_max_f32(mloc);
         double Lsum = 0.0;
         if (lane < ns && st0[r].x != ninf)
             Lsum = (double)(st0[r].y * __builtin_amdgcn_exp2f(st0[r].x - M));
         for (int s = lane + kWave; s < ns; s += kWave) {
-            const float2 v = ml[(size_t)s * TG];
+            const float2 v = ml[(size_t)s * mstride];
             if (v.x != ninf)
                 Lsum += (double)(v.y * __builtin_amdgcn_exp2f(v.x - M));
         }
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
                 for (int k = 0; k < PER; ++k)
                     ov[j][k] = 0.0f;
                 if (s < ns) {
-                    const float ms = ml[(size_t)s * TG].x;
+                    const float ms = ml[(size_t)s * mstride].x;
                     f[j] = (ms == ninf) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
                     if constexpr (PER == 2) {
                         const float2 v = *reinterpret_cast<const float2 *>(po + s * sstride);
@@ -480,45 +488,57 @@ __device__ __forceinline__ void tile_store32(float *tile, const floatx16 (&acc)[
     }
 }
 
-// Merges the NT wave tiles of rows r0 .. r1-1 of one workgroup and stores
-// the result: normalised output when slot < 0 (the workgroup saw the unit's
-// whole context), else the unnormalised partial (o, max, sum) in workspace
-// slot `slot` for the merge kernel.  tiles: NT tiles
-// holding rows r0.. as [rows][D+4] floats, `pitch` floats apart; sm/sl:
-// per-wave row max (base-2 units) and row sum.
+// Merges the wave tiles of rows r0 .. r1-1 of one workgroup and stores the
+// result, for nh KV heads side by side (g .. g+nh-1): head hh's NT / nh waves
+// are hh, hh + nh, ...  Normalised output when slot < 0 (the workgroup saw
+// the unit's whole context), else the unnormalised partial (o, max, sum) in
+// workspace slot slot + hh for the merge kernel.  tiles: NT tiles holding
+// rows r0.. as [rows][D+4] floats, `pitch` floats apart; sm/sl: per-wave row
+// max (base-2 units) and row sum.
 template <int D, int RG, int NT>
 __device__ __forceinline__ void merge_waves_and_store(const AttnParams &p, const float *tiles, int pitch,
                                                       const float (*sm)[kMaxRows], const float (*sl)[kMaxRows],
-                                                      int slot, int b, int g, int r0, int r1)
+                                                      int slot, int b, int g, int r0, int r1, int nh = 1)
 {
     constexpr int OP = D + 4;
     constexpr int C4 = D / 4;
     const float ninf = -__builtin_inff();
     const int G = p.G;
-    const size_t pbase = (size_t)(slot < 0 ? 0 : slot) * p.TG;
-    for (int idx = threadIdx.x; idx < (r1 - r0) * C4; idx += blockDim.x) {
-        const int lr = idx / C4, c4 = idx - lr * C4;
+    const int nv = NT / nh;           // waves per head
+    const int per = (r1 - r0) * C4;   // items per head
+    for (int idx = threadIdx.x; idx < nh * per; idx += blockDim.x) {
+        const int hh = nh == 1 ? 0 : idx / per;
+        const int r = idx - hh * per;
+        const int lr = r / C4, c4 = r - lr * C4;
         const int row = r0 + lr;
-        float M = sm[0][row];
+        float M = sm[hh][row];
 #pragma unroll
-        for (int v = 1; v < NT; ++v)
-            M = fmaxf(M, sm[v][row]);
+        for (int v = 1; v < NT; ++v) {
+            if (v >= nv)
+                break;
+            M = fmaxf(M, sm[hh + v * nh][row]);
+        }
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         float Ls = 0.0f;
 #pragma unroll
         for (int v = 0; v < NT; ++v) {
-            const float mv = sm[v][row];
+            if (v >= nv)
+                break;
+            const int w = hh + v * nh;
+            const float mv = sm[w][row];
             const float f = (mv == ninf) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            const float4 x = *reinterpret_cast<const float4 *>(tiles + v * pitch + lr * OP + c4 * 4);
+            const float4 x = *reinterpret_cast<const float4 *>(tiles + w * pitch + lr * OP + c4 * 4);
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
-            Ls += f * sl[v][row];
+            Ls += f * sl[w][row];
         }
         if (slot < 0) {
             const float inv = 1.0f / Ls;
             o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-            const int t = row / G, hh = row - t * G;
-            *reinterpret_cast<float4 *>(p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)g * G + hh) * D + c4 * 4) = o;
+            const int t = row / G, q = row - t * G;
+            *reinterpret_cast<float4 *>(p.out + (((size_t)b * p.T + t) * p.Hq + (size_t)(g + hh) * G + q) * D +
+                                        c4 * 4) = o;
         } else {
+            const size_t pbase = (size_t)(slot + hh) * p.TG;
             *reinterpret_cast<float4 *>(p.part_o + (pbase + row) * D + c4 * 4) = o;
             if (c4 == 0)
                 reinterpret_cast<float2 *>(p.part_ml)[pbase + row] = make_float2(M, Ls);
@@ -601,16 +621,18 @@ struct MfmaShape {
     static constexpr int SMEM = LOOP_LDS > NW * PSTRIDE ? LOOP_LDS : NW * PSTRIDE;
 };
 
-// One run of pages of one (sequence b, KV head g) unit: pages blk_begin ..
+// One run of pages of one (sequence b, KV head g0) unit: pages blk_begin ..
 // blk_begin + cap - 1, clipped to the context.  slot >= 0: the result is an
 // unnormalised partial in that workspace slot; slot < 0: the run is the
 // unit's whole context and the result is normalised into `out`.  With fixed
 // splits (fixed = true) the slot given is that of (unit, split), replaced by
-// -1 when the sequence has a single split.  Called by every thread of the
-// workgroup.
+// -1 when the sequence has a single split.  Head groups (balanced shares,
+// p.bal_hg > 1, see bal_heads): the run covers heads g0 .. g0 + bal_hg - 1,
+// whose partials go to slots slot .. slot + bal_hg - 1.  Called by every
+// thread of the workgroup.
 template <int D, int RG, bool FP8, bool BAL>
 __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char *smem, float (*s_m)[kMaxRows],
-                                             float (*s_l)[kMaxRows], int *s_pages, const int b, const int g,
+                                             float (*s_l)[kMaxRows], int *s_pages, const int b, const int g0,
                                              const int blk_begin, const int cap, const int slot, const bool fixed)
 {
     typedef MfmaShape<D, RG, FP8, BAL> SH;
@@ -630,7 +652,14 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int pw = wave % NWP;                // page stream: pages pw, pw + NWP, ... of the run
+    // Head groups: with 8 waves that each stream pages of their own, wave w
+    // runs head g0 + w % hg and every (8 / hg)-th page of the run.
+    constexpr bool HGRP = BAL && NWP == 8 && SH::HV == 1;
+    const int hg = HGRP ? p.bal_hg : 1;
+    const int g = g0 + (HGRP ? wave % hg : 0);       // this wave's KV head
+    const int nstr = HGRP ? NWP / hg : NWP;          // page streams of the head
+    const int pw = HGRP ? wave / hg : wave % NWP;    // page stream: pages pw, pw + nstr, ... of the run
+    const int ring_id = HGRP ? wave : pw;            // the stream's copy ring
     const bool copier = wave < NWP;           // the wave that copies its stream's pages
     const int rt_base = (wave / NWP) * RGW;   // first row tile of this wave
     const int lane = tid & 63;
@@ -648,7 +677,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     int first[NS - 1];
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
-        const int i = pw + k * NWP;
+        const int i = pw + k * nstr;
         first[k] = i < avail ? trow[i] : 0;
     }
     // (all of the run's table entries are requested before any is stored:
@@ -775,18 +804,18 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     const int v_voff = PV32 ? head_off + (lane >> 3) * slot_stride + 16 * (lane & 7)
                             : head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
     const uint32_t ring_lds =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + pw * SH::RSTRIDE;
-    const unsigned char *ring = smem + pw * SH::RSTRIDE;
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + ring_id * SH::RSTRIDE;
+    const unsigned char *ring = smem + ring_id * SH::RSTRIDE;
     int4v dks{}, dvs{};
     if constexpr (FP8) {
         dks = page_desc(reinterpret_cast<const unsigned char *>(p.k_scale), 0, (uint32_t)p.num_blocks * 4u);
         dvs = page_desc(reinterpret_cast<const unsigned char *>(p.v_scale), 0, (uint32_t)p.num_blocks * 4u);
     }
 
-    // This wave's pages are blk_begin + pw + k*NWP, k = 0, 1, ...  With
+    // This wave's pages are blk_begin + pw + k*nstr, k = 0, 1, ...  With
     // shared pages every wave runs the same number of steps (one barrier
     // each); a stream with one page fewer skips its last step's work.
-    const int nk = npg > pw ? (npg - pw + NWP - 1) / NWP : 0;
+    const int nk = npg > pw ? (npg - pw + nstr - 1) / nstr : 0;
     const int nsteps = SHARE ? (npg + NWP - 1) / NWP : nk;
     auto issue = [&](int k, int ph) {
         const int stage = k % NS;
@@ -834,16 +863,16 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 wait_pages(min(NS - 2, nk - 1 - k));
             __syncthreads();
             if (copier && k + NS - 1 < nk)
-                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * NWP]);
+                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * nstr]);
             if (k >= nk)
                 continue;  // wave-uniform: this stream has one page fewer
         } else {
             if (k + NS - 1 < nk)
-                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * NWP]);
+                issue(k + NS - 1, s_pages[pw + (k + NS - 1) * nstr]);
             // wait for page k: the copies of up to NS-1 younger pages may stay in flight
             wait_pages(min(NS - 1, nk - 1 - k));
         }
-        const int pg = pw + k * NWP;
+        const int pg = pw + k * nstr;
         const int key0 = (blk_begin + pg) * kBlock;
         const unsigned char *st = ring + (k % NS) * PG::STAGE;
 
@@ -1095,7 +1124,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             const int r1 = min(p.TG, (h * RGW + min(rt0 + TPH, RGW)) * 16);
             if (r0 < r1)
                 merge_waves_and_store<D, RGW, NWP>(p, reinterpret_cast<const float *>(smem + h * NWP * SH::PSTRIDE),
-                                                   SH::PSTRIDE / 4, s_m + h * NWP, s_l + h * NWP, oslot, b, g, r0, r1);
+                                                   SH::PSTRIDE / 4, s_m + h * NWP, s_l + h * NWP, oslot, b, g0, r0,
+                                                   r1, hg);
         }
     }
 }
@@ -1129,6 +1159,11 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8, BAL>::NW), 1) void sv_a
     }
     __shared__ int s_P[kBalMaxB + 1];  // pages of the sequences before b
     __shared__ int s_wsum[NW];
+    // head groups (see bal_heads): the share cuts (group, page) pairs, ngr
+    // groups of hg heads per sequence
+    constexpr bool HGRP = SH::NWP == 8 && SH::HV == 1;
+    const int hg = HGRP ? p.bal_hg : 1;
+    const int ngr = p.Hkv / hg;
     int pos = 0, end = 0, sb = 0, total = 0;
     {
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1167,18 +1202,18 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8, BAL>::NW), 1) void sv_a
         if (blockIdx.x == 0)
             for (int i = tid; i <= p.B; i += NT)
                 p.bal_prefix[i] = s_P[i];
-        total = p.Hkv * s_P[p.B];
+        total = ngr * s_P[p.B];
         const int S = bal_share(total, SH::NW == 8);
         pos = (int)blockIdx.x * S;
         if (pos >= total)
             return;
         end = min(total, pos + S);
-        // the sequence holding pair pos: the largest sb with Hkv * P[sb] <= pos
+        // the sequence holding pair pos: the largest sb with ngr * P[sb] <= pos
         // (sequences without pages are skipped: their successor has the same P)
         int lo = 0, hi = p.B - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (p.Hkv * s_P[mid] <= pos)
+            if (ngr * s_P[mid] <= pos)
                 lo = mid;
             else
                 hi = mid - 1;
@@ -1191,24 +1226,24 @@ __global__ __launch_bounds__((64 * MfmaShape<D, RG, FP8, BAL>::NW), 1) void sv_a
             const int Pb = s_P[sb], nb = s_P[sb + 1] - Pb;
             if (nb <= 0)
                 return;  // unreachable: pair pos lies inside sequence sb
-            const int base = p.Hkv * Pb, rel = pos - base;
-            const int gg = rel / nb;
-            const int uend = base + (gg + 1) * nb;  // one past the unit's last pair
+            const int base = ngr * Pb, rel = pos - base;
+            const int gg = rel / nb;                // head group
+            const int uend = base + (gg + 1) * nb;  // one past the group's last pair
             const int send = min(end, uend);
             const int off = rel - gg * nb;
             b = __builtin_amdgcn_readfirstlane(sb);
-            g = __builtin_amdgcn_readfirstlane(gg);
+            g = __builtin_amdgcn_readfirstlane(gg * hg);
             blk_begin = __builtin_amdgcn_readfirstlane(off);
             cap = __builtin_amdgcn_readfirstlane(send - pos);
             slot = __builtin_amdgcn_readfirstlane((off == 0 && send == uend) ? -1
-                                                                              : sb * p.Hkv + gg + (int)blockIdx.x);
+                                                                              : (sb * ngr + gg + (int)blockIdx.x) * hg);
         }
         mfma_segment<D, RG, FP8, BAL>(p, smem, s_m, s_l, s_pages, b, g, blk_begin, cap, slot, false);
         pos += cap;
         if (pos >= end)
             return;
         __syncthreads();  // the next segment reuses the LDS this one's epilogue read
-        while (sb < p.B - 1 && p.Hkv * s_P[sb + 1] <= pos)
+        while (sb < p.B - 1 && ngr * s_P[sb + 1] <= pos)
             ++sb;
     }
 }

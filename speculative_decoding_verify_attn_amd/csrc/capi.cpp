@@ -95,6 +95,16 @@ int noalloc_scratch(hipStream_t stream, void **ptr)
 
 namespace sv {
 
+// KV heads that one balanced-share workgroup runs side by side (head groups,
+// see bal_heads): 8-wave workgroups whose waves each stream pages of their
+// own, i.e. at most two row tiles per KV head (with balanced shares that
+// shape does not depend on the KV storage type).
+int bal_group_heads(int T, int Hq, int Hkv, int d)
+{
+    const int rg = (T * (Hq / Hkv) + 15) / 16;
+    return attn_page_streams(d, rg, false, true) == 8 ? bal_heads(Hkv) : 1;
+}
+
 // Context split.  A workgroup streams its pages through a deep LDS pipeline,
 // so it wants long splits; the grid wants at least one workgroup per compute
 // unit (256).  Splits are multiples of 4 pages (one per wave) and at most
@@ -141,10 +151,14 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int d, int max_blocks, in
         // shares: S is kBalMaxShare, or at least ceil(total / (2 *
         // kBalTargetWgs)); 8-wave shares, one per compute unit, are fewer:
         // at most max(kBalTargetWgs, ceil(total / kBalMaxShareOne)), the grid
-        // such a call launches, see attn_impl)
+        // such a call launches, see attn_impl).  Partials: slot unit + share;
+        // with head groups of hg heads, (group + share) * hg + head in group,
+        // below units + grid * hg.
         const long long g = std::max<long long>(2 * kBalTargetWgs, (pairs + kBalMaxShare - 1) / kBalMaxShare);
         pl.grid_bal = (int)g;
-        const long long slots = units + g;
+        const int hg = bal_group_heads(T, Hq, Hkv, d);
+        const long long g1 = std::max<long long>(kBalTargetWgs, (pairs / hg + kBalMaxShareOne - 1) / kBalMaxShareOne);
+        const long long slots = units + std::max(g, g1 * hg);
         size_t o = 0;
         pl.off_prefix = o;
         o = align256(o + (size_t)(B + 1) * 4);
@@ -358,6 +372,7 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.balanced = (pl.balanced && use_mfma) ? 1 : 0;
     // the share rule follows the kernel's workgroup shape (8 waves: one share per compute unit)
     p.bal_one = (p.balanced && sv::attn_waves(d, (T * (Hq / Hkv) + 15) / 16, fp8, true) == 8) ? 1 : 0;
+    p.bal_hg = p.bal_one ? sv::bal_group_heads(T, Hq, Hkv, d) : 1;
     p.part_o = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_o : pl.off_part_o));
     p.part_ml = reinterpret_cast<float *>(ws + (p.balanced ? pl.off_bal_ml : pl.off_part_ml));
     p.bal_prefix = p.balanced ? reinterpret_cast<int *>(ws + pl.off_prefix) : nullptr;
@@ -374,10 +389,10 @@ int attn_impl(const float *q, const void *k_cache, const void *v_cache, const fl
     p.max_splits = pl.max_splits;
     // fixed splits: 8 * ceil(units / 8) * max_splits workgroups (see
     // work_item in attn.hip); balanced shares: the most shares the rule can
-    // make from at most units * max_blocks pairs (one per compute unit:
-    // shares of up to kBalMaxShareOne pages; else the plan's grid, which also
-    // sizes the workspace)
-    const long long pairs = (long long)B * Hkv * max_blocks_per_seq;
+    // make from at most (B * Hkv / bal_hg) * max_blocks pairs (one per
+    // compute unit: shares of up to kBalMaxShareOne pages; else the plan's
+    // grid, which also sizes the workspace)
+    const long long pairs = (long long)B * (Hkv / p.bal_hg) * max_blocks_per_seq;
     const long long wgs = !p.balanced  ? ((long long)B * Hkv + 7) / 8 * 8 * pl.max_splits
                           : p.bal_one ? std::max<long long>(sv::kBalTargetWgs,
                                                              (pairs + sv::kBalMaxShareOne - 1) / sv::kBalMaxShareOne)

@@ -59,6 +59,7 @@ struct AttnParams {
     int *bal_prefix;       // balanced shares: [B+1] pages of the sequences before b (written by workgroup 0)
     int balanced;          // 1: every workgroup takes an equal share of all (unit, page) pairs
     int bal_one;           // balanced shares: 1 = one share per compute unit (8-wave workgroups)
+    int bal_hg;            // balanced shares: KV heads a workgroup runs side by side (see bal_heads), else 1
     int B, T, Hq, Hkv, G, TG, d;
     int max_blocks, num_blocks;
     int bps;               // context blocks per split (multiple of 8)
@@ -92,6 +93,22 @@ struct AttnPlan {
 // second round of a few).
 // Chosen by the planner for large batches of several sequences (at least
 // kBalMinPages pairs at the longest context, at most kBalMaxB sequences).
+// Head groups.  With 8-wave workgroups in which every wave streams pages of
+// its own (at most two row tiles), the workgroup runs bal_heads(Hkv) KV heads
+// side by side: wave w takes head w % hg of the group and every (8 / hg)-th
+// page of the run, so both heads' slices of a page are read at about the same
+// time, and each head's pages go to two older and two younger waves.  Shares
+// then cut the list of (group, page) pairs, groups in order
+// b * (Hkv / hg) + head group.  Ragged 64-sequence batch of 8 KV heads, main
+// kernel: one head per workgroup 419.5 us, 2 heads 412, 4 heads 412, 8 heads
+// 414.5; every sequence at the mean length: 383, 376, 401, 412 (the larger
+// groups cut every group of that batch, and with 8 heads the heads of the
+// younger waves set the pace).  (A read-only probe of the same bytes: one
+// head's slices at a time 351 us, whole pages 328 us.)
+constexpr int bal_heads(int hkv)
+{
+    return hkv % 2 == 0 ? 2 : 1;
+}
 constexpr int kSplitBalanced = -1;      // blocks_per_split value that asks for balanced shares
 constexpr int kBalMaxB = 1024;          // sequences (prefix sums held in LDS)
 constexpr int kBalTargetWgs = 256;      // shares aimed for: one per compute unit

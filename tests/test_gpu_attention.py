@@ -359,10 +359,11 @@ def test_balanced_shares_many_sequences(B, T, Hq, d, kv):
 def test_balanced_shares_capped_more_than_one_round():
     """More (sequence, KV head, page) pairs than 256 shares of the largest
     run an 8-wave workgroup holds (2048 pages): the shares are capped, the
-    grid exceeds the compute units, and every unit (1024 here, 2.5 GB of KV)
-    is still covered once."""
+    grid exceeds the compute units, and every unit (960 here, 2.4 GB of KV)
+    is still covered once.  15 KV heads: no head groups (an odd head count
+    runs one head per workgroup), so the pairs are (unit, page) pairs."""
     rng = np.random.default_rng(7)
-    B, T, Hq, Hkv, d = 64, 2, 16, 16, 64
+    B, T, Hq, Hkv, d = 64, 2, 15, 15, 64
     lens = [int(x) for x in rng.integers(8000, 11000, size=B)]
     a = W.make_attn_from_lens(7, B, T, Hq, Hkv, d, lens, kv="bf16", extra_blocks=2)
     assert Hkv * sum((L + 15) // 16 for L in lens) > 256 * 2048
@@ -371,6 +372,29 @@ def test_balanced_shares_capped_more_than_one_round():
     assert len(units) == B * Hkv
     for bps in (-1, 0):
         out = run_attn(a, t, blocks_per_split=bps)
+        assert _check(a, out, rows) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
+
+
+# Head groups under balanced shares (at most two row tiles per KV head: the
+# workgroup runs two heads side by side, a share cuts (group, page) pairs and
+# a cut group's partials sit two slots apart).  Ragged lengths, so shares
+# start and end inside groups; odd group counts (6 heads: 3 groups).
+HGROUPS = [(2, 4, 8, 128, "bf16"), (4, 2, 8, 64, "fp8"), (6, 2, 16, 128, "bf16"), (8, 4, 8, 128, "bf16"),
+           (8, 4, 8, 128, "fp8"), (12, 1, 7, 64, "bf16"), (16, 2, 5, 128, "fp8"), (8, 1, 1, 64, "bf16")]
+
+
+@pytest.mark.parametrize("Hkv,G,T,d,kv", HGROUPS, ids=["Hkv%d-G%d-T%d-d%d-%s" % c for c in HGROUPS])
+def test_head_groups_ragged(Hkv, G, T, d, kv):
+    rng = np.random.default_rng(Hkv * 100 + G * 10 + T)
+    B = 24
+    lens = [int(x) for x in rng.integers(T, 2500, size=B - 3)] + [T, 16, 17]
+    a = W.make_attn_from_lens(50 + Hkv, B, T, Hkv * G, Hkv, d, lens, kv=kv, extra_blocks=2)
+    t = upload_attn(a)
+    rows, units = unit_rows(a, seed=4)
+    assert len(units) == B * Hkv
+    for bps in (-1, 0):
+        out = run_attn(a, t, blocks_per_split=bps)
+        assert torch.isfinite(out).all()
         assert _check(a, out, rows) <= TOL[a.kv_dtype], "blocks_per_split %d" % bps
 
 

@@ -16,12 +16,16 @@ pytestmark = pytest.mark.gpu
 # (seed, B, T, Hq, Hkv, d, lens, kv): each pair is a larger call, then a
 # smaller one.  The first pair splits contexts with the fixed split (merge
 # kernel reads the scratch), the second takes balanced shares (prefix sums
-# and partials in the scratch), the third is E4M3 with one long sequence.
+# and partials in the scratch), the third is E4M3 with one long sequence,
+# the fourth balanced shares over head groups (two KV heads per workgroup)
+# twice, the second on a smaller batch.
 PAIRS = [
     ((31, 4, 6, 32, 8, 128, [2000, 1500, 37, 900], "bf16"), (32, 2, 6, 32, 8, 128, [700, 100], "bf16")),
     ((33, 16, 5, 64, 8, 128, [int(x) for x in np.linspace(300, 8192, 16)], "bf16"),
      (34, 3, 4, 32, 8, 128, [1200, 16, 555], "bf16")),
     ((35, 1, 7, 64, 8, 128, [20000], "fp8"), (36, 1, 3, 16, 2, 64, [900], "fp8")),
+    ((38, 24, 8, 32, 8, 128, [int(x) for x in np.linspace(8192, 40, 24)], "bf16"),
+     (39, 16, 4, 16, 8, 64, [int(x) for x in np.linspace(100, 8192, 16)], "bf16")),
 ]
 
 
@@ -33,7 +37,7 @@ def _noalloc(a, t):
     return out
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=["fixed-split", "balanced", "e4m3"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["fixed-split", "balanced", "e4m3", "head-groups"])
 def test_noalloc_matches_workspace_entry(pair):
     for case in pair:
         seed, B, T, Hq, Hkv, d, lens, kv = case

@@ -162,7 +162,7 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s o_s 2^(m_s - M) / L.
 // Lanes hold one split's statistics each (reduced with DPP) and slices of
 // the head dim.  Fixed splits: the context length, the statistics and the
-// partial rows of the first eight splits are requested together (all lie
+// partial rows of the first NB splits are requested together (all lie
 // inside the workspace), so the common case costs one round trip to memory;
 // entries of splits past the context are discarded.  Balanced shares: the
 // unit's first slot and its number of partials come from the prefix sums the
@@ -170,8 +170,9 @@ __device__ void finish_unit(const AttnParams &p, const UnitWork &w, const float 
 // all R rows at once).
 // NB: splits whose partial rows are requested at once (16 or 32 for many
 // fixed splits, where the grid has few waves: c5b's 32 splits 10.1 us with
-// 8, 9.0 with 16; else 8, whose fewer registers keep more waves resident:
-// balanced shares at B = 64 12.0 us against 15.6 with 16).
+// 8, 9.0 with 16; 4 under balanced shares, 8 otherwise: the fewer
+// registers keep more waves resident, balanced shares at B = 64 12.0 us
+// with 8 against 15.6 with 16).
 template <int D, int NB, int R>
 __global__ __launch_bounds__(256) void sv_attn_merge_kernel(AttnParams p)
 {
@@ -1426,6 +1427,17 @@ hipError_t launch_valu_d(const AttnParams &p, int kv, hipStream_t s)
 
 }  // namespace
 
+template <int D, int NB>
+void launch_merge_r(const AttnParams &p, int R, dim3 grid, hipStream_t stream)
+{
+    if (R == 1)
+        hipLaunchKernelGGL((sv_attn_merge_kernel<D, NB, 1>), grid, dim3(256), 0, stream, p);
+    else if (R == 2)
+        hipLaunchKernelGGL((sv_attn_merge_kernel<D, NB, 2>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((sv_attn_merge_kernel<D, NB, 4>), grid, dim3(256), 0, stream, p);
+}
+
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
 {
     if (!p.balanced && p.max_splits <= 1)
@@ -1438,25 +1450,26 @@ hipError_t launch_attn_merge(const AttnParams &p, hipStream_t stream)
     const int R = rows <= 8192 ? 1 : (rows <= 16384 ? 2 : 4);
     const long long waves = (long long)p.B * p.Hkv * ((p.TG + R - 1) / R);
     const dim3 grid((unsigned)((waves + 3) / 4));
+    // Partial rows requested at once: 4 under balanced shares (which cut a
+    // unit into two or three), whose smaller waves keep more of the grid
+    // resident (ragged 64-sequence batch: 12.0-12.2 -> 10.6-11.3 us in two
+    // traces), else 8.
+    const bool few = p.balanced != 0;
     if (p.d == 64) {
-        if (R == 1)
-            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 1>), grid, dim3(256), 0, stream, p);
-        else if (R == 2)
-            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 2>), grid, dim3(256), 0, stream, p);
+        if (few)
+            launch_merge_r<64, 4>(p, R, grid, stream);
         else
-            hipLaunchKernelGGL((sv_attn_merge_kernel<64, 8, 4>), grid, dim3(256), 0, stream, p);
+            launch_merge_r<64, 8>(p, R, grid, stream);
     } else if (!p.balanced && p.max_splits > 16) {
         const dim3 g1((unsigned)((rows + 3) / 4));
         hipLaunchKernelGGL((sv_attn_merge_kernel<128, 32, 1>), g1, dim3(256), 0, stream, p);
     } else if (!p.balanced && p.max_splits > 8) {
         const dim3 g1((unsigned)((rows + 3) / 4));
         hipLaunchKernelGGL((sv_attn_merge_kernel<128, 16, 1>), g1, dim3(256), 0, stream, p);
-    } else if (R == 1) {
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 1>), grid, dim3(256), 0, stream, p);
-    } else if (R == 2) {
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 2>), grid, dim3(256), 0, stream, p);
+    } else if (few) {
+        launch_merge_r<128, 4>(p, R, grid, stream);
     } else {
-        hipLaunchKernelGGL((sv_attn_merge_kernel<128, 8, 4>), grid, dim3(256), 0, stream, p);
+        launch_merge_r<128, 8>(p, R, grid, stream);
     }
     return hipGetLastError();
 }

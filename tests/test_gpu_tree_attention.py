@@ -101,6 +101,23 @@ def test_tree_at_70b_geometry(shape, kv):
         assert err <= TOL[a.kv_dtype]
 
 
+@pytest.mark.parametrize("shape,kv", [("wide5x2", "bf16"), ("binary3", "fp8")])
+def test_tree_head_pairs(shape, kv):
+    """Trees at a GQA ratio of 2 (at most 32 rows per KV head): balanced
+    shares then run two KV heads per workgroup (head pairs), each head's
+    rows with its own ancestor sets; ragged contexts so shares start and
+    end inside a pair's pages."""
+    par = W.tree_parents(W.TREE_SHAPES[shape])
+    N = par.shape[0]
+    B = 5
+    a = W.make_attn_from_lens(13, B, N, 16, 8, 128, [N, 900, 5000, 40, 2000], kv=kv, extra_blocks=2)
+    masks = oracle.tree_masks(np.broadcast_to(par, (B, N)))
+    for bps in (0, -1):
+        err = _err(a, _run_tree(a, masks, bps=bps), masks)
+        print("%s %s bps %d: max row rel err %.3e" % (shape, kv, bps, err))
+        assert err <= TOL[a.kv_dtype]
+
+
 def test_chain_sets_equal_the_chain_call():
     B, T = 3, 6
     a = W.make_attn_from_lens(9, B, T, 32, 8, 128, [6, 250, 1200], kv="bf16")

@@ -1,4 +1,5 @@
-"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU).
+"""Host code under AddressSanitizer, UndefinedBehaviorSanitizer and (the
+oracle's threads) ThreadSanitizer (no GPU).
 
 The CPU oracle (oracle/oracle.c) is built with a C driver that calls every
 entry point on small seeded inputs; the C ABI layer (capi.cpp: argument
@@ -38,6 +39,19 @@ def test_oracle_under_sanitizers(tmp_path):
     _run(["gcc", *flags, os.path.join(ROOT, "oracle", "oracle.c"), os.path.join(HERE, "oracle_driver.c"),
           "-lm", "-lpthread", "-o", exe], str(tmp_path))
     env = dict(os.environ, UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    out = _run([exe], str(tmp_path), env=env, timeout=300)
+    assert out.strip().endswith("ok")
+
+
+def test_oracle_threads_under_thread_sanitizer(tmp_path):
+    # the oracle splits rows and sequences over POSIX threads that write
+    # disjoint outputs; ThreadSanitizer checks that no two of them race
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "oracle_tsan")
+    _run(["gcc", "-O1", "-g", "-std=c11", "-fsanitize=thread", os.path.join(ROOT, "oracle", "oracle.c"),
+          os.path.join(HERE, "oracle_driver.c"), "-lm", "-lpthread", "-o", exe], str(tmp_path))
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
     out = _run([exe], str(tmp_path), env=env, timeout=300)
     assert out.strip().endswith("ok")
 

@@ -210,6 +210,8 @@ SamplePlan plan_sample(int B, int K, int V)
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * kCutCoarse * 8);
     pl.off_ent = off;  // typical acceptance: entropy sums per chunk
     off = align256(off + (size_t)B * (K + 1) * pl.nchunk * 8);
+    pl.off_gate = off;  // early exit: one flag per sequence
+    off = align256(off + (size_t)B * 4);
     pl.total = off;
     return pl;
 }
@@ -581,6 +583,7 @@ int sample_impl(const float *target_logits, const float *draft_probs, const int3
     p.sub_mass = reinterpret_cast<double *>(ws + pl.off_mass);
     p.row_cut = top_p ? ws + pl.off_cut : nullptr;
     p.cut_part = reinterpret_cast<unsigned long long *>(ws + pl.off_part);
+    p.gate = reinterpret_cast<int32_t *>(ws + pl.off_gate);
     p.B = B;
     p.K = K;
     p.V = V;

@@ -190,88 +190,6 @@ __device__ __forceinline__ T load_or(const T *ptr, size_t i, bool ok, T fill)
     return ok ? v : fill;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(SampleParams p)
-{
-    __shared__ float s_f[kNWs];
-    __shared__ double s_d[kNWs];
-    const int row = blockIdx.x / p.nchunk;
-    const int chunk = blockIdx.x - row * p.nchunk;
-    const int K = p.K, K1 = K + 1;
-    const int b = row / K1, i = row - b * K1;
-    const int base = chunk * kSampleChunk;
-    const int n = min(kSampleChunk, p.V - base);
-    float v[kPer];
-    load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
-    // x_i's own entries, fetched while the chunk streams in.
-    const bool rec = !p.tree && chunk == 0 && i < K;
-    RowX rx{0.0f, 0.0f};
-    if (rec) {
-        const int x = clamp_token(p.tokens[(size_t)b * K + i], p.V);
-        rx.lx = p.logits[(size_t)row * p.V + x];
-        rx.qx = p.probs ? p.probs[((size_t)b * K + i) * p.V + x] : 0.0f;
-    }
-    float mx = v[0];
-#pragma unroll
-    for (int k = 1; k < kPer; ++k)
-        mx = fmaxf(mx, v[k]);
-    const float M = block_max(mx, s_f);
-    const Temp tp = temp_of(p, b);
-    RowStat st;
-    st.m = M;
-    st.arg = 0;
-    st.z = 0.0;
-    if (tp.greedy) {
-        // first index of the maximum within the chunk
-        int first = 0x7FFFFFFF;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int e = VEC ? ((k >> 2) * kSampleThreads + (int)threadIdx.x) * 4 + (k & 3)
-                              : k * kSampleThreads + (int)threadIdx.x;
-            if (v[k] == M && e < first)
-                first = e;
-        }
-        first = wave_min_i32(first);
-        __shared__ int s_i[kNWs];
-        if ((threadIdx.x & 63) == 0)
-            s_i[threadIdx.x >> 6] = first;
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < kNWs; ++w)
-            first = min(first, s_i[w]);
-        st.arg = base + first;
-        if (p.typical && threadIdx.x == 0)
-            p.row_ent[(size_t)row * p.nchunk + chunk] = 0.0;
-    } else {
-        // exp((v - M) / T) = 2^((v - M) log2(e) / T) with the hardware exp2;
-        // the constant log2(e) / T enters as two floats, so the scaled
-        // argument carries one rounding; terms are summed in fp64.  The clamp
-        // sends -inf entries (and a chunk that is -inf throughout, where
-        // v - M is NaN) to a finite difference whose term is 0, whatever the
-        // sign of the low part of the constant.
-        double z = 0.0, ze = 0.0;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const float dv = fmaxf(v[k] - M, -3.0e38f);
-            const double w = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo));
-            z += w;
-            if (p.typical)  // entropy: sum of w * (l - m) / T, in nats
-                ze += w * ((double)dv * tp.inv);
-        }
-        st.z = block_sum(z, s_d);
-        if (p.typical) {
-            ze = block_sum(ze, s_d);
-            if (threadIdx.x == 0)
-                p.row_ent[(size_t)row * p.nchunk + chunk] = ze;
-        }
-    }
-    if (threadIdx.x == 0) {
-        static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
-        if (rec)
-            static_cast<RowX *>(p.row_x)[(size_t)b * K + i] = rx;
-    }
-}
-
 // Target probability p~_j of entry j from its logit, the row maximum M, 1/Z
 // and the temperature, to about one fp32 ulp: the base-2 argument
 // t = (l - M) log2(e) / T is formed in fp64 (l - M is exact there) and split
@@ -860,39 +778,46 @@ __device__ __forceinline__ void sub_chunk_masses(const float *lrow, const float 
     }
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
-{
-    __shared__ float s_M[16];
-    __shared__ double s_Z[16];   // 1 / (kept) row mass
-    __shared__ int s_A[16];
-    __shared__ float s_tau[16];
-    __shared__ double s_ratio[16];
-    __shared__ double s_th[16];
-    __shared__ int s_acc[16];
-    __shared__ int s_n;
-    __shared__ double s_part[kDecideMaxSpw][kNWs][2];
+// Per-sequence statistics and tests shared by the decide kernel and the
+// gated second rowstats launch (see launch_sample).
+struct SeqTests {
+    float M[16];
+    double Z[16];  // 1 / (kept) row mass
+    int A[16];
+    float tau[16];
+    double ratio[16];
+    double th[16];
+    int acc[16];
+    int n;
+};
 
-    // This workgroup covers sub-chunks sub0 .. sub0 + nsh - 1 of sequence b
-    // (the statistics and the tests are done once for all of them).
-    const int nsub = (p.V + kSampleSub - 1) / kSampleSub;
-    const int spw = p.spw;
-    const int ngrp = (nsub + spw - 1) / spw;
-    const int b = blockIdx.x / ngrp;
-    const int sub0 = (blockIdx.x - b * ngrp) * spw;
-    const int nsh = min(spw, nsub - sub0);
+// Merges the chunk statistics of rows 0 .. nrows-1 of sequence b into each
+// row's maximum, 1/Z (or the top-p cut's 1/kept mass), first argmax and cut,
+// and runs the tests of positions 0 .. ntests-1 (ntests <= nrows, rows past
+// nrows are not read), leaving the first rejection (or ntests) in sh.n.  The
+// arithmetic of a row or a test does not depend on nrows or ntests, so two
+// callers with different counts agree on every position both test.  Called
+// by every thread of the workgroup.
+__device__ __forceinline__ void seq_tests(const SampleParams &p, int b, const Temp &tp, int nrows, int ntests,
+                                          SeqTests &sh)
+{
+    float *s_M = sh.M;
+    double *s_Z = sh.Z;
+    int *s_A = sh.A;
+    float *s_tau = sh.tau;
+    double *s_ratio = sh.ratio;
+    double *s_th = sh.th;
+    int *s_acc = sh.acc;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int K = p.K, K1 = K + 1, V = p.V;
-
-    // 1. Row statistics of the K+1 rows of this sequence (one wave per row,
-    //    lanes over vocabulary chunks) and the draft tokens' entries, all
-    //    requested together.
-    const Temp tp = temp_of(p, b);
+    // 1. Row statistics of the first nrows rows of this sequence (one wave
+    //    per row, lanes over vocabulary chunks) and the draft tokens'
+    //    entries, all requested together.
     RowX rx{0.0f, 0.0f};
     float u = 0.0f;
     int x = 0;
-    if (tid < K) {
+    if (tid < ntests) {
         rx = static_cast<const RowX *>(p.row_x)[(size_t)b * K + tid];
         u = p.uniforms[(size_t)b * K1 + tid];
         x = clamp_token(p.tokens[(size_t)b * K + tid], V);
@@ -931,7 +856,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
             const int i = wave + j * kNWs;
             rs[j] = RowStat{-__builtin_inff(), 0x7FFFFFFF, 0.0};
             re[j] = 0.0;
-            if (i < K1 && lane < p.nchunk) {
+            if (i < nrows && lane < p.nchunk) {
                 rs[j] = static_cast<const RowStat *>(p.row_stats)[(size_t)(b * K1 + i) * p.nchunk + lane];
                 if (p.typical)
                     re[j] = p.row_ent[(size_t)(b * K1 + i) * p.nchunk + lane];
@@ -940,7 +865,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j) {
             const int i = wave + j * kNWs;
-            if (i >= K1)
+            if (i >= nrows)
                 break;  // uniform
             const float M = wave_max_f32(rs[j].m);
             double z = 0.0, sl = 0.0;
@@ -963,7 +888,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
             finish_row(i, M, Z, A, S);
         }
     } else {
-        for (int i = wave; i < K1; i += kNWs) {
+        for (int i = wave; i < nrows; i += kNWs) {
             const RowStat *st = static_cast<const RowStat *>(p.row_stats) + (size_t)(b * K1 + i) * p.nchunk;
             float mloc = -__builtin_inff();
             for (int c = lane; c < p.nchunk; c += kWave)
@@ -994,7 +919,7 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     __syncthreads();
     // 2. Acceptance tests u_i * q_i(x_i) < p~_i(x_i), or for typical
     //    acceptance p~_i(x_i) > min(eps, delta exp(-H_i)).
-    if (tid < K) {
+    if (tid < ntests) {
         const double a = target_prob(rx.lx, x, s_M[tid], s_Z[tid], tp, s_A[tid], s_tau[tid]);
         if (p.typical) {
             s_acc[tid] = (a > s_th[tid]) ? 1 : 0;
@@ -1007,16 +932,146 @@ __global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(Sample
     }
     __syncthreads();
     if (tid == 0) {
-        int n = K;
-        for (int i = 0; i < K; ++i)
+        int n = ntests;
+        for (int i = 0; i < ntests; ++i)
             if (!s_acc[i]) {
                 n = i;
                 break;
             }
-        s_n = n;
+        sh.n = n;
     }
     __syncthreads();
-    const int n = s_n;
+}
+
+// GATED: the launch covers rows row_lo .. row_lo + row_cnt - 1 of every
+// sequence and skips the sequences whose gate flag is 0; otherwise it covers
+// every row (and reads neither the range nor the flags).
+template <bool VEC, bool GATED>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_rowstats_kernel(SampleParams p)
+{
+    __shared__ float s_f[kNWs];
+    __shared__ double s_d[kNWs];
+    const int rloc = blockIdx.x / p.nchunk;
+    const int chunk = blockIdx.x - rloc * p.nchunk;
+    const int K = p.K, K1 = K + 1;
+    const int rc = GATED ? p.row_cnt : K1;
+    const int b = rloc / rc, i = (GATED ? p.row_lo : 0) + (rloc - b * rc);
+    const int row = b * K1 + i;
+    if (GATED && p.gate_r > 0 && p.gate[b] == 0)
+        return;  // uniform: a draft before this row was rejected, so the row never reaches the output
+    const int base = chunk * kSampleChunk;
+    const int n = min(kSampleChunk, p.V - base);
+    float v[kPer];
+    load_chunk<VEC>(p.logits + (size_t)row * p.V + base, n, -__builtin_inff(), v);
+    // x_i's own entries, fetched while the chunk streams in.
+    const bool rec = !p.tree && chunk == 0 && i < K;
+    RowX rx{0.0f, 0.0f};
+    if (rec) {
+        const int x = clamp_token(p.tokens[(size_t)b * K + i], p.V);
+        rx.lx = p.logits[(size_t)row * p.V + x];
+        rx.qx = p.probs ? p.probs[((size_t)b * K + i) * p.V + x] : 0.0f;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int k = 1; k < kPer; ++k)
+        mx = fmaxf(mx, v[k]);
+    const float M = block_max(mx, s_f);
+    const Temp tp = temp_of(p, b);
+    RowStat st;
+    st.m = M;
+    st.arg = 0;
+    st.z = 0.0;
+    if (tp.greedy) {
+        // first index of the maximum within the chunk
+        int first = 0x7FFFFFFF;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int e = VEC ? ((k >> 2) * kSampleThreads + (int)threadIdx.x) * 4 + (k & 3)
+                              : k * kSampleThreads + (int)threadIdx.x;
+            if (v[k] == M && e < first)
+                first = e;
+        }
+        first = wave_min_i32(first);
+        __shared__ int s_i[kNWs];
+        if ((threadIdx.x & 63) == 0)
+            s_i[threadIdx.x >> 6] = first;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kNWs; ++w)
+            first = min(first, s_i[w]);
+        st.arg = base + first;
+        if (p.typical && threadIdx.x == 0)
+            p.row_ent[(size_t)row * p.nchunk + chunk] = 0.0;
+    } else {
+        // exp((v - M) / T) = 2^((v - M) log2(e) / T) with the hardware exp2;
+        // the constant log2(e) / T enters as two floats, so the scaled
+        // argument carries one rounding; terms are summed in fp64.  The clamp
+        // sends -inf entries (and a chunk that is -inf throughout, where
+        // v - M is NaN) to a finite difference whose term is 0, whatever the
+        // sign of the low part of the constant.
+        double z = 0.0, ze = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const float dv = fmaxf(v[k] - M, -3.0e38f);
+            const double w = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(dv, tp.c_hi, dv * tp.c_lo));
+            z += w;
+            if (p.typical)  // entropy: sum of w * (l - m) / T, in nats
+                ze += w * ((double)dv * tp.inv);
+        }
+        st.z = block_sum(z, s_d);
+        if (p.typical) {
+            ze = block_sum(ze, s_d);
+            if (threadIdx.x == 0)
+                p.row_ent[(size_t)row * p.nchunk + chunk] = ze;
+        }
+    }
+    if (threadIdx.x == 0) {
+        static_cast<RowStat *>(p.row_stats)[(size_t)row * p.nchunk + chunk] = st;
+        if (rec)
+            static_cast<RowX *>(p.row_x)[(size_t)b * K + i] = rx;
+    }
+}
+
+// Early exit, between the two row-statistics launches: one workgroup per
+// sequence runs the tests of positions 0 .. gate_r-1 from the first gate_r
+// rows (as the decide pass will, with the same arithmetic) and flags the
+// sequences that accepted all of them, whose later rows are still needed.
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_gate_kernel(SampleParams p)
+{
+    __shared__ SeqTests sh;
+    const int b = blockIdx.x;
+    seq_tests(p, b, temp_of(p, b), p.gate_r, p.gate_r, sh);
+    if (threadIdx.x == 0)
+        p.gate[b] = sh.n >= p.gate_r ? 1 : 0;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void sv_sample_decide_kernel(SampleParams p)
+{
+    __shared__ SeqTests sh;
+    __shared__ double s_part[kDecideMaxSpw][kNWs][2];
+
+    // This workgroup covers sub-chunks sub0 .. sub0 + nsh - 1 of sequence b
+    // (the statistics and the tests are done once for all of them).
+    const int nsub = (p.V + kSampleSub - 1) / kSampleSub;
+    const int spw = p.spw;
+    const int ngrp = (nsub + spw - 1) / spw;
+    const int b = blockIdx.x / ngrp;
+    const int sub0 = (blockIdx.x - b * ngrp) * spw;
+    const int nsh = min(spw, nsub - sub0);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int K = p.K, K1 = K + 1, V = p.V;
+
+    const Temp tp = temp_of(p, b);
+    seq_tests(p, b, tp, K1, K, sh);
+    const int n = sh.n;
+    const float *s_M = sh.M;
+    const double *s_Z = sh.Z;
+    const int *s_A = sh.A;
+    const float *s_tau = sh.tau;
+    const double *s_ratio = sh.ratio;
+    const double *s_th = sh.th;
     const bool residual = n < K && !p.typical;  // typical: the draw is from p~_n itself
     const float M = s_M[n];
     const double invZ = s_Z[n];
@@ -1746,14 +1801,44 @@ hipError_t launch_sample(const SampleParams &p0, hipStream_t stream)
     p.spw = decide_spw(nsub * p.B, p.vec4 ? (const void *)sv_sample_decide_kernel<true>
                                           : (const void *)sv_sample_decide_kernel<false>,
                        p.vec4 ? 0 : 1, stream);
+    const int K1 = p.K + 1;
+    p.row_lo = 0;
+    p.row_cnt = K1;
+    p.gate_r = 0;
+    // Early exit ("50 | Speculative Decoding" 3.1: verification stops at the
+    // first rejected draft, so the target rows after it never reach the
+    // output): for large batches the row statistics run as two launches,
+    // rows 0 .. R-1 of every sequence, then (after a one-workgroup-per-
+    // sequence launch that flags the sequences whose drafts 0 .. R-1 were all
+    // accepted) rows R .. K of the flagged sequences, when no output needs
+    // every row (acceptance ratios, typical acceptance, top-p cuts).  The
+    // decide pass uses the statistics only of rows up to the first rejection
+    // (those of a skipped row may be stale and never reach the output).
+    const bool gate = !p.tree && !p.typical && !p.row_cut && !p.accept_prob && !p.threshold_out && K1 >= 4 &&
+                      (double)p.B * K1 * p.V * 4.0 >= kGateMinBytes;
+    const int R = K1 / 2;
+    SampleParams pa = p, pb = p;
+    pa.row_cnt = R;
+    pb.row_lo = R;
+    pb.row_cnt = K1 - R;
+    pb.gate_r = R;
+    const dim3 gg((unsigned)p.B);
     const dim3 block(kSampleThreads);
-    const dim3 g1((unsigned)(p.nchunk * p.B * (p.K + 1)));
+    const dim3 g1((unsigned)(p.nchunk * p.B * K1));
+    const dim3 ga((unsigned)(p.nchunk * p.B * R));
+    const dim3 gb((unsigned)(p.nchunk * p.B * (K1 - R)));
     const dim3 g2((unsigned)(((nsub + p.spw - 1) / p.spw) * p.B));
     const dim3 g3((unsigned)p.B);
-    const dim3 gc((unsigned)(p.B * (p.K + 1)));
+    const dim3 gc((unsigned)(p.B * K1));
     const dim3 gh = g1;
     if (p.vec4) {
-        hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
+        if (gate) {
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<true, true>), ga, block, 0, stream, pa);
+            hipLaunchKernelGGL(sv_sample_gate_kernel, gg, block, 0, stream, pb);
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<true, true>), gb, block, 0, stream, pb);
+        } else {
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<true, false>), g1, block, 0, stream, p);
+        }
         if (p.row_cut) {
             hipLaunchKernelGGL(sv_sample_cut_hist_kernel<true>, gh, block, 0, stream, p);
             hipLaunchKernelGGL(sv_sample_cut_kernel<true>, gc, dim3(kCutThreads), 0, stream, p);
@@ -1761,7 +1846,13 @@ hipError_t launch_sample(const SampleParams &p0, hipStream_t stream)
         hipLaunchKernelGGL(sv_sample_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
-        hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
+        if (gate) {
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<false, true>), ga, block, 0, stream, pa);
+            hipLaunchKernelGGL(sv_sample_gate_kernel, gg, block, 0, stream, pb);
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<false, true>), gb, block, 0, stream, pb);
+        } else {
+            hipLaunchKernelGGL((sv_sample_rowstats_kernel<false, false>), g1, block, 0, stream, p);
+        }
         if (p.row_cut) {
             hipLaunchKernelGGL(sv_sample_cut_hist_kernel<false>, gh, block, 0, stream, p);
             hipLaunchKernelGGL(sv_sample_cut_kernel<false>, gc, dim3(kCutThreads), 0, stream, p);
@@ -1781,18 +1872,21 @@ hipError_t launch_sample_tree(const SampleParams &p0, hipStream_t stream)
                        p.vec4 ? 2 : 3, stream);
     const dim3 block(kSampleThreads);
     const int N = p.K + 1;
+    p.row_lo = 0;  // every row of every sequence
+    p.row_cnt = N;
+    p.gate_r = 0;
     const dim3 g1((unsigned)(p.nchunk * p.B * N));
     const dim3 gl((unsigned)(p.nchunk * p.B));
     const dim3 g2((unsigned)(((nsub + p.spw - 1) / p.spw) * p.B));
     const dim3 g3((unsigned)p.B);
     if (p.vec4) {
-        hipLaunchKernelGGL(sv_sample_rowstats_kernel<true>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL((sv_sample_rowstats_kernel<true, false>), g1, block, 0, stream, p);
         for (int r = 2; r <= p.tree_max_children; ++r)
             hipLaunchKernelGGL(sv_tree_level_kernel<true>, gl, dim3(kSampleThreads * 4), 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<true>, g2, block, 0, stream, p);
         hipLaunchKernelGGL(sv_sample_pick_kernel<true>, g3, block, 0, stream, p);
     } else {
-        hipLaunchKernelGGL(sv_sample_rowstats_kernel<false>, g1, block, 0, stream, p);
+        hipLaunchKernelGGL((sv_sample_rowstats_kernel<false, false>), g1, block, 0, stream, p);
         for (int r = 2; r <= p.tree_max_children; ++r)
             hipLaunchKernelGGL(sv_tree_level_kernel<false>, gl, dim3(kSampleThreads * 4), 0, stream, p, r);
         hipLaunchKernelGGL(sv_tree_decide_kernel<false>, g2, block, 0, stream, p);

@@ -131,6 +131,11 @@ constexpr int kSampleSub = 1024;    // entries per sub-chunk (unit of the draw's
 constexpr int kSampleThreads = 256;
 constexpr int kDecideMaxSpw = 16;    // sub-chunks one decide workgroup covers at most
 constexpr int kMaxSampleChunks = 2048;  // V <= 2048 * 8192
+// Chain sampler, early exit: at least this many bytes of target rows (and
+// no output that needs every row) split the row statistics in two launches,
+// the second reading only the sequences that accepted every draft the first
+// half of the rows tests (see launch_sample).
+constexpr double kGateMinBytes = 64.0 * 1024 * 1024;
 
 struct SampleParams {
     const float *logits;     // [B][K+1][V]
@@ -162,11 +167,14 @@ struct SampleParams {
     int B, K, V, nchunk;
     int vec4;                // rows start 16-byte aligned and V % 4 == 0
     int spw;                 // chain decide: consecutive sub-chunks per workgroup (1..kDecideMaxSpw; set by launch_sample)
+    int row_lo, row_cnt;     // rowstats: rows row_lo .. row_lo + row_cnt - 1 of every sequence (set by the launchers)
+    int gate_r;              // rowstats: > 0 reads only the sequences whose gate flag is set
+    int32_t *gate;           // [B] 1 iff drafts 0 .. R-1 are all accepted (early exit, see launch_sample)
 };
 
 struct SamplePlan {
     int nchunk;
-    size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, off_ent, total;
+    size_t off_state, off_stats, off_rowx, off_mass, off_cut, off_part, off_ent, off_gate, total;
 };
 
 constexpr size_t kSeqStateBytes = 64;  // workspace bytes per sequence of the decide -> pick state

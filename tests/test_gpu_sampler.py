@@ -152,3 +152,54 @@ def test_gpu_mean_tokens_per_round():
     se = np.sqrt(((vals ** 2 * probs).sum() - closed ** 2) / tau.size)
     print("mean tau %.5f closed form %.5f (se %.2e)" % (tau.mean(), closed, se))
     assert abs(tau.mean() - closed) < 4 * se
+
+
+# Early exit (large batches, no acceptance-ratio output): the row statistics
+# run as two launches and the second skips the sequences that rejected a
+# draft among the first half of the positions, so rows after a sequence's
+# first rejection are not summarised.  The result must be that of the full
+# pass: bit for bit against the same call with acceptance ratios requested
+# (which reads every row), and against the oracle.  The workspace starts
+# filled with garbage, and a second call on other inputs runs over the
+# statistics the first call left, so a skipped row's stale statistics can
+# never leak into the output.
+EARLY = [
+    # (seed, B, K, V, sigma, noise): B * (K+1) * V * 4 >= 64 MiB
+    (21, 64, 7, 32768, 3.0, 1.0),
+    (22, 64, 7, 32768, 0.5, 0.1),    # high acceptance: most sequences need the later rows
+    (23, 64, 7, 32768, 3.0, 4.0),    # low acceptance: most skip them
+    (24, 32, 5, 99001, 2.0, 1.5),    # scalar path (V not a multiple of 4)
+    (25, 16, 15, 65536, 1.0, 0.5),   # K = 15
+    (26, 128, 3, 40000, 2.0, 1.0),   # K = 3: rows 0-1, then 2-3
+]
+
+
+def _sample_no_ratios(s, t, ws):
+    d = dev()
+    n = torch.full((s.B,), -7, dtype=torch.int32, device=d)
+    toks = torch.full((s.B, s.K + 1), -7, dtype=torch.int32, device=d)
+    sv.spec_verify_sample(t["logits"], t["probs"], t["tokens"], t["u"], n, toks, ws)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), toks.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", EARLY, ids=[str(c[0]) for c in EARLY])
+def test_early_exit_parity(case):
+    seed, B, K, V, sigma, noise = case
+    assert B * (K + 1) * V * 4 >= 64 * 1024 * 1024
+    s = W.make_sample_from_params(seed, B, K, V, sigma, noise)
+    t = upload_sample(s)
+    ws = sv.alloc_workspace(sv.sample_workspace_size(B, K, V), dev())
+    ws.fill_(0xFF)  # NaN statistics wherever a row is not summarised
+    n_e, toks_e = _sample_no_ratios(s, t, ws)
+    n_f, toks_f, _ = run_sample(s, t=t, ws=ws)  # acceptance ratios requested: every row summarised
+    assert np.array_equal(n_e, n_f) and np.array_equal(toks_e, toks_f)
+    mism, flagged, _ = compare_sampler(s, n_e, toks_e)
+    print("case %d: mean accepted %.2f of %d, mismatches=%d flagged=%d" % (seed, float(n_e.mean()), K, mism, flagged))
+    assert mism == 0
+    # another batch over the statistics this one left behind
+    s2 = W.make_sample_from_params(seed + 100, B, K, V, sigma, noise)
+    t2 = upload_sample(s2)
+    n2, toks2 = _sample_no_ratios(s2, t2, ws)
+    mism2, _, _ = compare_sampler(s2, n2, toks2)
+    assert mism2 == 0

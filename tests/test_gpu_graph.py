@@ -135,6 +135,29 @@ def test_graph_replay_sampler_variants():
     _replays_match(typical, outputs, dev)
 
 
+def test_graph_replay_sampler_early_exit():
+    """A batch large enough for the two-stage row statistics (64 sequences x
+    8 rows x 32768 entries = 64 MiB): the per-sequence gate flags and the
+    statistics of skipped rows are left in the shared workspace by the eager
+    call on the other inputs between replays."""
+    dev = torch.device("cuda", 0)
+    ss = [W.make_sample_from_params(41 + i, 64, 7, 32768, 3.0, 0.5 + 1.5 * i) for i in range(2)]
+    assert ss[0].B * (ss[0].K + 1) * ss[0].V * 4 >= 64 * 1024 * 1024
+    ts = [upload_sample(s) for s in ss]
+    s = ss[0]
+    ws = sv.alloc_workspace(sv.sample_workspace_size(s.B, s.K, s.V), dev)
+
+    def outputs():
+        return (torch.empty(s.B, dtype=torch.int32, device=dev),
+                torch.empty((s.B, s.K + 1), dtype=torch.int32, device=dev))
+
+    def chain(o, stream, which):
+        t = ts[which]
+        sv.spec_verify_sample(t["logits"], t["probs"], t["tokens"], t["u"], o[0], o[1], ws, stream=stream)
+
+    _replays_match(chain, outputs, dev)
+
+
 def test_graph_replay_tree_sampler_and_commit():
     dev = torch.device("cuda", 0)
     par = W.tree_parents(W.TREE_SHAPES["wide5x2"])

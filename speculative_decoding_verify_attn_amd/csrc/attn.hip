@@ -580,15 +580,18 @@ struct MfmaShape {
     // page ids a balanced share holds (one share per compute unit for 8 waves)
     static constexpr int PCAP_BAL = NW == 8 ? kBalMaxShareOne : kBalMaxShare;
     static constexpr int RGW = (RG + HV - 1) / HV;    // row tiles per wave
-    // E4M3, d = 128, an even number of row tiles per wave: PV runs on the
-    // 32x32x16 matrix instruction (see mfma_segment).
-    static constexpr bool PV32 = FP8 && D == 128 && RGW % 2 == 0;
-    // PV32: the V slice moves as two 16-byte copies per page (key-major rows
-    // of 128 bytes) and each lane reads its keys' dims from other lanes'
-    // bytes once the copying wave's wait (and, with shared pages, the
-    // barrier) has passed; otherwise each lane reads back only its own copies.
-    static constexpr int NVI = PV32 ? 2 : PG::NVI;            // V copies per page
-    static constexpr int VB = PV32 ? 16 : PG::VBYTES;          // V copy width
+    // d = 128 and an even number of row tiles per wave, for E4M3 and for
+    // bf16 from four tiles per wave on: PV runs on the 32x32x16 matrix
+    // instruction (see mfma_segment).
+    static constexpr bool PV32 = D == 128 && RGW % 2 == 0 && (FP8 || RGW >= 4);
+    // PV32: the V slice moves in key-major rows of D * EB bytes (16-byte
+    // copies: two per page for E4M3, four for bf16), and each lane reads its
+    // keys' dims from other lanes' bytes once the copying wave's wait (and,
+    // with shared pages, the barrier) has passed; otherwise each lane reads
+    // back only its own copies.
+    static constexpr int VLPR = D * PG::EB / 16;                // PV32: lanes per key row of a copy
+    static constexpr int NVI = PV32 ? PG::PT / 1024 : PG::NVI;  // V copies per page
+    static constexpr int VB = PV32 ? 16 : PG::VBYTES;           // V copy width
     static constexpr int NI = PG::NKI + NVI + (FP8 ? 2 : 0);  // copies per page
     // Ring stages per page stream: about 8 KB of copies in flight behind the
     // page being computed (shared pages: one page behind the page being
@@ -801,8 +804,9 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         k_voff[i] = head_off + r * slot_stride + ((lane % PG::KPS) ^ PG::kswz(i * PG::KSPC + r)) * 16;
     }
     // V copy: lane -> (dims NDT*l16.., key 4*q4 + copy / VPK); PV32: lane ->
-    // (bytes 16*(l%8) .. +15 of key l/8 + 8*copy)
-    const int v_voff = PV32 ? head_off + (lane >> 3) * slot_stride + 16 * (lane & 7)
+    // (bytes 16*(l%VLPR) .. +15 of key l/VLPR + (64/VLPR)*copy)
+    constexpr int VLPR = SH::VLPR;
+    const int v_voff = PV32 ? head_off + (lane / VLPR) * slot_stride + 16 * (lane % VLPR)
                             : head_off + 4 * q4 * slot_stride + l16 * PG::VKB;
     const uint32_t ring_lds =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(smem) + ring_id * SH::RSTRIDE;
@@ -829,7 +833,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 #pragma unroll
         for (int n = 0; n < SH::NVI; ++n)
             dma_to_lds<SH::VB>(lds + PG::PT + n * 64 * SH::VB, dv, v_voff,
-                               PV32 ? n * 8 * slot_stride
+                               PV32 ? n * (64 / VLPR) * slot_stride
                                     : (n / PG::VPK) * slot_stride + (n % PG::VPK) * PG::VBYTES);
         if constexpr (FP8) {
             const int soff = __builtin_amdgcn_readfirstlane(ph) * 4;
@@ -883,12 +887,19 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         for (int i = 0; i < PG::NKI; ++i)
             kraw[i] = *reinterpret_cast<const uint4 *>(st + PG::kread(l16, 4 * i + q4));
         uint32_t vr[4][NDT / 2];  // [key j][dims 2w, 2w+1 as bf16]
-        uint32_t vc[8];           // PV32: E4M3 codes of dims 4i..4i+3 (i = l%32) of key 8*(l/32) + j
+        // PV32: dims 4i..4i+3 (i = l%32) of key 8*(l/32) + j, as E4M3 codes
+        // (vc) or as two bf16 pairs (vb)
+        uint32_t vc[8];
+        uint2 vb[8];
         if constexpr (PV32) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vc[j] = *reinterpret_cast<const uint32_t *>(st + PG::PT + (8 * (lane >> 5) + j) * 128 +
-                                                            4 * (lane & 31));
+            for (int j = 0; j < 8; ++j) {
+                const unsigned char *vrow = st + PG::PT + (8 * (lane >> 5) + j) * (D * EB);
+                if constexpr (FP8)
+                    vc[j] = *reinterpret_cast<const uint32_t *>(vrow + 4 * (lane & 31));
+                else
+                    vb[j] = *reinterpret_cast<const uint2 *>(vrow + 8 * (lane & 31));
+            }
         } else if constexpr (PG::VBYTES == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -944,8 +955,15 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         if (key0 + kBlock > L) {  // wave-uniform: only a sequence's last page
             if constexpr (PV32) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    vc[j] &= slot_keep(true, key0 + 8 * (lane >> 5) + j, L);
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t keep = slot_keep(true, key0 + 8 * (lane >> 5) + j, L);
+                    if constexpr (FP8) {
+                        vc[j] &= keep;
+                    } else {
+                        vb[j].x &= keep;
+                        vb[j].y &= keep;
+                    }
+                }
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -962,7 +980,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             uint2 y[8];  // per key: dims (4i, 4i+1), (4i+2, 4i+3) as bf16 pairs
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                y[j] = e4m3x4_to_bf16x4(vc[j]);
+                y[j] = FP8 ? e4m3x4_to_bf16x4(vc[j]) : vb[j];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 uint32_t w[4];

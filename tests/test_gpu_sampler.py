@@ -203,3 +203,33 @@ def test_early_exit_parity(case):
     n2, toks2 = _sample_no_ratios(s2, t2, ws)
     mism2, _, _ = compare_sampler(s2, n2, toks2)
     assert mism2 == 0
+
+
+def test_early_exit_with_temperatures():
+    """Temperature alone keeps the early exit: a mix of temperatures, greedy
+    rows (T = 0) among them, on the two-stage path against the full pass and
+    the oracle."""
+    B, K, V = 64, 7, 32768
+    s = W.make_sample_from_params(27, B, K, V, 3.0, 1.0)
+    rng = np.random.default_rng(28)
+    temp = rng.choice(np.array([0.0, 0.4, 0.8, 1.0, 1.6], np.float32), size=B)
+    arg = np.argmax(s.target_logits, axis=-1)  # greedy rows accept only the argmax
+    take = rng.random((B, K)) < 0.7
+    s = W.SampleInputs(s.target_logits, s.draft_probs,
+                       np.where(take, arg[:, :K], s.draft_tokens).astype(np.int32), s.uniforms)
+    t = upload_sample(s)
+    d = dev()
+    ws = sv.alloc_workspace(sv.sample_workspace_size(B, K, V), d)
+    ws.fill_(0xFF)
+    tt = torch.from_numpy(temp).to(d)
+    n = torch.full((B,), -7, dtype=torch.int32, device=d)
+    toks = torch.full((B, K + 1), -7, dtype=torch.int32, device=d)
+    sv.spec_verify_sample(t["logits"], t["probs"], t["tokens"], t["u"], n, toks, ws, temperature=tt)
+    torch.cuda.synchronize()
+    n_e, toks_e = n.cpu().numpy(), toks.cpu().numpy()
+    n_f, toks_f, _ = run_sample(s, t=t, ws=ws, temperature=temp)
+    assert np.array_equal(n_e, n_f) and np.array_equal(toks_e, toks_f)
+    mism, flagged, _ = compare_sampler(s, n_e, toks_e, temperature=temp)
+    print("mean accepted %.2f of %d, mismatches=%d flagged=%d" % (float(n_e.mean()), K, mism, flagged))
+    assert mism == 0
+    assert 0 < (n_e >= K // 2 + K % 2).sum() < B  # both sides of the gate are exercised

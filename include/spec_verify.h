@@ -232,6 +232,10 @@ int spec_verify_probe_read(const void *src, size_t bytes, float *sink, size_t si
  * num_accepted [B] int32; out_tokens [B,K+1] int32; accept_prob [B,K] float32
  * (optional, NULL to skip) receives min(1, p_i(x_i)/q_i(x_i)) for every i.
  * 1 <= K <= 15; V >= 1.  workspace as for attention.
+ * Rows after a sequence's first rejection cannot change any output; when the
+ * batch holds at least 64 MiB of target rows and accept_prob is NULL (and no
+ * top-p cut is asked for), the rows after a rejection among the first
+ * (K+1)/2 drafts are not read at all.
  * ------------------------------------------------------------------------ */
 /* Typical acceptance ("50 | Speculative Decoding" 9.1; "KV Cache +
  * Speculative Decoding" 8.2 and Q18): NOT exact.  Draft x_i is accepted iff

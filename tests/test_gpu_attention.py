@@ -43,7 +43,27 @@ SMALL = [
     (22, 2, 16, 64, 8, 128, [800, 100], "fp8"),         # E4M3, T*G = 128
     (23, 2, 11, 32, 4, 64, [333, 11], "fp8"),           # E4M3, d=64, T*G = 88
     (24, 2, 13, 64, 8, 128, [250, 140], "f32"),         # fp32 (vector ALU), T*G = 104
+    # E4M3, d = 128, four row tiles (shared pages, 32x32 PV)
+    (25, 3, 8, 16, 2, 128, [5000, 17, 1200], "fp8"),    # two KV heads, T*G = 64, ragged
+    (26, 2, 7, 24, 3, 128, [900, 30], "fp8"),           # odd Hkv, T*G = 56
+    (27, 1, 7, 64, 8, 128, [7], "fp8"),                 # one page: most page streams get none
 ]
+
+
+# E4M3 with four row tiles under forced fixed splits: more splits than the
+# merge requests at once, a split of one page per stream, and splits past
+# the end of the short sequence, over a garbage-filled workspace.
+@pytest.mark.parametrize("bps", [4, 8, 64])
+def test_e4m3_four_tiles_forced_splits(bps):
+    a = W.make_attn_from_lens(28, 2, 7, 64, 8, 128, [2600, 50], kv="fp8", extra_blocks=2)
+    t = upload_attn(a)
+    ws = sv.alloc_workspace(sv.attn_workspace_size(a.B, a.T, a.Hq, a.Hkv, a.d, a.max_blocks, bps),
+                            torch.device("cuda", 0))
+    ws.fill_(0xFF)
+    out = run_attn(a, t, blocks_per_split=bps, ws=ws)
+    err = _check(a, out)
+    print("bps %d: max row rel err %.3e" % (bps, err))
+    assert err <= TOL[a.kv_dtype]
 
 
 def _check(a, out, rows=None):

@@ -976,11 +976,30 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         }
         short4v va4[PV32 ? 1 : NDT];
         bf16x8 va32[PV32 ? 4 : 1];
-        if constexpr (PV32) {
+        if constexpr (PV32 && FP8) {
+            // E4M3: one byte permute puts dims (4i, 4i+1) -- or (4i+2, 4i+3)
+            // -- of keys 2w and 2w+1 side by side, so the two conversions of
+            // its halves are already A-operand pairs (key 2w low, 2w+1 high)
+            // of dim tiles u and u+1: 8 permutes per page instead of 16 after
+            // converting.
+            uint32_t w[4][4];  // [dim tile u][key pair w2]
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const uint32_t zl = perm_b32(vc[2 * w2 + 1], vc[2 * w2], 0x05010400u);
+                const uint32_t zh = perm_b32(vc[2 * w2 + 1], vc[2 * w2], 0x07030602u);
+                w[0][w2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(zl, 1.0f, false));
+                w[1][w2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(zl, 1.0f, true));
+                w[2][w2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(zh, 1.0f, false));
+                w[3][w2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(zh, 1.0f, true));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                va32[u] = __builtin_bit_cast(bf16x8, make_uint4(w[u][0], w[u][1], w[u][2], w[u][3]));
+        } else if constexpr (PV32) {
             uint2 y[8];  // per key: dims (4i, 4i+1), (4i+2, 4i+3) as bf16 pairs
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                y[j] = FP8 ? e4m3x4_to_bf16x4(vc[j]) : vb[j];
+                y[j] = vb[j];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 uint32_t w[4];

@@ -766,13 +766,18 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
     // tile t, row l16).  bf16 storage gets its row sums from one extra MFMA
     // with an all-ones A operand; E4M3 storage scales P per page, so it sums
     // P on the VALU.
-    float m[RGW], lpart[RGW];
+    // mth = m + kSlack and nms = -(m, or 0 while m is -inf) change only with
+    // m (in the rare rescale branch), so they are kept rather than recomputed
+    // for every page.
+    float m[RGW], mth[RGW], nms[RGW], lpart[RGW];
     floatx4 lsum[RGW];
     floatx4 acc[PV32 ? 1 : NDT][PV32 ? 1 : RGW];
     floatx16 acc32[PV32 ? 4 : 1][NP];  // PV32: O^T of dim tile u, row pair pp
 #pragma unroll
     for (int rt = 0; rt < RGW; ++rt) {
         m[rt] = ninf;
+        mth[rt] = ninf + kSlack;
+        nms[rt] = -0.0f;
         lpart[rt] = 0.0f;
         lsum[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -1049,7 +1054,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
 #pragma unroll
         for (int rt = 0; rt < RGW; ++rt) {
             mloc[rt] = ksc * fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
-            need = need || (mloc[rt] > m[rt] + kSlack);
+            need = need || (mloc[rt] > mth[rt]);
         }
         if (__builtin_expect(__ballot(need) != 0, 0)) {
             __asm__ volatile("" ::: "memory");  // keep this block a real branch
@@ -1061,6 +1066,8 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
                 const float mnew = fmaxf(m[rt], mx);
                 const float alpha = (mnew == ninf) ? 1.0f : __builtin_amdgcn_exp2f(m[rt] - mnew);
                 m[rt] = mnew;
+                mth[rt] = mnew + kSlack;
+                nms[rt] = -((mnew == ninf) ? 0.0f : mnew);
                 lpart[rt] *= alpha;
                 lsum[rt] *= alpha;
                 if constexpr (PV32) {
@@ -1079,11 +1086,10 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         short4v pb[RGW];
 #pragma unroll
         for (int rt = 0; rt < RGW; ++rt) {
-            const float msafe = (m[rt] == ninf) ? 0.0f : m[rt];
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], ksc, -msafe));
+                pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], ksc, nms[rt]));
             if constexpr (FP8)
                 lpart[rt] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
             pb[rt] = __builtin_bit_cast(short4v, make_uint2(f32x2_to_bf16x2(pr[0] * vsc, pr[1] * vsc),

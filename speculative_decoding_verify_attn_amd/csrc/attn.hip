@@ -864,7 +864,9 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
             issue(k, clamp_block(first[k], p.num_blocks));
     __syncthreads();  // s_pages ready
 
-    for (int k = 0; k < nsteps; ++k) {
+    // soff: byte offset of page k's ring stage, (k % NS) * STAGE, carried from
+    // step to step (a wave-uniform scalar) instead of divided out per page
+    for (int k = 0, soff = 0; k < nsteps; ++k, soff = (soff == (NS - 1) * PG::STAGE) ? 0 : soff + PG::STAGE) {
         if constexpr (SHARE) {
             // Page k has landed (pages k+1 .. k+NS-2 may stay in flight);
             // after the barrier the partner may read it, and both waves are
@@ -884,7 +886,7 @@ __device__ __forceinline__ void mfma_segment(const AttnParams &p, unsigned char 
         }
         const int pg = pw + k * nstr;
         const int key0 = (blk_begin + pg) * kBlock;
-        const unsigned char *st = ring + (k % NS) * PG::STAGE;
+        const unsigned char *st = ring + soff;
 
         // 1. Read back this lane's K operands and V bytes of the page.
         uint4 kraw[PG::NKI];

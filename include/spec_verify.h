@@ -235,7 +235,7 @@ int spec_verify_probe_read(const void *src, size_t bytes, float *sink, size_t si
  * Rows after a sequence's first rejection cannot change any output; when the
  * batch holds at least 64 MiB of target rows and accept_prob is NULL (and no
  * top-p cut is asked for), the rows after a rejection among the first
- * (K+1)/2 drafts are not read at all.
+ * max(2, 3(K+1)/8) drafts are not read at all.
  * ------------------------------------------------------------------------ */
 /* Typical acceptance ("50 | Speculative Decoding" 9.1; "KV Cache +
  * Speculative Decoding" 8.2 and Q18): NOT exact.  Draft x_i is accepted iff

@@ -1441,6 +1441,8 @@ __global__ __launch_bounds__(kSampleThreads * 4) void sv_tree_level_kernel(Sampl
     __shared__ int s_par[kTreeMaxN], s_pv[kTreeMaxN], s_kid[kTreeMaxN], s_prev[kTreeMaxN];
     __shared__ int s_nk;
     __shared__ double s_part[kLevelWaves][kTreeMaxN];
+    __shared__ float s_M[kTreeMaxN];                 // per child of the rank: parent row maximum,
+    __shared__ double s_iZ[kTreeMaxN], s_C[kTreeMaxN];  // its 1/Z, and the child's C
     const int N = p.K + 1;
     const int chunk = blockIdx.x % p.nchunk;
     const int b = blockIdx.x / p.nchunk;
@@ -1480,37 +1482,20 @@ __global__ __launch_bounds__(kSampleThreads * 4) void sv_tree_level_kernel(Sampl
     const Temp t1 = temp_from_inv(false, 1.0);
     const bool fast = p.nchunk <= kWave;  // one chunk statistic per lane
     const bool hp = rank > 2;             // the previous sibling has its own test (rank >= 2)
-    // Child j's loads, all requested together; the next child's are in
+    // Child j's slices, all requested together; the next child's are in
     // flight while this one is summed.
     struct Fetch {
-        RowStat st;
-        double zp, cp;
         float v[8], w[8];
-        int c, prev, row;
     };
     auto fetch = [&](int j, Fetch &f) {
-        f.c = __builtin_amdgcn_readfirstlane(s_kid[j]);
-        f.prev = __builtin_amdgcn_readfirstlane(s_prev[j]);
-        f.row = b * N + __builtin_amdgcn_readfirstlane(s_par[f.c]);
-        const int pn = hp ? f.prev : f.c;  // (c: a valid address when unused)
-        f.st = load_or(static_cast<const RowStat *>(p.row_stats), (size_t)f.row * p.nchunk + lane,
-                       fast && lane < p.nchunk, RowStat{-__builtin_inff(), 0, 0.0});
-        f.zp = load_or(p.coefs, ((size_t)b * N + pn) * p.nchunk + lane, fast && hp && lane < p.nchunk, 0.0);
-        f.cp = load_or(p.tree_c, (size_t)b * N + pn, hp, 1.0);
-        load_slice<VEC>(p.logits + (size_t)f.row * p.V, base, n, -__builtin_inff(), f.v);
-        load_slice<VEC>(p.probs + (size_t)f.row * p.V, base, n, 0.0f, f.w);
+        const int c = __builtin_amdgcn_readfirstlane(s_kid[j]);
+        const int row = b * N + __builtin_amdgcn_readfirstlane(s_par[c]);
+        load_slice<VEC>(p.logits + (size_t)row * p.V, base, n, -__builtin_inff(), f.v);
+        load_slice<VEC>(p.probs + (size_t)row * p.V, base, n, 0.0f, f.w);
     };
     auto finish = [&](int j, const Fetch &f) {
-        float M;
-        double invZ;
-        if (fast) {
-            M = wave_max_f32(f.st.m);
-            const double z = f.st.z > 0.0 ? f.st.z * exp((double)f.st.m - (double)M) : 0.0;
-            invZ = 1.0 / wave_sum_f64(z);
-        } else {
-            tree_row_mz(p, f.row, M, invZ);
-        }
-        const double C = hp ? f.cp + wave_sum_f64(fast ? f.zp : tree_z_share(p, b, f.prev)) : 1.0;
+        const float M = s_M[j];
+        const double invZ = s_iZ[j], C = s_C[j];
         double acc = 0.0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -1519,14 +1504,42 @@ __global__ __launch_bounds__(kSampleThreads * 4) void sv_tree_level_kernel(Sampl
             acc += r > 0.0 ? r : 0.0;
         }
         acc = wave_sum_f64(acc);
-        if (lane == 0) {
+        if (lane == 0)
             s_part[wave][j] = acc;
-            if (chunk == 0 && wave == 0)
-                p.tree_c[(size_t)b * N + f.c] = C;  // for c's next sibling
-        }
     };
     Fetch fa, fb;
-    fetch(0, fa);
+    fetch(0, fa);  // in flight during the per-child pass
+    // Per child j of this rank (wave j; nk <= 15 < kLevelWaves): its parent
+    // row's maximum and 1/Z and the child's C, once for the workgroup rather
+    // than in every wave (the same reductions on the same values).
+    if (wave < nk) {
+        const int c = __builtin_amdgcn_readfirstlane(s_kid[wave]);
+        const int prev = __builtin_amdgcn_readfirstlane(s_prev[wave]);
+        const int row = b * N + __builtin_amdgcn_readfirstlane(s_par[c]);
+        const int pn = hp ? prev : c;  // (c: a valid address when unused)
+        const RowStat st = load_or(static_cast<const RowStat *>(p.row_stats), (size_t)row * p.nchunk + lane,
+                                   fast && lane < p.nchunk, RowStat{-__builtin_inff(), 0, 0.0});
+        const double zp = load_or(p.coefs, ((size_t)b * N + pn) * p.nchunk + lane, fast && hp && lane < p.nchunk, 0.0);
+        const double cp = load_or(p.tree_c, (size_t)b * N + pn, hp, 1.0);
+        float M;
+        double invZ;
+        if (fast) {
+            M = wave_max_f32(st.m);
+            const double z = st.z > 0.0 ? st.z * exp((double)st.m - (double)M) : 0.0;
+            invZ = 1.0 / wave_sum_f64(z);
+        } else {
+            tree_row_mz(p, row, M, invZ);
+        }
+        const double C = hp ? cp + wave_sum_f64(fast ? zp : tree_z_share(p, b, prev)) : 1.0;
+        if (lane == 0) {
+            s_M[wave] = M;
+            s_iZ[wave] = invZ;
+            s_C[wave] = C;
+            if (chunk == 0)
+                p.tree_c[(size_t)b * N + c] = C;  // for c's next sibling
+        }
+    }
+    __syncthreads();
     for (int j = 0; j < nk; j += 2) {
         if (j + 1 < nk)
             fetch(j + 1, fb);
